@@ -1,0 +1,17 @@
+"""CPU oracle for sparse 3-D convolution on voxel coordinate sets.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow reference that the
+HIP library is checked against.  Only the test suite, ``__graft_entry__.smoke``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the library itself
+never calls it and has no CPU fallback.  It shares no code with the HIP path.
+
+* ``kmap``  -- kernel maps: the submanifold ``[K^3, N]`` neighbour map by sorted
+  keys and binary search, and the strided output coordinates, maps and pair
+  lists written out from their definition.
+* ``conv``  -- forward, dinput, dfilter and dbias as per-offset fp64 sums.
+
+Every function cites the passage it follows.  Pins that tie it to the pages
+and to mathematics live in ``tests/test_oracle_*.py``.
+"""
+
+from . import conv, kmap  # noqa: F401

@@ -1,0 +1,97 @@
+"""Oracle convolution arithmetic (test infrastructure only; see the package docstring).
+
+All sums run in float64 on the exact values of the (already quantised)
+fp32 / fp16 / bf16 inputs.  ``nbr`` is always the output-stationary map
+``[K, n_out]`` (the submanifold ``nbr`` or the strided ``nbr_out``), and the
+weight layout is ``[K, Cin, Cout]`` (MLX ``sparse/conv.py`` page, ``SubMConv3d``).
+
+Forward (MLX page, module docstring): ``out[o] = bias + sum_k feats[nbr[k][o]] @ W[k]``
+over the offsets whose neighbour is present; an absent neighbour adds nothing.
+dinput and dfilter are the adjoint and the weight derivative of that same sum
+(the Hygon spconv-das README, "Public Interface Support": forward, dinput and
+dfilter), written from it here rather than from any transposed map.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def f64(t) -> np.ndarray:
+    """Exact float64 copy of a torch tensor or array of any float dtype."""
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def conv_fwd(feats, weight, bias, nbr) -> np.ndarray:
+    """``out[o] = bias + sum_k feats[nbr[k][o]] @ W[k]`` (MLX page formula), fp64."""
+    x, w = f64(feats), f64(weight)
+    nbr = np.asarray(nbr)
+    K, n_out = nbr.shape
+    out = np.zeros((n_out, w.shape[2]), dtype=np.float64)
+    if bias is not None:
+        out += f64(bias)[None, :]
+    for k in range(K):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        out[o] += x[nbr[k][o]] @ w[k]
+    return out
+
+
+def conv_fwd_rows(feats, weight, bias, nbr, rows) -> np.ndarray:
+    """The forward sum for selected output rows only, one row at a time."""
+    x, w = f64(feats), f64(weight)
+    b = None if bias is None else f64(bias)
+    res = np.zeros((len(rows), w.shape[2]), dtype=np.float64)
+    for r, o in enumerate(rows):
+        acc = np.zeros(w.shape[2]) if b is None else b.copy()
+        for k in range(nbr.shape[0]):
+            i = nbr[k][o]
+            if i >= 0:
+                acc += x[i] @ w[k]
+        res[r] = acc
+    return res
+
+
+def conv_bwd_input(dout, weight, nbr, n_in: int) -> np.ndarray:
+    """Adjoint of ``conv_fwd`` in the features: ``din[i] = sum over (k, o) with
+    nbr[k][o] = i of dout[o] @ W[k]^T``, fp64."""
+    g, w = f64(dout), f64(weight)
+    nbr = np.asarray(nbr)
+    din = np.zeros((n_in, w.shape[1]), dtype=np.float64)
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        i = nbr[k][o]
+        # one offset maps distinct outputs to distinct inputs, so a plain
+        # indexed add is exact here; np.add.at would give the same result
+        assert np.unique(i).size == i.size
+        din[i] += g[o] @ w[k].T
+    return din
+
+
+def conv_bwd_filter(feats, dout, nbr) -> np.ndarray:
+    """Weight derivative of ``conv_fwd``: ``dW[k] = sum_o feats[nbr[k][o]]^T dout[o]``
+    over present neighbours, fp64 ``[K, Cin, Cout]``."""
+    x, g = f64(feats), f64(dout)
+    nbr = np.asarray(nbr)
+    dw = np.zeros((nbr.shape[0], x.shape[1], g.shape[1]), dtype=np.float64)
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        dw[k] = x[nbr[k][o]].T @ g[o]
+    return dw
+
+
+def conv_bwd_bias(dout) -> np.ndarray:
+    """Bias derivative: the column sum of ``dout``, fp64."""
+    return f64(dout).sum(axis=0)
+
+
+def max_rel_err(got, ref) -> float:
+    """``max|got - ref| / max|ref|`` (0 when both are empty or ref is all zero)."""
+    g, r = f64(got), f64(ref)
+    if r.size == 0:
+        return 0.0
+    scale = np.abs(r).max()
+    err = np.abs(g - r).max()
+    return float(err / scale) if scale > 0 else float(err)
