@@ -1,0 +1,188 @@
+/*
+ * spc.h -- C ABI of libspc: kernel maps and sparse 3-D convolution on voxel
+ * coordinate sets, hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Coordinates are int32 rows (b, z, y, x), batch index first, as in spconv's
+ *   SparseConvTensor (spconv USAGE.md, "Creating and Converting
+ *   SparseConvTensor").  Rows may come in any order; no call reorders them.
+ * - Kernel offsets are flattened z-slowest, k = (kz * KY + ky) * KX + kx, and
+ *   output site o reads the input at o*stride - pad + k*dil per axis (torch
+ *   conv3d cross-correlation; spconv USAGE.md, "Core Concepts": a sparse
+ *   convolution equals the dense convolution of the densified tensor).  For a
+ *   submanifold convolution this is the centred C-order offset list of the MLX
+ *   sparse/conv.py page (_kernel_offsets) with stride 1 and pad ksize/2.
+ * - Weights are [K, Cin, Cout] row-major (MLX sparse/conv.py page, SubMConv3d).
+ * - feats / weight / out / dout / din share one dtype (spc_dtype); bias, dW and
+ *   dbias are fp32.  Accumulation is fp32, and a 16-bit output is rounded once,
+ *   round-to-nearest-even, from the fp32 accumulator with the bias added.
+ * - Every pointer except n_out / out_shape / bytes is a DEVICE pointer owned by
+ *   the caller; the library allocates nothing and keeps no state between calls
+ *   (apart from a thread-local error string).  Device pointers must be 16-byte
+ *   aligned.  Every launch is ordered on `stream` (NULL = the default stream).
+ * - Errors: a call returns before any launch when its host-side checks fail,
+ *   leaving outputs untouched; spc_last_error() then describes the failure.
+ *   Only the strided spc_build_kmap synchronises the stream (once, to learn the
+ *   output count); every other call is asynchronous.
+ * - Sizes: row counts below 2^31; channel counts multiples of 16.
+ */
+#ifndef SPC_H
+#define SPC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spc_status {
+    SPC_OK = 0,
+    SPC_ERR_ARG = 1,          /* a pointer, size or geometry argument is invalid   */
+    SPC_ERR_UNSUPPORTED = 2,  /* valid, but outside what this library implements   */
+    SPC_ERR_CAPACITY = 3,     /* out_cap too small; *n_out holds the count needed  */
+    SPC_ERR_COORD = 4,        /* duplicate or out-of-range input coordinates       */
+    SPC_ERR_WORKSPACE = 5,    /* ws_bytes below what the size query returned       */
+    SPC_ERR_HIP = 6           /* a HIP runtime call failed                          */
+} spc_status;
+
+typedef enum spc_dtype { SPC_F32 = 0, SPC_F16 = 1, SPC_BF16 = 2 } spc_dtype;
+
+/* Bits written to *coord_err by spc_build_kmap. */
+#define SPC_COORD_OUT_OF_RANGE 1  /* b not in [0, batch) or z/y/x outside shape  */
+#define SPC_COORD_DUPLICATE    2  /* two rows share (b, z, y, x)                  */
+
+/*
+ * Convolution geometry.  subm != 0 selects a submanifold convolution (spconv
+ * USAGE.md, "Submanifold Convolution": output sites are the input sites): each
+ * ksize must be odd (the MLX page's SubMConv3d rejects even sizes), and stride,
+ * pad and dil are ignored (1, ksize/2, 1).  subm == 0 selects a strided sparse
+ * convolution whose output extent per axis is
+ * floor((shape + 2*pad - dil*(ksize-1) - 1) / stride) + 1.
+ * batch * Z * Y * X (and the output grid's volume) must stay below 2^32.
+ */
+typedef struct spc_geom {
+    int32_t batch;      /* samples; coords[:,0] in [0, batch)           */
+    int32_t shape[3];   /* input spatial extent (Z, Y, X)               */
+    int32_t ksize[3];
+    int32_t stride[3];
+    int32_t pad[3];
+    int32_t dil[3];
+    int32_t subm;
+} spc_geom;
+
+/* Host only.  Output spatial extent of a strided geometry (the input shape for
+ * subm).  Extents <= 0 mean an empty output (spconv COMMON_PROBLEMS.md: the
+ * [8,200,200] example whose only site is dropped along z). */
+spc_status spc_out_shape(const spc_geom* g, int32_t out_shape[3]);
+
+/* Host only.  Workspace bytes spc_build_kmap needs for n_in input rows. */
+spc_status spc_kmap_workspace(const spc_geom* g, int64_t n_in, size_t* bytes);
+
+/*
+ * Kernel map ("indice pairs"; spconv's get_indice_pairs_implicit_gemm on the
+ * context7 spconv page, INT8_GUIDE.md snippet).  Builds a GPU hash table over
+ * the packed keys ((b*Z + z)*Y + y)*X + x of the input rows and probes it for
+ * every kernel offset.
+ *
+ * subm != 0 (the MLX page's build_indice_map, computed on the GPU):
+ *   nbr       [K, n_in] int32: nbr[k*n_in + i] = row j with coords[j] =
+ *             coords[i] + d_k in the same sample, else -1.  *n_out = n_in.
+ *   out_coords, out_cap, nbr_in: unused (may be NULL / 0).
+ * subm == 0 (spconv USAGE.md, "Sparse Convolution"):
+ *   out_coords [out_cap, 4] int32: the M output sites, sorted by (b, z, y, x).
+ *   nbr       [K, M] int32 compact (row stride M, written at the start of a
+ *             buffer of K*out_cap entries): input row read by output o through
+ *             offset k, else -1.
+ *   nbr_in    [K, n_in] int32 (NULL ok): output row fed by input i through
+ *             offset k, else -1.
+ *   *n_out    receives M.  The call synchronises `stream` once to learn M.
+ *   If out_coords is NULL the call only counts: *n_out = M, nothing else is
+ *   written.  If M > out_cap it returns SPC_ERR_CAPACITY with *n_out = M.
+ *   An empty output (M = 0) is valid.
+ * Pair lists (both kinds; all three NULL or all three set): for each offset
+ *   k, the pairs (nbr[k][o], o) with nbr[k][o] >= 0 in ascending o, as CSR:
+ *   pair_ptr [K+1] int32 (offset k owns [pair_ptr[k], pair_ptr[k+1])),
+ *   pair_in / pair_out [pair_cap] int32, pair_cap >= K * n_in.
+ * coord_err (NULL ok): device int32 receiving SPC_COORD_* bits.  Rows flagged
+ *   out of range are left out of the table; for a duplicate the map refers to
+ *   one of the equal rows.  The strided call also returns SPC_ERR_COORD.
+ * ws: device workspace of at least spc_kmap_workspace() bytes; its contents
+ *   are scratch and need no initialisation.
+ */
+spc_status spc_build_kmap(const spc_geom* g, const int32_t* coords, int64_t n_in,
+                          int32_t* out_coords, int64_t out_cap, int64_t* n_out,
+                          int32_t* nbr, int32_t* nbr_in,
+                          int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
+                          int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Submanifold forward (the MLX page's module docstring formula):
+ *   out[c] = bias + sum_k feats[nbr[k][c]] @ W[k]   over offsets with nbr >= 0.
+ * feats [n, cin], weight [K, cin, cout], bias [cout] fp32 (NULL ok),
+ * nbr [K, n] from spc_build_kmap, out [n, cout].  K == 1 is the per-voxel
+ * linear layer out = feats @ W[0] + bias (MLX page, k=1 path; the Hygon
+ * spconv-das README routes 1x1 convolutions to a GEMM); nbr may then be NULL.
+ * One fused kernel: gathered rows feed MFMA tiles directly, the fp32
+ * accumulator stays in registers per output row (no atomics, deterministic).
+ */
+spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int64_t n, int32_t cin,
+                             const void* weight, int32_t K, int32_t cout, const float* bias,
+                             const int32_t* nbr, void* out, hipStream_t stream);
+
+/*
+ * Strided forward: out[o] = bias + sum_k feats[nbr_out[k][o]] @ W[k] for the
+ * n_out output rows of a strided spc_build_kmap (nbr_out = its compact nbr).
+ */
+spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
+                               const void* weight, int32_t K, int32_t cout, const float* bias,
+                               const int32_t* nbr_out, int64_t n_out, void* out,
+                               hipStream_t stream);
+
+/*
+ * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput
+ * and dfilter): din[i] = sum over (k, o) with map_fwd[k][o] = i of
+ * dout[o] @ W[k]^T, computed output-stationary over the input rows:
+ *   map_is_subm != 0: map is the submanifold nbr [K, n_in] (n_out == n_in); by
+ *                     symmetry din[i] = sum_k dout[nbr[K-1-k][i]] @ W[k]^T.
+ *   map_is_subm == 0: map is the strided nbr_in [K, n_in];
+ *                     din[i] = sum_k dout[nbr_in[k][i]] @ W[k]^T.
+ * K == 1 with map NULL is the per-voxel case (n_out == n_in).
+ * dout [n_out, cout], weight [K, cin, cout], din [n_in, cin] (overwritten).
+ */
+spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int64_t n_out, int32_t cout,
+                              const void* weight, int32_t K, int32_t cin,
+                              const int32_t* map, int32_t map_is_subm, int64_t n_in,
+                              void* din, hipStream_t stream);
+
+/* Host only.  Workspace bytes spc_conv_bwd_filter needs. */
+spc_status spc_conv_bwd_filter_workspace(int64_t n_in, int64_t n_out, int32_t cin, int32_t cout,
+                                         int32_t K, int32_t want_dbias, size_t* bytes);
+
+/*
+ * dfilter: dW[k] = sum over the pairs (i, o) of offset k of feats[i]^T dout[o],
+ * fp32 [K, cin, cout] (overwritten), from the CSR pair lists of
+ * spc_build_kmap.  dbias (NULL ok) = column sums of dout, fp32 [cout].
+ * K == 1 with all pair pointers NULL pairs row i with row i (n_in == n_out).
+ * Reduction: fixed-size pair chunks per offset, each a partial in the
+ * workspace, summed in a fixed order, so the result is run-to-run identical.
+ */
+spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
+                               const void* dout, int64_t n_out, int32_t cout, int32_t K,
+                               const int32_t* pair_ptr, const int32_t* pair_in,
+                               const int32_t* pair_out, float* dw, float* dbias,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* spc_last_error(void);
+
+/* Library version string. */
+const char* spc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPC_H */

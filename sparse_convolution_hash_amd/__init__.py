@@ -1,0 +1,19 @@
+"""MI355X-native sparse 3-D convolution on voxel coordinate sets.
+
+The compute lives in ``libspc.so`` (hand-written HIP kernels for gfx950
+behind the C ABI of ``include/spc.h``); this package only binds it.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTS,
+    SpcError,
+    build_kmap,
+    conv_bwd_filter,
+    conv_bwd_input,
+    lib,
+    make_geom,
+    out_shape,
+    sparse_conv_fwd,
+    subm_conv_fwd,
+    version,
+)

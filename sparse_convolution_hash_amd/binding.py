@@ -1,0 +1,281 @@
+"""ctypes binding of libspc (include/spc.h): argument marshalling only.
+
+Each function here has the name of the C entry point it wraps, takes torch
+tensors that already live on the GPU, allocates the outputs and the workspace
+with torch (device memory is all torch provides) and passes raw pointers and
+the current HIP stream to the library.  Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
+``libspc.so`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspc.so")
+
+SPC_OK, SPC_ERR_ARG, SPC_ERR_UNSUPPORTED, SPC_ERR_CAPACITY, SPC_ERR_COORD, SPC_ERR_WORKSPACE, SPC_ERR_HIP = range(7)
+COORD_OUT_OF_RANGE, COORD_DUPLICATE = 1, 2
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4: "SPC_ERR_COORD",
+           5: "SPC_ERR_WORKSPACE", 6: "SPC_ERR_HIP"}
+
+EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
+           "spc_sparse_conv_fwd", "spc_conv_bwd_input", "spc_conv_bwd_filter_workspace",
+           "spc_conv_bwd_filter", "spc_last_error", "spc_version")
+
+
+class SpcError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("shape", ctypes.c_int32 * 3), ("ksize", ctypes.c_int32 * 3),
+                ("stride", ctypes.c_int32 * 3), ("pad", ctypes.c_int32 * 3), ("dil", ctypes.c_int32 * 3),
+                ("subm", ctypes.c_int32)]
+
+
+def _t3(v) -> tuple:
+    if isinstance(v, int):
+        return (v, v, v)
+    v = tuple(int(a) for a in v)
+    if len(v) != 3:
+        raise ValueError("expected an int or 3 ints")
+    return v
+
+
+def make_geom(batch: int, shape, ksize, stride=1, pad=0, dil=1, subm: bool = True) -> Geom:
+    a = lambda v: (ctypes.c_int32 * 3)(*_t3(v))
+    return Geom(int(batch), a(shape), a(ksize), a(stride), a(pad), a(dil), 1 if subm else 0)
+
+
+_lib = None
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_convolution_hash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    GP = ctypes.POINTER(Geom)
+    sig = {
+        "spc_out_shape": [GP, ctypes.POINTER(_I32)],
+        "spc_kmap_workspace": [GP, _I64, ctypes.POINTER(_SZ)],
+        "spc_build_kmap": [GP, _P, _I64, _P, _I64, ctypes.POINTER(_I64), _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P],
+        "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P],
+        "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _I64, _P, _P],
+        "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _I64, _P, _P],
+        "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+        "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    for name in ("spc_last_error", "spc_version"):
+        f = getattr(L, name)
+        f.argtypes = []
+        f.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str):
+    if status != SPC_OK:
+        raise SpcError(status, func, lib().spc_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def version() -> str:
+    return lib().spc_version().decode()
+
+
+def out_shape(batch, shape, ksize, stride=1, pad=0, dil=1, subm=False) -> tuple:
+    g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
+    o = (ctypes.c_int32 * 3)()
+    _check(lib().spc_out_shape(ctypes.byref(g), o), "spc_out_shape")
+    return tuple(o)
+
+
+def kmap_workspace(g: Geom, n_in: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().spc_kmap_workspace(ctypes.byref(g), int(n_in), ctypes.byref(b)), "spc_kmap_workspace")
+    return b.value
+
+
+def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
+               subm: bool = True, pairs: bool = True, with_nbr_in: bool = True,
+               out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Kernel map of int32 [N, 4] (b, z, y, x) coordinates (spc_build_kmap).
+
+    Returns a dict with ``nbr`` [K, n_out] (submanifold neighbour map or the
+    strided nbr_out), ``n_out``, ``coord_err`` (device int32 [1]) and, as
+    requested, ``out_coords`` [n_out, 4], ``nbr_in`` [K, N] and the CSR pair
+    lists ``pair_ptr`` [K+1], ``pair_in`` / ``pair_out`` (first pair_ptr[K]
+    entries valid).  A strided call without ``out_cap`` first asks the library
+    for the output count, then allocates exactly.
+    """
+    _need(coords, "coords", torch.int32)
+    if coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be [N, 4]")
+    dev = coords.device
+    n = coords.shape[0]
+    g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
+    K = int(g.ksize[0] * g.ksize[1] * g.ksize[2])
+    ws_bytes = kmap_workspace(g, n)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = _stream(dev)
+    n_out = ctypes.c_int64(0)
+    err = torch.zeros(4, dtype=torch.int32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    if not subm and out_cap is None:
+        st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, None, 0, ctypes.byref(n_out), None, None,
+                                  None, None, None, 0, _ptr(err), _ptr(workspace), workspace.numel(), stream)
+        _check(st, "spc_build_kmap")
+        out_cap = n_out.value
+    cap = n if subm else int(out_cap)
+    res = {"coord_err": err[:1]}
+    out_coords = None if subm else torch.empty((max(cap, 1), 4), **i32)
+    nbr = torch.empty(max(K * cap, 4), **i32)
+    nbr_in = torch.empty((K, n), **i32) if (not subm and with_nbr_in) else None
+    pp = pi = po = None
+    if pairs:
+        pp = torch.empty(K + 1, **i32)
+        pi = torch.empty(max(K * n, 4), **i32)
+        po = torch.empty(max(K * n, 4), **i32)
+    st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, _ptr(out_coords), cap, ctypes.byref(n_out),
+                              _ptr(nbr), _ptr(nbr_in), _ptr(pp), _ptr(pi), _ptr(po), max(K * n, 0) if pairs else 0,
+                              _ptr(err), _ptr(workspace), workspace.numel(), stream)
+    _check(st, "spc_build_kmap")
+    m = int(n_out.value)
+    res["n_out"] = m
+    res["nbr"] = nbr[:K * m].view(K, m)
+    if not subm:
+        res["out_coords"] = out_coords[:m]
+    if nbr_in is not None:
+        res["nbr_in"] = nbr_in
+    if pairs:
+        res["pair_ptr"], res["pair_in"], res["pair_out"] = pp, pi, po
+    return res
+
+
+def _conv_checks(x, weight, bias, dev):
+    _need(x, "input", dev=dev)
+    _need(weight, "weight", x.dtype, dev)
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if weight.dim() != 3:
+        raise ValueError("weight must be [K, Cin, Cout]")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev)
+
+
+def subm_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                  nbr: Optional[torch.Tensor], out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = bias + sum_k feats[nbr[k]] @ W[k] (spc_subm_conv_fwd)."""
+    dev = feats.device
+    _conv_checks(feats, weight, bias, dev)
+    K, cin, cout = weight.shape
+    n = feats.shape[0]
+    if nbr is not None:
+        _need(nbr, "nbr", torch.int32, dev)
+    if out is None:
+        out = torch.empty((n, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_subm_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), n, cin, _ptr(weight), K, cout, _ptr(bias),
+                                 _ptr(nbr), _ptr(out), _stream(dev))
+    _check(st, "spc_subm_conv_fwd")
+    return out
+
+
+def sparse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                    nbr_out: torch.Tensor, n_out: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Strided forward over the n_out output rows of a strided kernel map (spc_sparse_conv_fwd)."""
+    dev = feats.device
+    _conv_checks(feats, weight, bias, dev)
+    _need(nbr_out, "nbr_out", torch.int32, dev)
+    K, cin, cout = weight.shape
+    if out is None:
+        out = torch.empty((n_out, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_sparse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,
+                                   _ptr(bias), _ptr(nbr_out), int(n_out), _ptr(out), _stream(dev))
+    _check(st, "spc_sparse_conv_fwd")
+    return out
+
+
+def conv_bwd_input(dout: torch.Tensor, weight: torch.Tensor, map_: Optional[torch.Tensor], map_is_subm: bool,
+                   n_in: int, din: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the input features (spc_conv_bwd_input)."""
+    dev = dout.device
+    _conv_checks(dout, weight, None, dev)
+    if map_ is not None:
+        _need(map_, "map", torch.int32, dev)
+    K, cin, cout = weight.shape
+    if din is None:
+        din = torch.empty((n_in, cin), dtype=dout.dtype, device=dev)
+    st = lib().spc_conv_bwd_input(_DTYPES[dout.dtype], _ptr(dout), dout.shape[0], cout, _ptr(weight), K, cin,
+                                  _ptr(map_), 1 if map_is_subm else 0, int(n_in), _ptr(din), _stream(dev))
+    _check(st, "spc_conv_bwd_input")
+    return din
+
+
+def conv_bwd_filter_workspace(n_in, n_out, cin, cout, K, want_dbias) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().spc_conv_bwd_filter_workspace(int(n_in), int(n_out), int(cin), int(cout), int(K),
+                                               1 if want_dbias else 0, ctypes.byref(b)),
+           "spc_conv_bwd_filter_workspace")
+    return b.value
+
+
+def conv_bwd_filter(feats: torch.Tensor, dout: torch.Tensor, K: int, pair_ptr: Optional[torch.Tensor],
+                    pair_in: Optional[torch.Tensor], pair_out: Optional[torch.Tensor], want_dbias: bool = False,
+                    workspace: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None):
+    """Weight (and optionally bias) gradient from CSR pair lists (spc_conv_bwd_filter).
+
+    Returns ``(dw [K, Cin, Cout] fp32, dbias [Cout] fp32 or None)``."""
+    dev = feats.device
+    _need(feats, "feats", dev=dev)
+    _need(dout, "dout", feats.dtype, dev)
+    for t, nm in ((pair_ptr, "pair_ptr"), (pair_in, "pair_in"), (pair_out, "pair_out")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
+    cin, cout = feats.shape[1], dout.shape[1]
+    ws = conv_bwd_filter_workspace(feats.shape[0], dout.shape[0], cin, cout, K, want_dbias)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    if dw is None:
+        dw = torch.empty((K, cin, cout), dtype=torch.float32, device=dev)
+    db = torch.empty(cout, dtype=torch.float32, device=dev) if want_dbias else None
+    st = lib().spc_conv_bwd_filter(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(dout),
+                                   dout.shape[0], cout, int(K), _ptr(pair_ptr), _ptr(pair_in), _ptr(pair_out),
+                                   _ptr(dw), _ptr(db), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "spc_conv_bwd_filter")
+    return dw, db

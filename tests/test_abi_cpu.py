@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/spc.h declares, and host-side checks return their status before any
+launch (so fake, never-dereferenced pointers are safe here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_convolution_hash_amd.binding as B
+from oracle import kmap as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libspc.so not built")
+
+FAKE = ctypes.c_void_p(0x100000)        # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:spc_status|const char\*)\s+(spc_\w+)\(", txt, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for f in ("spc_build_kmap", "spc_subm_conv_fwd", "spc_sparse_conv_fwd", "spc_conv_bwd_input",
+              "spc_conv_bwd_filter"):
+        assert f in names
+    assert sorted(B.EXPORTS) == names
+
+
+def test_every_declared_symbol_is_exported():
+    L = B.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    assert B.version().startswith("libspc")
+
+
+@pytest.mark.parametrize("shape,k,s,p,d", [
+    ((41, 1600, 1408), 3, 2, 1, 1), ((8, 200, 200), 3, 2, (0, 1, 1), 1), ((10, 11, 12), 2, 3, 0, 2),
+    ((5, 5, 5), 3, 1, 0, 3), ((3, 3, 3), 5, 2, 0, 1),
+])
+def test_out_shape_matches_oracle(shape, k, s, p, d):
+    assert B.out_shape(1, shape, k, s, p, d, subm=False) == O.out_shape(shape, k, s, p, d)
+
+
+def _ws(g, n):
+    b = ctypes.c_size_t()
+    return B.lib().spc_kmap_workspace(ctypes.byref(g), n, ctypes.byref(b)), b.value
+
+
+def test_kmap_workspace_checks():
+    assert _ws(B.make_geom(2, (41, 1600, 1408), 3), 120000)[0] == B.SPC_OK
+    assert _ws(B.make_geom(1, (8, 8, 8), 2), 10)[0] == B.SPC_ERR_ARG            # even submanifold k
+    assert _ws(B.make_geom(0, (8, 8, 8), 3), 10)[0] == B.SPC_ERR_ARG            # batch
+    assert _ws(B.make_geom(1, (0, 8, 8), 3), 10)[0] == B.SPC_ERR_ARG            # shape
+    assert _ws(B.make_geom(64, (2048, 2048, 1024), 3), 10)[0] == B.SPC_ERR_UNSUPPORTED  # key space
+    assert _ws(B.make_geom(1, (8, 8, 8), 9), 10)[0] == B.SPC_ERR_UNSUPPORTED    # ksize > 7
+    assert _ws(B.make_geom(1, (8, 8, 8), 3, 0, 1, 1, subm=False), 10)[0] == B.SPC_ERR_ARG  # stride 0
+    assert _ws(B.make_geom(1, (8, 8, 8), 3), -1)[0] == B.SPC_ERR_ARG
+    st, small = _ws(B.make_geom(1, (8, 8, 8), 3), 10)
+    st2, big = _ws(B.make_geom(1, (8, 8, 8), 3), 100000)
+    assert st == st2 == B.SPC_OK and big > small
+
+
+def test_build_kmap_host_checks():
+    L = B.lib()
+    g = B.make_geom(1, (8, 8, 8), 3)
+    n_out = ctypes.c_int64()
+    args = lambda **kw: dict(dict(coords=FAKE, nbr=FAKE, pp=None, pi=None, po=None, cap=0, ws=FAKE, wsb=1 << 30), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.spc_build_kmap(ctypes.byref(g), a["coords"], 10, None, 0, ctypes.byref(n_out), a["nbr"], None,
+                                a["pp"], a["pi"], a["po"], a["cap"], None, a["ws"], a["wsb"], None)
+    assert call(ws=None) == B.SPC_ERR_ARG
+    assert call(wsb=16) == B.SPC_ERR_WORKSPACE
+    assert call(coords=None) == B.SPC_ERR_ARG
+    assert call(nbr=None) == B.SPC_ERR_ARG
+    assert call(coords=MISALIGNED) == B.SPC_ERR_ARG
+    assert call(pp=FAKE) == B.SPC_ERR_ARG                       # pair lists: all or none
+    assert call(pp=FAKE, pi=FAKE, po=FAKE, cap=10) == B.SPC_ERR_ARG  # pair_cap < K * n
+    assert "pair_cap" in B.lib().spc_last_error().decode()
+
+
+def test_conv_host_checks():
+    L = B.lib()
+    fwd = lambda dt, cin, cout, K, nbr=FAKE, x=FAKE: L.spc_subm_conv_fwd(dt, x, 100, cin, FAKE, K, cout, None,
+                                                                        nbr, FAKE, None)
+    assert fwd(2, 24, 32, 27) == B.SPC_ERR_UNSUPPORTED          # cin not a multiple of 16
+    assert fwd(2, 32, 8, 27) == B.SPC_ERR_UNSUPPORTED
+    assert fwd(7, 32, 32, 27) == B.SPC_ERR_ARG                  # dtype
+    assert fwd(2, 32, 32, 0) == B.SPC_ERR_ARG                   # K
+    assert fwd(2, 32, 32, 27, nbr=None) == B.SPC_ERR_ARG        # map required for K > 1
+    assert fwd(2, 32, 32, 27, x=MISALIGNED) == B.SPC_ERR_ARG
+    # zero rows: valid, nothing launched
+    assert L.spc_subm_conv_fwd(2, None, 0, 32, FAKE, 27, 32, None, None, FAKE, None) == B.SPC_OK
+    # submanifold dinput needs n_out == n_in
+    assert L.spc_conv_bwd_input(1, FAKE, 10, 64, FAKE, 27, 64, FAKE, 1, 11, FAKE, None) == B.SPC_ERR_ARG
+    b = ctypes.c_size_t()
+    assert L.spc_conv_bwd_filter_workspace(1000, 1000, 64, 64, 27, 1, ctypes.byref(b)) == B.SPC_OK and b.value > 0
+    # dfilter: identity pairs only for K == 1, workspace size enforced
+    assert L.spc_conv_bwd_filter(1, FAKE, 10, 64, FAKE, 10, 64, 27, None, None, None, FAKE, None, FAKE,
+                                 1 << 30, None) == B.SPC_ERR_ARG
+    assert L.spc_conv_bwd_filter(1, FAKE, 10, 64, FAKE, 10, 64, 1, None, None, None, FAKE, None, FAKE,
+                                 8, None) == B.SPC_ERR_WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        B.subm_conv_fwd(torch.zeros(4, 16), torch.zeros(27, 16, 16), None, torch.zeros(27, 4, dtype=torch.int32))

@@ -1,0 +1,154 @@
+"""GPU convolutions vs the oracle (fp64): submanifold and strided forward,
+k=1, dinput, dfilter and dbias, for fp32 / fp16 / bf16, at small sizes that
+span several tiles with ragged tails and at the named workloads' full sizes."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_convolution_hash_amd as spc
+import workloads as W
+from oracle import conv as OC
+from oracle import kmap as O
+from tests.parity import TOL, TOL_DW, assert_close, cuda, host
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+
+
+def _subm_case(seed, side, fill, batch, k, cin, cout, dtype, bias=True):
+    c = W.tiny_grid(W.rng(seed), side, fill, batch)
+    t = W.small_layer(seed, c, cin, cout, k ** 3, dtype, bias=bias)
+    return c, t
+
+
+def run_subm_layer(c, batch, shape, k, t, dtype, train=True, what=""):
+    """Forward (and dinput / dfilter / dbias) of one submanifold layer vs the oracle."""
+    print(f"subm conv {what} n={c.shape[0]} k={k} {tuple(t['weight'].shape)} {dtype}", flush=True)
+    km = spc.build_kmap(cuda(c), batch, shape, k, pairs=train)
+    nbr_ref = O.subm_kmap(c, shape, k)
+    x, w = cuda(t["feats"]), cuda(t["weight"])
+    b = cuda(t["bias"]) if t.get("bias") is not None else None
+    out = spc.subm_conv_fwd(x, w, b, km["nbr"] if k > 1 else None)
+    errs = {"fwd": assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr_ref), TOL[dtype], "fwd")}
+    if not train:
+        return errs
+    g = cuda(t["grad"])
+    din = spc.conv_bwd_input(g, w, km["nbr"] if k > 1 else None, True, c.shape[0])
+    errs["din"] = assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], nbr_ref, c.shape[0]), TOL[dtype], "din")
+    pp, pi, po = (km["pair_ptr"], km["pair_in"], km["pair_out"]) if k > 1 else (None, None, None)
+    dw, db = spc.conv_bwd_filter(x, g, k ** 3, pp, pi, po, want_dbias=True)
+    errs["dw"] = assert_close(dw, OC.conv_bwd_filter(t["feats"], t["grad"], nbr_ref), TOL_DW, "dw")
+    errs["db"] = assert_close(db, OC.conv_bwd_bias(t["grad"]), TOL_DW, "dbias")
+    return errs
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("seed,side,fill,batch,k,cin,cout", [
+    (1, 9, 0.3, 1, 3, 16, 16),        # one tile, ragged
+    (2, 14, 0.25, 2, 3, 32, 48),      # several tiles, cout 48 (3 blocks)
+    (3, 12, 0.4, 1, 3, 64, 128),      # full 128-channel tile
+    (4, 10, 0.3, 2, 1, 48, 32),       # k = 1 (identity map)
+    (5, 8, 0.5, 1, 5, 16, 32),        # k = 5, 125 offsets (several offset tiles)
+    (6, 16, 0.2, 3, 3, 96, 96),
+    (7, 11, 0.3, 1, 3, 144, 32),      # contraction above 128 channels
+])
+def test_subm_small(dtype, seed, side, fill, batch, k, cin, cout):
+    if dtype == torch.float32 and cin > 128:
+        pytest.skip("fp32 contraction is limited to 128 channels")
+    c, t = _subm_case(seed, side, fill, batch, k, cin, cout, dtype)
+    run_subm_layer(c, batch, (side,) * 3, k, t, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_single_voxel_and_empty(dtype):
+    c = np.array([[0, 1, 2, 3]], np.int32)
+    t = W.small_layer(3, c, 16, 32, 27, dtype)
+    run_subm_layer(c, 1, (4, 4, 4), 3, t, dtype)
+    out = spc.subm_conv_fwd(cuda(t["feats"][:0]), cuda(t["weight"]), None,
+                            torch.empty((27, 0), dtype=torch.int32, device="cuda"))
+    assert out.shape == (0, 32)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,k,s,p,d,cin,cout", [
+    ((12, 14, 10), 3, 2, 1, 1, 16, 32), ((15, 13, 11), 2, 2, 0, 1, 32, 16), ((11, 11, 11), 3, 1, 0, 2, 48, 64),
+])
+def test_strided_small(dtype, shape, k, s, p, d, cin, cout):
+    c = W.tiny_grid(W.rng(40 + k + s), min(shape), 0.25, 2)
+    print(f"strided conv n={c.shape[0]} {shape} k={k} s={s} {dtype}", flush=True)
+    km = spc.build_kmap(cuda(c), 2, shape, k, s, p, d, subm=False)
+    ref = O.strided_kmap(c, 2, shape, k, s, p, d)
+    M = ref["out_coords"].shape[0]
+    t = W.small_layer(50, c, cin, cout, k ** 3, dtype, n_out=M)
+    x, w, b, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"]), cuda(t["grad"])
+    out = spc.sparse_conv_fwd(x, w, b, km["nbr"], km["n_out"])
+    assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], ref["nbr_out"]), TOL[dtype], "fwd")
+    din = spc.conv_bwd_input(g, w, km["nbr_in"], False, c.shape[0])
+    assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], ref["nbr_out"], c.shape[0]), TOL[dtype], "din")
+    dw, db = spc.conv_bwd_filter(x, g, k ** 3, km["pair_ptr"], km["pair_in"], km["pair_out"], want_dbias=True)
+    assert_close(dw, OC.conv_bwd_filter(t["feats"], t["grad"], ref["nbr_out"]), TOL_DW, "dw")
+    assert_close(db, OC.conv_bwd_bias(t["grad"]), TOL_DW, "dbias")
+
+
+def test_deterministic():
+    c, t = _subm_case(8, 20, 0.3, 2, 3, 64, 64, torch.bfloat16)
+    km = spc.build_kmap(cuda(c), 2, (20,) * 3, 3)
+    x, w, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["grad"])
+    o1, o2 = spc.subm_conv_fwd(x, w, None, km["nbr"]), spc.subm_conv_fwd(x, w, None, km["nbr"])
+    assert torch.equal(o1, o2)
+    a = spc.conv_bwd_filter(x, g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"], True)
+    b = spc.conv_bwd_filter(x, g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"], True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def test_workload_uniform32_fp32():
+    w = W.workload("subm_k3_f32_uniform32", with_grad=True)
+    t = {"feats": w.feats, "weight": w.weight, "bias": w.bias, "grad": w.grad}
+    run_subm_layer(w.coords, w.batch, w.shape, 3, t, w.dtype, what=w.name)
+
+
+def test_workload_lidar_fp16():
+    w = W.workload("subm_k3_f16_lidar120k", with_grad=True)
+    t = {"feats": w.feats, "weight": w.weight, "bias": None, "grad": w.grad}
+    run_subm_layer(w.coords, w.batch, w.shape, 3, t, w.dtype, what=w.name)
+
+
+def test_workload_shells_bf16_k3_then_k1():
+    w = W.workload("subm_k3_k1_bf16_shells128")
+    print(f"{w.name} n={w.n}", flush=True)
+    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, pairs=False)
+    nbr_ref = O.subm_kmap(w.coords, w.shape, 3)
+    x, wt, w1 = cuda(w.feats), cuda(w.weight), cuda(w.extra["weight_k1"])
+    y = spc.subm_conv_fwd(x, wt, None, km["nbr"])
+    y_ref = OC.conv_fwd(w.feats, w.weight, None, nbr_ref)
+    assert_close(y, y_ref, TOL[w.dtype], "k3")
+    # layer 2 (k=1) consumes the GPU's own bf16 layer-1 output; the oracle gets the same values
+    z = spc.subm_conv_fwd(y, w1, None, None)
+    assert_close(z, OC.conv_fwd(y.cpu(), w.extra["weight_k1"], None, np.arange(w.n)[None]), TOL[w.dtype], "k1")
+
+
+def test_workload_strided_lidar_fp16():
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False)
+    ref = O.strided_kmap(w.coords, w.batch, w.shape, 3, 2, 1, 1)
+    M = km["n_out"]
+    print(f"{w.name} n={w.n} M={M}", flush=True)
+    g = W.grad_for(w.extra["grad_rng"], M, w.cout, w.dtype)
+    x, wt, gd = cuda(w.feats), cuda(w.weight), cuda(g)
+    out = spc.sparse_conv_fwd(x, wt, None, km["nbr"], M)
+    assert_close(out, OC.conv_fwd(w.feats, w.weight, None, ref["nbr_out"]), TOL[w.dtype], "fwd")
+    din = spc.conv_bwd_input(gd, wt, km["nbr_in"], False, w.n)
+    assert_close(din, OC.conv_bwd_input(g, w.weight, ref["nbr_out"], w.n), TOL[w.dtype], "din")
+    dw, _ = spc.conv_bwd_filter(x, gd, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
+    assert_close(dw, OC.conv_bwd_filter(w.feats, g, ref["nbr_out"]), TOL_DW, "dw")
+
+
+def test_workload_train_shells_bf16():
+    w = W.workload("train_subm_k3_bf16_shells96")
+    t = {"feats": w.feats, "weight": w.weight, "bias": None, "grad": w.grad}
+    errs = run_subm_layer(w.coords, w.batch, w.shape, 3, t, w.dtype, what=w.name)
+    print("errors", errs, flush=True)

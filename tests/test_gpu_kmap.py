@@ -1,0 +1,128 @@
+"""GPU kernel maps vs the oracle: bit-exact neighbour maps, output
+coordinates, transposed maps and CSR pair lists."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_convolution_hash_amd as spc
+import workloads as W
+from oracle import kmap as O
+from tests.parity import cuda, host, pairs_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def check_subm(coords, batch, shape, k, pairs=True):
+    print(f"subm kmap n={coords.shape[0]} shape={shape} k={k}", flush=True)
+    res = spc.build_kmap(cuda(coords), batch, shape, k, subm=True, pairs=pairs)
+    ref = O.subm_kmap(coords, shape, k)
+    assert res["n_out"] == coords.shape[0]
+    assert np.array_equal(host(res["nbr"]), ref)
+    assert int(host(res["coord_err"])[0]) == 0
+    if pairs:
+        pairs_equal(res, *O.pairs_from_map(ref))
+    return res
+
+
+def check_strided(coords, batch, shape, k, s, p, d, out_cap=None):
+    print(f"strided kmap n={coords.shape[0]} shape={shape} k={k} s={s} p={p} d={d}", flush=True)
+    res = spc.build_kmap(cuda(coords), batch, shape, k, s, p, d, subm=False, out_cap=out_cap)
+    ref = O.strided_kmap(coords, batch, shape, k, s, p, d)
+    assert res["n_out"] == ref["out_coords"].shape[0]
+    assert np.array_equal(host(res["out_coords"]), ref["out_coords"])
+    assert np.array_equal(host(res["nbr"]), ref["nbr_out"])
+    assert np.array_equal(host(res["nbr_in"]), ref["nbr_in"])
+    pairs_equal(res, *O.pairs_from_map(ref["nbr_out"]))
+    return res
+
+
+@pytest.mark.parametrize("seed,side,fill,batch,k", [
+    (1, 5, 0.3, 1, 3), (2, 12, 0.05, 3, 3), (3, 9, 0.6, 2, 3), (4, 10, 0.25, 1, 5), (5, 8, 0.4, 2, 1),
+    (6, 20, 0.2, 2, 3), (7, 11, 0.3, 1, 7),
+])
+def test_subm_tiny(seed, side, fill, batch, k):
+    check_subm(W.tiny_grid(W.rng(seed), side, fill, batch), batch, (side,) * 3, k)
+
+
+@pytest.mark.parametrize("name", ["subm_k3_f32_uniform32", "subm_k3_f16_lidar120k", "subm_k3_k1_bf16_shells128"])
+def test_subm_workloads(name):
+    w = W.workload(name)
+    check_subm(w.coords, w.batch, w.shape, w.ksize)
+
+
+def test_subm_edge_cases():
+    check_subm(np.zeros((0, 4), np.int32), 1, (4, 4, 4), 3)
+    check_subm(np.array([[0, 0, 0, 0]], np.int32), 1, (1, 1, 1), 3)          # single voxel at a corner
+    check_subm(W.random_block(W.rng(9), 4), 1, (4, 4, 4), 3)                   # full block, P = 1000
+    # rows that touch every face of a non-cubic grid
+    c = np.array([[0, 0, 0, 0], [0, 6, 4, 2], [1, 6, 0, 2], [1, 0, 4, 0], [0, 3, 2, 1]], np.int32)
+    check_subm(c, 2, (7, 5, 3), 3)
+
+
+def test_subm_flags_bad_coordinates():
+    shape = (6, 6, 6)
+    c = np.array([[0, 1, 1, 1], [0, 1, 1, 1], [0, 2, 2, 2]], np.int32)
+    res = spc.build_kmap(cuda(c), 1, shape, 3)
+    assert int(host(res["coord_err"])[0]) & spc.binding.COORD_DUPLICATE
+    c = np.array([[0, 1, 1, 1], [0, 6, 1, 1], [1, 2, 2, 2], [0, -1, 0, 0]], np.int32)
+    res = spc.build_kmap(cuda(c), 1, shape, 3)
+    assert int(host(res["coord_err"])[0]) == spc.binding.COORD_OUT_OF_RANGE
+    nbr = host(res["nbr"])
+    assert nbr[13, 0] == 0 and (nbr[:, 1:] == -1).all()      # bad rows are left out
+
+
+@pytest.mark.parametrize("seed,shape,fill,batch,k,s,p,d", [
+    (21, (6, 5, 7), 0.2, 1, 3, 2, 1, 1), (22, (7, 7, 7), 0.1, 2, 3, 2, 0, 1), (23, (8, 6, 5), 0.15, 1, 2, 2, 0, 1),
+    (24, (6, 6, 6), 0.2, 1, 3, 1, 1, 2), (25, (9, 7, 8), 0.1, 2, 3, 3, 2, 1), (26, (17, 19, 23), 0.2, 2, 3, 2, 1, 1),
+    (27, (12, 12, 12), 0.3, 1, 5, 2, 2, 1),
+])
+def test_strided_tiny(seed, shape, fill, batch, k, s, p, d):
+    r = W.rng(seed)
+    rows = []
+    for b in range(batch):
+        keep = r.random(int(np.prod(shape))) < fill
+        z, y, x = np.unravel_index(np.nonzero(keep)[0], shape)
+        rows.append(np.stack([np.full(z.size, b), z, y, x], 1))
+    c = np.concatenate(rows).astype(np.int32)
+    check_strided(c[r.permutation(c.shape[0])], batch, shape, k, s, p, d)
+
+
+def test_strided_lidar_workload():
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    res = check_strided(w.coords, w.batch, w.shape, 3, 2, 1, 1)
+    # the same call with an exact capacity (no counting pass) gives the same maps
+    res2 = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=res["n_out"])
+    assert torch.equal(res["nbr"], res2["nbr"]) and torch.equal(res["out_coords"], res2["out_coords"])
+
+
+def test_strided_golden_empty_output():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "empty_strided_output.json")))
+    res = spc.build_kmap(cuda(np.array(g["coords"], np.int32)), g["batch"], g["spatial_shape"], g["ksize"],
+                         g["stride"], g["padding"], g["dilation"], subm=False)
+    assert res["n_out"] == g["expected_n_out"]
+    assert int(host(res["pair_ptr"])[-1]) == 0
+    assert (host(res["nbr_in"]) == -1).all()
+
+
+def test_strided_capacity_and_errors():
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    with pytest.raises(spc.SpcError) as e:
+        spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=100)
+    assert e.value.status == spc.binding.SPC_ERR_CAPACITY
+    bad = np.array([[0, 1, 1, 1], [0, 1, 1, 1]], np.int32)
+    with pytest.raises(spc.SpcError) as e:
+        spc.build_kmap(cuda(bad), 1, (4, 4, 4), 3, 2, 1, 1, subm=False)
+    assert e.value.status == spc.binding.SPC_ERR_COORD
+    check_strided(np.zeros((0, 4), np.int32), 1, (4, 4, 4), 3, 2, 1, 1)
+
+
+def test_kmap_repeatable():
+    w = W.workload("subm_k3_f16_lidar120k")
+    c = cuda(w.coords)
+    a = spc.build_kmap(c, w.batch, w.shape, 3)
+    b = spc.build_kmap(c, w.batch, w.shape, 3)
+    assert torch.equal(a["nbr"], b["nbr"]) and torch.equal(a["pair_in"], b["pair_in"])
