@@ -1,0 +1,340 @@
+#!/usr/bin/env python
+"""Throughput of the sparse-convolution hot path on one MI355X.
+
+One step runs every stage of the path once on one batch of synthetic input.
+It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
+1408 grid, fp16, 64 channels.  The stages are, in order:
+
+    kmap_subm       submanifold kernel map k=3 (hash build + probe + pair lists)
+    fwd_subm        SubMConv3d k=3 forward 64 -> 64
+    fwd_k1          k=1 layer 64 -> 64 on that output
+    dinput_subm     dinput of the k=3 layer
+    dfilter_subm    dfilter of the k=3 layer
+    kmap_strided    strided kernel map k=3 s=2 p=1 (output sites, maps, pairs)
+    fwd_strided     SparseConv3d forward 64 -> 128
+    dinput_strided  its dinput
+    dfilter_strided its dfilter
+
+``--workload shells`` runs the same stages on the mesh-shell sets: 4 x 128^3,
+bf16, 128 channels, with k=1 128 -> 128.  The strided layer there is 128 -> 128.
+
+value = effective TFLOP/s of the whole step: 2 * pairs * Cin * Cout summed
+over the convolution stages (pairs counted from the kernel map, k=1 counts N
+pairs), divided by the step time.  The kernel-map rate is reported as voxels/s
+(N over the kmap_subm time).  Every stage is timed with HIP events on the
+stream the library launches on.  The roofline is given for the slowest stage
+that is a single kernel launch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "dinput_strided")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=("lidar", "shells"), default="lidar")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work to time at most")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- inputs
+
+def make_inputs(kind: str):
+    import numpy as np
+    import torch
+    import workloads as W
+
+    if kind == "lidar":
+        w = W.workload("subm_k3_f16_lidar120k", with_grad=True)
+        ws = W.workload("strided_k3s2_f16_lidar120k")
+        return dict(name="lidar_2x60k_41x1600x1408_f16_c64", coords=w.coords, batch=w.batch, shape=w.shape,
+                    dtype=w.dtype, feats=w.feats, w3=w.weight, w1=w.extra["weight_k1"], grad=w.grad,
+                    ws=ws.weight, grad_rng=ws.extra["grad_rng"])
+    w = W.workload("subm_k3_k1_bf16_shells128")
+    g = W.rng(6, "grad")
+    c = w.cin
+    grad = W.grad_for(g, w.n, c, w.dtype)
+    wstr = (torch.from_numpy(W.rng(6, "weight").standard_normal((27, c, c), dtype=np.float32)
+                             / np.sqrt(27 * c)).to(w.dtype))
+    return dict(name="shells_4x128^3_bf16_c128", coords=w.coords, batch=w.batch, shape=w.shape, dtype=w.dtype,
+                feats=w.feats, w3=w.weight, w1=w.extra["weight_k1"], grad=grad, ws=wstr, grad_rng=W.rng(6, "bias"))
+
+
+# ---------------------------------------------------------------- GPU step
+
+class Step:
+    """Holds device inputs and runs the stages of one step through the library."""
+
+    def __init__(self, inp, dev):
+        import torch
+        import sparse_convolution_hash_amd as spc
+        import workloads as W
+
+        self.spc, self.torch = spc, torch
+        self.inp = inp
+        t = lambda a: (torch.from_numpy(a) if not isinstance(a, torch.Tensor) else a).contiguous().to(dev)
+        self.coords, self.x, self.w3, self.w1, self.g = (t(inp[k]) for k in ("coords", "feats", "w3", "w1", "grad"))
+        self.ws = t(inp["ws"])
+        self.n = self.coords.shape[0]
+        self.dev = dev
+        # strided output size and its upstream gradient, drawn once
+        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False)
+        self.m = km["n_out"]
+        self.gs = t(W.grad_for(inp["grad_rng"], self.m, self.ws.shape[2], inp["dtype"]))
+        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3)
+        self.P = int(ks["pair_ptr"][-1].item())
+        self.Ps = int(km["pair_ptr"][-1].item())
+        self.names = ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm",
+                      "kmap_strided", "fwd_strided", "dinput_strided", "dfilter_strided")
+        self.ev = None
+
+    def run(self, events=None):
+        spc, inp = self.spc, self.inp
+        E = events or {}
+
+        def mark(name, i):
+            if name in E:
+                E[name][i].record()
+
+        mark("kmap_subm", 0)
+        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3)
+        mark("kmap_subm", 1)
+        mark("fwd_subm", 0)
+        y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"])
+        mark("fwd_subm", 1)
+        mark("fwd_k1", 0)
+        spc.subm_conv_fwd(y, self.w1, None, None)
+        mark("fwd_k1", 1)
+        mark("dinput_subm", 0)
+        spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n)
+        mark("dinput_subm", 1)
+        mark("dfilter_subm", 0)
+        spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
+        mark("dfilter_subm", 1)
+        mark("kmap_strided", 0)
+        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m)
+        mark("kmap_strided", 1)
+        mark("fwd_strided", 0)
+        spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"])
+        mark("fwd_strided", 1)
+        mark("dinput_strided", 0)
+        spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n)
+        mark("dinput_strided", 1)
+        mark("dfilter_strided", 0)
+        spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"])
+        mark("dfilter_strided", 1)
+
+    # effective FLOP and algorithmic HBM bytes per stage (one launch / call)
+    def work(self):
+        n, m, P, Ps = self.n, self.m, self.P, self.Ps
+        cin, c1 = self.w3.shape[1], self.w3.shape[2]
+        cs = self.ws.shape[2]
+        s = self.x.element_size()
+        K = 27
+        f = {
+            "fwd_subm": 2 * P * cin * c1, "fwd_k1": 2 * n * c1 * self.w1.shape[2],
+            "dinput_subm": 2 * P * cin * c1, "dfilter_subm": 2 * P * cin * c1,
+            "fwd_strided": 2 * Ps * cin * cs, "dinput_strided": 2 * Ps * cin * cs,
+            "dfilter_strided": 2 * Ps * cin * cs,
+        }
+        b = {
+            "kmap_subm": n * (16 + 4 * K) + 8 * P + 4 * (K + 1),
+            "fwd_subm": n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s,
+            "fwd_k1": n * c1 * s + c1 * self.w1.shape[2] * s + n * self.w1.shape[2] * s,
+            "dinput_subm": n * c1 * s + K * n * 4 + K * cin * c1 * s + n * cin * s,
+            "dfilter_subm": n * cin * s + n * c1 * s + 8 * P + 4 * (K + 1) + K * cin * c1 * 4,
+            "kmap_strided": n * 16 + m * 16 + 4 * K * (m + n) + 8 * Ps + 4 * (K + 1),
+            "fwd_strided": n * cin * s + K * m * 4 + K * cin * cs * s + m * cs * s,
+            "dinput_strided": m * cs * s + K * n * 4 + K * cin * cs * s + n * cin * s,
+            "dfilter_strided": n * cin * s + m * cs * s + 8 * Ps + 4 * (K + 1) + K * cin * cs * 4,
+        }
+        return f, b
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(inp, step_flops_fn, budget):
+    """Times the oracle on the same step, stage by stage, until the budget is spent."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import conv as OC
+    from oracle import kmap as OK
+    import workloads as W
+
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    c, sh, b = inp["coords"], inp["shape"], inp["batch"]
+    done, spent, flops = [], 0.0, 0.0
+    state = {}
+
+    def st_kmap_subm():
+        state["nbr"] = OK.subm_kmap(c, sh, 3)
+        state["P"] = int((state["nbr"] >= 0).sum())
+
+    def st_fwd():
+        state["y"] = OC.conv_fwd(inp["feats"], inp["w3"], None, state["nbr"])
+
+    def st_k1():
+        OC.conv_fwd(state["y"], inp["w1"], None, np.arange(c.shape[0])[None])
+
+    def st_din():
+        OC.conv_bwd_input(inp["grad"], inp["w3"], state["nbr"], c.shape[0])
+
+    def st_dw():
+        OC.conv_bwd_filter(inp["feats"], inp["grad"], state["nbr"])
+
+    def st_kmap_str():
+        state["s"] = OK.strided_kmap(c, b, sh, 3, 2, 1, 1)
+        state["Ps"] = int((state["s"]["nbr_out"] >= 0).sum())
+        state["gs"] = W.grad_for(inp["grad_rng"], state["s"]["out_coords"].shape[0], inp["ws"].shape[2],
+                                 inp["dtype"])
+
+    def st_fwd_s():
+        OC.conv_fwd(inp["feats"], inp["ws"], None, state["s"]["nbr_out"])
+
+    def st_din_s():
+        OC.conv_bwd_input(state["gs"], inp["ws"], state["s"]["nbr_out"], c.shape[0])
+
+    def st_dw_s():
+        OC.conv_bwd_filter(inp["feats"], state["gs"], state["s"]["nbr_out"])
+
+    stages = [("kmap_subm", st_kmap_subm), ("fwd_subm", st_fwd), ("fwd_k1", st_k1), ("dinput_subm", st_din),
+              ("dfilter_subm", st_dw), ("kmap_strided", st_kmap_str), ("fwd_strided", st_fwd_s),
+              ("dinput_strided", st_din_s), ("dfilter_strided", st_dw_s)]
+    times = {}
+    for name, fn in stages:
+        if spent > budget:
+            break
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        times[name] = dt
+        spent += dt
+        done.append(name)
+        flops += step_flops_fn(name, state)
+    return {"value": flops / spent / 1e12 if spent > 0 else None, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": ("whole step" if len(done) == len(stages) else f"first {len(done)} of {len(stages)} stages")
+                      + f" ({', '.join(done)}), {spent:.1f} s, numpy fp64 on {threads} BLAS threads",
+            "stage_s": {k: round(v, 3) for k, v in times.items()},
+            "kmap_voxels_per_s": c.shape[0] / times["kmap_subm"] if "kmap_subm" in times else None}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the per-sample sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    inp = make_inputs(args.workload)
+    step = Step(inp, dev)
+    flops, bytes_ = step.work()
+    total_flop = sum(flops.values())
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    events = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)] for k in step.names}
+    stage_ms = {k: 0.0 for k in step.names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run({k: events[k][i] for k in step.names})
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for k in step.names:
+        stage_ms[k] = sum(a.elapsed_time(b) for a, b in events[k]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bb = torch.empty_like(a)
+        bb.copy_(a)
+        torch.cuda.synchronize()
+
+    dtype = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[inp["dtype"]]
+    stages = {}
+    for k in step.names:
+        t = stage_ms[k] * 1e-3
+        stages[k] = {"ms": round(stage_ms[k], 4),
+                     "TFLOP/s": round(flops[k] / t / 1e12, 2) if k in flops and t > 0 else None,
+                     "alg_GB/s": round(bytes_[k] / t / 1e9, 1) if t > 0 else None}
+    dom = max(SINGLE_KERNEL_STAGES, key=lambda k: stage_ms[k])
+    t_dom = stage_ms[dom] * 1e-3
+    ai = flops[dom] / bytes_[dom]
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(bytes_[dom] / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = f"k_conv ({dom})"
+    roof["algorithmic_bytes_per_launch"] = bytes_[dom]
+    roof["flop_per_launch"] = flops[dom]
+    roof["avg_launch_ms"] = round(stage_ms[dom], 4)
+
+    kmap_vps = step.n / (stage_ms["kmap_subm"] * 1e-3)
+    out = {
+        "metric": "effective TFLOP/s of SubMConv3d fwd (occupied pairs) + kmap voxels/s, 1 MI355X",
+        "value": round(total_flop / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": inp["name"], "n_voxels": step.n, "pairs_subm_k3": step.P,
+                   "n_out_strided": step.m, "pairs_strided": step.Ps,
+                   "channels": [int(step.w3.shape[1]), int(step.w3.shape[2]), int(step.ws.shape[2])]},
+        "subm_fwd_TFLOP/s": stages["fwd_subm"]["TFLOP/s"],
+        "kmap_voxels_per_s": round(kmap_vps, 1),
+        "stages": stages,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        def stage_flops(name, state):
+            cin, c1, cs = inp["w3"].shape[1], inp["w3"].shape[2], inp["ws"].shape[2]
+            n = inp["coords"].shape[0]
+            return {"fwd_subm": 2 * state.get("P", 0) * cin * c1, "fwd_k1": 2 * n * c1 * inp["w1"].shape[2],
+                    "dinput_subm": 2 * state.get("P", 0) * cin * c1, "dfilter_subm": 2 * state.get("P", 0) * cin * c1,
+                    "fwd_strided": 2 * state.get("Ps", 0) * cin * cs,
+                    "dinput_strided": 2 * state.get("Ps", 0) * cin * cs,
+                    "dfilter_strided": 2 * state.get("Ps", 0) * cin * cs}.get(name, 0)
+        out["cpu_baseline"] = cpu_baseline(inp, stage_flops, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -221,8 +221,12 @@ def workload(name: str, with_grad: bool = False) -> Workload:
         if name == "subm_k3_f16_lidar120k":
             w = _to_dtype(_normal(g["weight"], (27, 64, 64), 1.0 / np.sqrt(27 * 64)), torch.float16)
             grad = _to_dtype(_normal(g["grad"], (n, 64)), torch.float16) if with_grad else None
-            return Workload(name, coords, 2, (41, 1600, 1408), 3, 1, 1, 1, True, 64, 64,
-                            torch.float16, feats, w, None, grad)
+            wl = Workload(name, coords, 2, (41, 1600, 1408), 3, 1, 1, 1, True, 64, 64,
+                          torch.float16, feats, w, None, grad)
+            # a following k=1 layer (per-voxel linear, 64 -> 64)
+            wl.extra["weight_k1"] = _to_dtype(_normal(g["weight2"], (1, 64, 64), 1.0 / np.sqrt(64)),
+                                              torch.float16)
+            return wl
         g4 = _rngs(4)
         w = _to_dtype(_normal(g4["weight"], (27, 64, 128), 1.0 / np.sqrt(27 * 64)), torch.float16)
         wl = Workload(name, coords, 2, (41, 1600, 1408), 3, 2, 1, 1, False, 64, 128,
