@@ -97,7 +97,7 @@ class Step:
         self.n = self.coords.shape[0]
         self.dev = dev
         # strided output size and its upstream gradient, drawn once
-        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False)
+        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, orders=True)
         self.m = km["n_out"]
         self.gs = t(W.grad_for(inp["grad_rng"], self.m, self.ws.shape[2], inp["dtype"]))
         ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3)
@@ -116,28 +116,29 @@ class Step:
                 E[name][i].record()
 
         mark("kmap_subm", 0)
-        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3)
+        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         mark("kmap_subm", 1)
         mark("fwd_subm", 0)
-        y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"])
+        y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
         mark("fwd_subm", 1)
         mark("fwd_k1", 0)
         spc.subm_conv_fwd(y, self.w1, None, None)
         mark("fwd_k1", 1)
         mark("dinput_subm", 0)
-        spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n)
+        spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n, km["order"])
         mark("dinput_subm", 1)
         mark("dfilter_subm", 0)
         spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
         mark("dfilter_subm", 1)
         mark("kmap_strided", 0)
-        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m)
+        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
+                            orders=True)
         mark("kmap_strided", 1)
         mark("fwd_strided", 0)
-        spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"])
+        spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"], ks["order"])
         mark("fwd_strided", 1)
         mark("dinput_strided", 0)
-        spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n)
+        spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n, ks["order_in"])
         mark("dinput_strided", 1)
         mark("dfilter_strided", 0)
         spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"])
@@ -157,12 +158,12 @@ class Step:
             "dfilter_strided": 2 * Ps * cin * cs,
         }
         b = {
-            "kmap_subm": n * (16 + 4 * K) + 8 * P + 4 * (K + 1),
+            "kmap_subm": n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n,
             "fwd_subm": n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s,
             "fwd_k1": n * c1 * s + c1 * self.w1.shape[2] * s + n * self.w1.shape[2] * s,
             "dinput_subm": n * c1 * s + K * n * 4 + K * cin * c1 * s + n * cin * s,
             "dfilter_subm": n * cin * s + n * c1 * s + 8 * P + 4 * (K + 1) + K * cin * c1 * 4,
-            "kmap_strided": n * 16 + m * 16 + 4 * K * (m + n) + 8 * Ps + 4 * (K + 1),
+            "kmap_strided": n * 16 + m * 16 + 4 * K * (m + n) + 8 * Ps + 4 * (K + 1) + 4 * (m + n),
             "fwd_strided": n * cin * s + K * m * 4 + K * cin * cs * s + m * cs * s,
             "dinput_strided": m * cs * s + K * n * 4 + K * cin * cs * s + n * cin * s,
             "dfilter_strided": n * cin * s + m * cs * s + 8 * Ps + 4 * (K + 1) + K * cin * cs * 4,

@@ -84,28 +84,32 @@ spc_status spc_kmap_workspace(const spc_geom* g, int64_t n_in, size_t* bytes);
 /*
  * Kernel map ("indice pairs"; spconv's get_indice_pairs_implicit_gemm on the
  * context7 spconv page, INT8_GUIDE.md snippet).  Builds a GPU hash table over
- * the packed keys ((b*Z + z)*Y + y)*X + x of the input rows and probes it for
- * every kernel offset.
+ * the packed keys ((b*Z + z)*Y + y)*X + x of the input rows.  Maps are
+ * row-major: entry k of a row is that row's neighbour through offset k.
  *
  * subm != 0 (the MLX page's build_indice_map, computed on the GPU):
- *   nbr       [K, n_in] int32: nbr[k*n_in + i] = row j with coords[j] =
+ *   nbr       [n_in, K] int32: nbr[i*K + k] = row j with coords[j] =
  *             coords[i] + d_k in the same sample, else -1.  *n_out = n_in.
- *   out_coords, out_cap, nbr_in: unused (may be NULL / 0).
+ *   out_coords, out_cap, nbr_in, order_in: unused (may be NULL / 0).
  * subm == 0 (spconv USAGE.md, "Sparse Convolution"):
  *   out_coords [out_cap, 4] int32: the M output sites, sorted by (b, z, y, x).
- *   nbr       [K, M] int32 compact (row stride M, written at the start of a
- *             buffer of K*out_cap entries): input row read by output o through
+ *   nbr       [M, K] int32 (a buffer of out_cap*K entries): input row read by
+ *             output o through offset k, else -1.
+ *   nbr_in    [n_in, K] int32 (NULL ok): output row fed by input i through
  *             offset k, else -1.
- *   nbr_in    [K, n_in] int32 (NULL ok): output row fed by input i through
- *             offset k, else -1.
- *   *n_out    receives M.  The call synchronises `stream` once to learn M.
+ *   *n_out    receives M.  The call synchronises `stream` once, at its end.
  *   If out_coords is NULL the call only counts: *n_out = M, nothing else is
  *   written.  If M > out_cap it returns SPC_ERR_CAPACITY with *n_out = M.
  *   An empty output (M = 0) is valid.
  * Pair lists (both kinds; all three NULL or all three set): for each offset
- *   k, the pairs (nbr[k][o], o) with nbr[k][o] >= 0 in ascending o, as CSR:
- *   pair_ptr [K+1] int32 (offset k owns [pair_ptr[k], pair_ptr[k+1])),
+ *   k, the pairs (nbr[o*K + k], o) with nbr[o*K + k] >= 0 in ascending o, as
+ *   CSR: pair_ptr [K+1] int32 (offset k owns [pair_ptr[k], pair_ptr[k+1])),
  *   pair_in / pair_out [pair_cap] int32, pair_cap >= K * n_in.
+ * Processing orders (NULL ok): order [rows of nbr] receives the rows of nbr
+ *   sorted by their neighbour mask (bit k set iff entry k >= 0), ties by row
+ *   index; order_in [n_in] (strided only) does the same for nbr_in.  The
+ *   convolutions take these orders to gather rows with equal neighbour sets
+ *   into the same tiles.  For K > 32 they are the identity.
  * coord_err (NULL ok): device int32 receiving SPC_COORD_* bits.  Rows flagged
  *   out of range are left out of the table; for a duplicate the map refers to
  *   one of the equal rows.  The strided call also returns SPC_ERR_COORD.
@@ -116,13 +120,16 @@ spc_status spc_build_kmap(const spc_geom* g, const int32_t* coords, int64_t n_in
                           int32_t* out_coords, int64_t out_cap, int64_t* n_out,
                           int32_t* nbr, int32_t* nbr_in,
                           int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
+                          int32_t* order, int32_t* order_in,
                           int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Submanifold forward (the MLX page's module docstring formula):
- *   out[c] = bias + sum_k feats[nbr[k][c]] @ W[k]   over offsets with nbr >= 0.
+ *   out[c] = bias + sum_k feats[nbr[c*K + k]] @ W[k]   over offsets with nbr >= 0.
  * feats [n, cin], weight [K, cin, cout], bias [cout] fp32 (NULL ok),
- * nbr [K, n] from spc_build_kmap, out [n, cout].  K == 1 is the per-voxel
+ * nbr [n, K] from spc_build_kmap, out [n, cout].  order (NULL ok) is the
+ * processing order from spc_build_kmap; it changes only which rows share a
+ * tile, never a result.  K == 1 is the per-voxel
  * linear layer out = feats @ W[0] + bias (MLX page, k=1 path; the Hygon
  * spconv-das README routes 1x1 convolutions to a GEMM); nbr may then be NULL.
  * One fused kernel: gathered rows feed MFMA tiles directly, the fp32
@@ -130,32 +137,34 @@ spc_status spc_build_kmap(const spc_geom* g, const int32_t* coords, int64_t n_in
  */
 spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int64_t n, int32_t cin,
                              const void* weight, int32_t K, int32_t cout, const float* bias,
-                             const int32_t* nbr, void* out, hipStream_t stream);
+                             const int32_t* nbr, const int32_t* order, void* out, hipStream_t stream);
 
 /*
- * Strided forward: out[o] = bias + sum_k feats[nbr_out[k][o]] @ W[k] for the
- * n_out output rows of a strided spc_build_kmap (nbr_out = its compact nbr).
+ * Strided forward: out[o] = bias + sum_k feats[nbr_out[o*K + k]] @ W[k] for
+ * the n_out output rows of a strided spc_build_kmap (nbr_out = its nbr,
+ * order = its order, NULL ok).
  */
 spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
                                const void* weight, int32_t K, int32_t cout, const float* bias,
-                               const int32_t* nbr_out, int64_t n_out, void* out,
+                               const int32_t* nbr_out, const int32_t* order, int64_t n_out, void* out,
                                hipStream_t stream);
 
 /*
  * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput
  * and dfilter): din[i] = sum over (k, o) with map_fwd[k][o] = i of
  * dout[o] @ W[k]^T, computed output-stationary over the input rows:
- *   map_is_subm != 0: map is the submanifold nbr [K, n_in] (n_out == n_in); by
- *                     symmetry din[i] = sum_k dout[nbr[K-1-k][i]] @ W[k]^T.
- *   map_is_subm == 0: map is the strided nbr_in [K, n_in];
- *                     din[i] = sum_k dout[nbr_in[k][i]] @ W[k]^T.
- * K == 1 with map NULL is the per-voxel case (n_out == n_in).
+ *   map_is_subm != 0: map is the submanifold nbr [n_in, K] (n_out == n_in); by
+ *                     symmetry din[i] = sum_k dout[nbr[i*K + K-1-k]] @ W[k]^T.
+ *   map_is_subm == 0: map is the strided nbr_in [n_in, K];
+ *                     din[i] = sum_k dout[nbr_in[i*K + k]] @ W[k]^T.
+ * K == 1 with map NULL is the per-voxel case (n_out == n_in).  order (NULL
+ * ok) is the order of the map's rows (order for subm, order_in for strided).
  * dout [n_out, cout], weight [K, cin, cout], din [n_in, cin] (overwritten).
  */
 spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int64_t n_out, int32_t cout,
                               const void* weight, int32_t K, int32_t cin,
-                              const int32_t* map, int32_t map_is_subm, int64_t n_in,
-                              void* din, hipStream_t stream);
+                              const int32_t* map, int32_t map_is_subm, const int32_t* order,
+                              int64_t n_in, void* din, hipStream_t stream);
 
 /* Host only.  Workspace bytes spc_conv_bwd_filter needs. */
 spc_status spc_conv_bwd_filter_workspace(int64_t n_in, int64_t n_out, int32_t cin, int32_t cout,

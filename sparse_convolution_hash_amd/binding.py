@@ -71,10 +71,11 @@ def lib() -> ctypes.CDLL:
     sig = {
         "spc_out_shape": [GP, ctypes.POINTER(_I32)],
         "spc_kmap_workspace": [GP, _I64, ctypes.POINTER(_SZ)],
-        "spc_build_kmap": [GP, _P, _I64, _P, _I64, ctypes.POINTER(_I64), _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P],
-        "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P],
-        "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _I64, _P, _P],
-        "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _I64, _P, _P],
+        "spc_build_kmap": [GP, _P, _I64, _P, _I64, ctypes.POINTER(_I64), _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                           _SZ, _P],
+        "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P],
+        "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
+        "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     }
@@ -132,16 +133,18 @@ def kmap_workspace(g: Geom, n_in: int) -> int:
 
 
 def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
-               subm: bool = True, pairs: bool = True, with_nbr_in: bool = True,
+               subm: bool = True, pairs: bool = True, with_nbr_in: bool = True, orders: bool = False,
                out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> dict:
     """Kernel map of int32 [N, 4] (b, z, y, x) coordinates (spc_build_kmap).
 
-    Returns a dict with ``nbr`` [K, n_out] (submanifold neighbour map or the
-    strided nbr_out), ``n_out``, ``coord_err`` (device int32 [1]) and, as
-    requested, ``out_coords`` [n_out, 4], ``nbr_in`` [K, N] and the CSR pair
-    lists ``pair_ptr`` [K+1], ``pair_in`` / ``pair_out`` (first pair_ptr[K]
-    entries valid).  A strided call without ``out_cap`` first asks the library
-    for the output count, then allocates exactly.
+    Returns a dict with ``nbr`` [n_out, K] (submanifold neighbour map or the
+    strided output-side map, row-major), ``n_out``, ``coord_err`` (device
+    int32 [1]) and, as requested, ``out_coords`` [n_out, 4], ``nbr_in`` [N, K],
+    the CSR pair lists ``pair_ptr`` [K+1], ``pair_in`` / ``pair_out`` (first
+    pair_ptr[K] entries valid) and the processing orders ``order`` (rows of
+    nbr) and ``order_in`` (rows of nbr_in).  A strided call without
+    ``out_cap`` first asks the library for the output count, then allocates
+    exactly.
     """
     _need(coords, "coords", torch.int32)
     if coords.dim() != 2 or coords.shape[1] != 4:
@@ -159,14 +162,17 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     i32 = dict(dtype=torch.int32, device=dev)
     if not subm and out_cap is None:
         st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, None, 0, ctypes.byref(n_out), None, None,
-                                  None, None, None, 0, _ptr(err), _ptr(workspace), workspace.numel(), stream)
+                                  None, None, None, 0, None, None, _ptr(err), _ptr(workspace), workspace.numel(),
+                                  stream)
         _check(st, "spc_build_kmap")
         out_cap = n_out.value
     cap = n if subm else int(out_cap)
     res = {"coord_err": err[:1]}
     out_coords = None if subm else torch.empty((max(cap, 1), 4), **i32)
     nbr = torch.empty(max(K * cap, 4), **i32)
-    nbr_in = torch.empty((K, n), **i32) if (not subm and with_nbr_in) else None
+    nbr_in = torch.empty((n, K), **i32) if (not subm and (with_nbr_in or orders)) else None
+    order = torch.empty(max(cap, 4), **i32) if orders else None
+    order_in = torch.empty(max(n, 4), **i32) if (orders and not subm) else None
     pp = pi = po = None
     if pairs:
         pp = torch.empty(K + 1, **i32)
@@ -174,15 +180,19 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
         po = torch.empty(max(K * n, 4), **i32)
     st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, _ptr(out_coords), cap, ctypes.byref(n_out),
                               _ptr(nbr), _ptr(nbr_in), _ptr(pp), _ptr(pi), _ptr(po), max(K * n, 0) if pairs else 0,
-                              _ptr(err), _ptr(workspace), workspace.numel(), stream)
+                              _ptr(order), _ptr(order_in), _ptr(err), _ptr(workspace), workspace.numel(), stream)
     _check(st, "spc_build_kmap")
     m = int(n_out.value)
     res["n_out"] = m
-    res["nbr"] = nbr[:K * m].view(K, m)
+    res["nbr"] = nbr[:K * m].view(m, K)
     if not subm:
         res["out_coords"] = out_coords[:m]
     if nbr_in is not None:
         res["nbr_in"] = nbr_in
+    if orders:
+        res["order"] = order[:m]
+        if order_in is not None:
+            res["order_in"] = order_in[:n]
     if pairs:
         res["pair_ptr"], res["pair_in"], res["pair_out"] = pp, pi, po
     return res
@@ -200,49 +210,57 @@ def _conv_checks(x, weight, bias, dev):
 
 
 def subm_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
-                  nbr: Optional[torch.Tensor], out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out = bias + sum_k feats[nbr[k]] @ W[k] (spc_subm_conv_fwd)."""
+                  nbr: Optional[torch.Tensor], order: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[c] = bias + sum_k feats[nbr[c, k]] @ W[k] (spc_subm_conv_fwd)."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     K, cin, cout = weight.shape
     n = feats.shape[0]
-    if nbr is not None:
-        _need(nbr, "nbr", torch.int32, dev)
+    for t, nm in ((nbr, "nbr"), (order, "order")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
     if out is None:
         out = torch.empty((n, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_subm_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), n, cin, _ptr(weight), K, cout, _ptr(bias),
-                                 _ptr(nbr), _ptr(out), _stream(dev))
+                                 _ptr(nbr), _ptr(order), _ptr(out), _stream(dev))
     _check(st, "spc_subm_conv_fwd")
     return out
 
 
 def sparse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
-                    nbr_out: torch.Tensor, n_out: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    nbr_out: torch.Tensor, n_out: int, order: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Strided forward over the n_out output rows of a strided kernel map (spc_sparse_conv_fwd)."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     _need(nbr_out, "nbr_out", torch.int32, dev)
+    if order is not None:
+        _need(order, "order", torch.int32, dev)
     K, cin, cout = weight.shape
     if out is None:
         out = torch.empty((n_out, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_sparse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,
-                                   _ptr(bias), _ptr(nbr_out), int(n_out), _ptr(out), _stream(dev))
+                                   _ptr(bias), _ptr(nbr_out), _ptr(order), int(n_out), _ptr(out), _stream(dev))
     _check(st, "spc_sparse_conv_fwd")
     return out
 
 
 def conv_bwd_input(dout: torch.Tensor, weight: torch.Tensor, map_: Optional[torch.Tensor], map_is_subm: bool,
-                   n_in: int, din: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   n_in: int, order: Optional[torch.Tensor] = None,
+                   din: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Gradient of the input features (spc_conv_bwd_input)."""
     dev = dout.device
     _conv_checks(dout, weight, None, dev)
-    if map_ is not None:
-        _need(map_, "map", torch.int32, dev)
+    for t, nm in ((map_, "map"), (order, "order")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
     K, cin, cout = weight.shape
     if din is None:
         din = torch.empty((n_in, cin), dtype=dout.dtype, device=dev)
     st = lib().spc_conv_bwd_input(_DTYPES[dout.dtype], _ptr(dout), dout.shape[0], cout, _ptr(weight), K, cin,
-                                  _ptr(map_), 1 if map_is_subm else 0, int(n_in), _ptr(din), _stream(dev))
+                                  _ptr(map_), 1 if map_is_subm else 0, _ptr(order), int(n_in), _ptr(din),
+                                  _stream(dev))
     _check(st, "spc_conv_bwd_input")
     return din
 

@@ -28,13 +28,16 @@ namespace {
 
 constexpr int CT = 256;          // threads per workgroup
 constexpr int NW = CT / WAVE;    // waves per workgroup
-constexpr int KTILE = 32;        // offsets whose map rows are staged at once
+// s_waitcnt vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+constexpr int WAIT_VMCNT0 = 0x0F70;
+constexpr int KTILE = 28;        // offsets whose map rows are staged at once (a 3x3x3 kernel in one go)
 
 struct ConvArgs {
     const void* x;       // gathered operand [n_src, CK]
     const void* w;       // weights [K, cin, cout]
     const float* bias;   // [CN] or NULL
-    const int32_t* map;  // [K, n_rows] or NULL (identity, K == 1)
+    const int32_t* map;  // [n_rows, K] row-major, or NULL (identity, K == 1)
+    const int32_t* order;  // processing order of the rows, or NULL (natural order)
     void* y;             // [n_rows, CN]
     int32_t n_rows, n_src, K;
     int32_t CK, CN;      // contraction / output channels
@@ -51,29 +54,62 @@ __device__ __forceinline__ int slab_off(int kb, int n) {
     return kb * (BN * 16 + 16) + n * 16;
 }
 
-// Stages B_k (slab ws of W) into LDS.  TRANS: B[kk][n] = W[ws][kk][n] (the
-// forward; W rows are output channels apart, so E x E blocks are transposed
-// in registers).  !TRANS: B[kk][n] = W[ws][n][kk] (dinput; already
-// contraction-contiguous).  Chunks beyond CK are zero.
+// Weight slab staging.  TRANS: B[kk][n] = W[ws][kk][n] (the forward; W rows
+// are output channels apart, so E x E blocks are transposed in registers).
+// !TRANS: B[kk][n] = W[ws][n][kk] (dinput; already contraction-contiguous).
+// Chunks beyond CK are zero.  A thread holds up to WREG 16-byte registers of
+// the slab so the next offset's slab can be in flight during the MFMAs; any
+// rest of a large slab is copied when it is stored.
+constexpr int WREG = 8;
+
 template <typename TT, int BN, bool TRANS>
-__device__ __forceinline__ void stage_slab(char* lds, const ConvArgs& a, int ws, int col0) {
+struct WStage {
     using S = typename TT::storage;
-    constexpr int E = TT::E;
-    const S* w = static_cast<const S*>(a.w);
-    const int ckc = a.CK / E;  // real chunks
-    if (TRANS) {
-        constexpr int NBK = BN / E;
-        for (int idx = threadIdx.x; idx < a.kch * NBK; idx += CT) {
-            const int kb = idx % a.kch, nbk = idx / a.kch;
-            u32x4 in[E];
-            if (kb < ckc) {
-                const S* src = w + (int64_t(ws) * a.cin + kb * E) * a.cout + col0 + nbk * E;
+    static constexpr int E = TT::E;
+    // one item: an E x E block (TRANS) or one 16-byte chunk (!TRANS)
+    static constexpr int ITEM_REGS = TRANS ? E : 1;
+    static constexpr int PRE = WREG / ITEM_REGS;  // items prefetched per thread
+    u32x4 r[WREG];
+    // per prefetched item, fixed for the whole kernel: element offset inside a
+    // weight slab (-1: zero padding or no item) and LDS byte offset
+    int32_t gofs[PRE], lofs[PRE];
+
+    __device__ static int items(const ConvArgs& a) { return TRANS ? a.kch * (BN / E) : a.kch * BN; }
+
+    __device__ static void place(const ConvArgs& a, int col0, int idx, int32_t& g, int32_t& l) {
+        const int kb = idx % a.kch, q = idx / a.kch;  // q: channel block (TRANS) or channel
+        const bool real = kb < a.CK / E;
+        if (TRANS) {
+            g = real ? kb * E * a.cout + col0 + q * E : -1;
+            l = slab_off<BN>(kb, q * E);
+        } else {
+            g = real ? (col0 + q) * a.cout + kb * E : -1;
+            l = slab_off<BN>(kb, q);
+        }
+    }
+
+    __device__ void init(const ConvArgs& a, int col0) {
+        const int n = items(a);
 #pragma unroll
-                for (int e = 0; e < E; ++e) in[e] = ld16(src + int64_t(e) * a.cout);
-            } else {
+        for (int p = 0; p < PRE; ++p) {
+            const int idx = threadIdx.x + p * CT;
+            gofs[p] = -1;
+            lofs[p] = -1;
+            if (idx < n) place(a, col0, idx, gofs[p], lofs[p]);
+        }
+    }
+
+    __device__ static void load_at(u32x4* dst, const S* w, int32_t g, int cout) {
+        if (TRANS) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) in[e] = zero4();
-            }
+            for (int e = 0; e < E; ++e) dst[e] = g >= 0 ? ld16(w + g + int64_t(e) * cout) : zero4();
+        } else {
+            dst[0] = g >= 0 ? ld16(w + g) : zero4();
+        }
+    }
+
+    __device__ static void store_at(char* lds, const u32x4* in, int32_t l) {
+        if (TRANS) {
             if constexpr (E == 8) {
                 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
                 u16x8 v[8];
@@ -82,7 +118,7 @@ __device__ __forceinline__ void stage_slab(char* lds, const ConvArgs& a, int ws,
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     u16x8 o = {v[0][j], v[1][j], v[2][j], v[3][j], v[4][j], v[5][j], v[6][j], v[7][j]};
-                    st16(lds + slab_off<BN>(kb, nbk * 8 + j), __builtin_bit_cast(u32x4, o));
+                    st16(lds + l + j * 16, __builtin_bit_cast(u32x4, o));
                 }
             } else {
                 const uint32_t m[4][4] = {{in[0].x, in[0].y, in[0].z, in[0].w},
@@ -90,36 +126,77 @@ __device__ __forceinline__ void stage_slab(char* lds, const ConvArgs& a, int ws,
                                           {in[2].x, in[2].y, in[2].z, in[2].w},
                                           {in[3].x, in[3].y, in[3].z, in[3].w}};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    st16(lds + slab_off<BN>(kb, nbk * 4 + j), u32x4{m[0][j], m[1][j], m[2][j], m[3][j]});
+                for (int j = 0; j < 4; ++j) st16(lds + l + j * 16, u32x4{m[0][j], m[1][j], m[2][j], m[3][j]});
             }
-        }
-    } else {
-        for (int idx = threadIdx.x; idx < a.kch * BN; idx += CT) {
-            const int kb = idx % a.kch, n = idx / a.kch;
-            u32x4 v = zero4();
-            if (kb < ckc) v = ld16(w + (int64_t(ws) * a.cin + col0 + n) * a.cout + kb * E);
-            st16(lds + slab_off<BN>(kb, n), v);
+        } else {
+            st16(lds + l, in[0]);
         }
     }
+
+    __device__ void load(const ConvArgs& a, int ws) {
+        const S* w = static_cast<const S*>(a.w) + int64_t(ws) * a.cin * a.cout;
+#pragma unroll
+        for (int p = 0; p < PRE; ++p)
+            if (lofs[p] >= 0) load_at(r + p * ITEM_REGS, w, gofs[p], a.cout);
+    }
+
+    __device__ void store(char* lds, const ConvArgs& a, int ws, int col0) const {
+#pragma unroll
+        for (int p = 0; p < PRE; ++p)
+            if (lofs[p] >= 0) store_at(lds, r + p * ITEM_REGS, lofs[p]);
+        const int n = items(a);
+        if (threadIdx.x + PRE * CT >= n) return;
+        const S* w = static_cast<const S*>(a.w) + int64_t(ws) * a.cin * a.cout;
+        for (int idx = threadIdx.x + PRE * CT; idx < n; idx += CT) {  // rest of a large slab
+            int32_t g, l;
+            place(a, col0, idx, g, l);
+            u32x4 t[ITEM_REGS];
+            load_at(t, w, g, a.cout);
+            store_at(lds, t, l);
+        }
+    }
+};
+
+template <typename TT, int RB, int KCMAX>
+__device__ __forceinline__ bool gather_rows(u32x4 (&af)[RB][KCMAX], const ConvArgs& a, const int32_t* tile_k,
+                                            int wave, int lr, int lg) {
+    using S = typename TT::storage;
+    constexpr int E = TT::E;
+    const S* x = static_cast<const S*>(a.x);
+    const int KC = a.kch / 4;
+    bool any = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int32_t src = tile_k[(wave * RB + rb) * 16 + lr];
+        any |= src >= 0;
+        const S* p = x + int64_t(src) * a.CK + lg * E;
+#pragma unroll
+        for (int kc = 0; kc < KCMAX; ++kc) {
+            af[rb][kc] = zero4();
+            if (kc < KC && src >= 0 && (kc * 4 + lg) * E < a.CK) af[rb][kc] = ld16(p + kc * 4 * E);
+        }
+    }
+    return __any(any);
 }
 
 template <typename TT, int RB, int NB, bool TRANS, int KCMAX>
 __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     using S = typename TT::storage;
-    constexpr int E = TT::E;
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB * 16;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    char* slab = lds;
-    int32_t* tile = reinterpret_cast<int32_t*>(lds + a.kch * (BN * 16 + 16));   // [KTILE][BM]
-    int32_t* flags = tile + KTILE * BM;                                            // [KTILE]
+    // the two slab buffers are addressed arithmetically from the __shared__
+    // base (a pointer table would hide the address space and turn the LDS
+    // reads into flat loads that wait on the global prefetches)
+    const int slab_bytes = a.kch * (BN * 16 + 16);
+    int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BM]
+    int32_t* flags = tile + KTILE * BM;                                // [KTILE]
+    int32_t* list = flags + KTILE;                                     // [KTILE + 1]
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = blockIdx.x * BM, col0 = blockIdx.y * BN;
     const int KC = a.kch / 4;  // MFMA steps along CK
-    const S* x = static_cast<const S*>(a.x);
 
     f32x4_t acc[RB][NB];
 #pragma unroll
@@ -127,52 +204,73 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    WStage<TT, BN, TRANS> wst;
+    wst.init(a, col0);
+    u32x4 acur[RB][KCMAX], anext[RB][KCMAX];
     for (int kt0 = 0; kt0 < a.K; kt0 += KTILE) {
         const int kt = min(KTILE, a.K - kt0);
-        __syncthreads();  // earlier readers of tile / flags / slab are done
+        __syncthreads();  // earlier readers of tile / list / slabs are done
         if (threadIdx.x < KTILE) flags[threadIdx.x] = 0;
         __syncthreads();
         for (int idx = threadIdx.x; idx < kt * BM; idx += CT) {
             const int k = idx / BM, r = idx - k * BM, row = row0 + r;
             int32_t v = -1;
-            if (row < a.n_rows) v = a.map ? a.map[int64_t(kt0 + k) * a.n_rows + row] : row;
+            if (row < a.n_rows) {
+                const int32_t src = a.order ? a.order[row] : row;
+                if ((unsigned)src < (unsigned)a.n_rows) v = a.map ? a.map[int64_t(src) * a.K + kt0 + k] : src;
+            }
             if ((unsigned)v >= (unsigned)a.n_src) v = -1;
             tile[idx] = v;
             if (v >= 0) flags[k] = 1;
         }
         __syncthreads();
-        for (int k = 0; k < kt; ++k) {
-            if (!flags[k]) continue;  // no row of this workgroup reads offset k
-            const int kg = kt0 + k;
-            // gather this wave's rows (in flight while the slab is staged)
-            u32x4 af[RB][KCMAX];
-            bool any = false;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int32_t src = tile[k * BM + (wave * RB + rb) * 16 + lr];
-                any |= src >= 0;
-                const S* p = x + int64_t(src) * a.CK + lg * E;
+        if (wave == 0) {  // compact list of the offsets that hit this tile
+            const bool f = lane < kt && flags[lane];
+            const uint64_t b = __ballot(f);
+            if (f) list[__popcll(b & ((1ull << lane) - 1))] = lane;
+            if (lane == 0) list[KTILE] = __popcll(b);
+        }
+        __syncthreads();
+        const int nk = list[KTILE];
+        if (nk == 0) continue;
+
+        auto slab_of = [&](int j) { const int kg = kt0 + list[j]; return a.w_rev ? a.K - 1 - kg : kg; };
+        wst.load(a, slab_of(0));
+        bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, tile + list[0] * BM, wave, lr, lg);
+        wst.store(lds, a, slab_of(0), col0);
+        // drain the prologue's gathers here, so that inside the loop the only
+        // loads in flight are the next offset's prefetches and the MFMAs need
+        // not wait for them
+        __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
+        __syncthreads();
+        for (int j = 0; j < nk; ++j) {
+            const bool has_next = j + 1 < nk;
+            bool any_next = false;
+            if (has_next) {
+                wst.load(a, slab_of(j + 1));
+                any_next = gather_rows<TT, RB, KCMAX>(anext, a, tile + list[j + 1] * BM, wave, lr, lg);
+            }
+            if (any_cur) {
+                const char* sl = lds + (j & 1) * slab_bytes;
 #pragma unroll
                 for (int kc = 0; kc < KCMAX; ++kc) {
-                    af[rb][kc] = zero4();
-                    if (kc < KC && src >= 0 && (kc * 4 + lg) * E < a.CK) af[rb][kc] = ld16(p + kc * 4 * E);
+                    if (kc >= KC) break;
+                    u32x4 bf[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], acur[rb][kc], acc[rb][nb]);
                 }
             }
-            __syncthreads();  // the previous slab is no longer read
-            stage_slab<TT, BN, TRANS>(slab, a, a.w_rev ? a.K - 1 - kg : kg, col0);
+            if (has_next) wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(j + 1), col0);
             __syncthreads();
-            if (!__any(any)) continue;  // wave-uniform: none of this wave's rows hit
 #pragma unroll
-            for (int kc = 0; kc < KCMAX; ++kc) {
-                if (kc >= KC) break;
-                u32x4 bf[NB];
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(slab + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], af[rb][kc], acc[rb][nb]);
-            }
+                for (int kc = 0; kc < KCMAX; ++kc) acur[rb][kc] = anext[rb][kc];
+            any_cur = any_next;
         }
     }
 
@@ -181,8 +279,12 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     S* y = static_cast<S*>(a.y);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int row = row0 + (wave * RB + rb) * 16 + lr;
+        int row = row0 + (wave * RB + rb) * 16 + lr;
         if (row >= a.n_rows) continue;
+        if (a.order) {
+            row = a.order[row];
+            if ((unsigned)row >= (unsigned)a.n_rows) continue;
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int ch = col0 + nb * 16 + lg * 4;
@@ -203,7 +305,7 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB_DEFAULT * 16;
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
-    const size_t lds = size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + KTILE * 4;
+    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 1) * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
@@ -246,7 +348,7 @@ spc_status run_conv(spc_dtype dt, ConvArgs& a, bool trans, hipStream_t stream) {
 
 spc_status check_common(spc_dtype dt, int64_t n_rows, int64_t n_src, int32_t cin, int32_t cout, int32_t K,
                         const void* x, const void* w, const float* bias, const void* y, const int32_t* map,
-                        bool map_required) {
+                        const int32_t* order, bool map_required) {
     if (dt != SPC_F32 && dt != SPC_F16 && dt != SPC_BF16) return fail(SPC_ERR_ARG, "unknown dtype %d", int(dt));
     if (n_rows < 0 || n_rows >= (int64_t(1) << 31) || n_src < 0 || n_src >= (int64_t(1) << 31))
         return fail(SPC_ERR_ARG, "row counts out of range");
@@ -258,7 +360,7 @@ spc_status check_common(spc_dtype dt, int64_t n_rows, int64_t n_src, int32_t cin
         if (n_src > 0 && !x) return fail(SPC_ERR_ARG, "input pointer is NULL");
         if (map_required && !map) return fail(SPC_ERR_ARG, "map is NULL");
     }
-    const void* ptrs[] = {x, w, bias, y, map};
+    const void* ptrs[] = {x, w, bias, y, map, order};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
     return SPC_OK;
@@ -271,35 +373,39 @@ using namespace spc;
 
 extern "C" spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int64_t n, int32_t cin,
                                         const void* weight, int32_t K, int32_t cout, const float* bias,
-                                        const int32_t* nbr, void* out, hipStream_t stream) {
+                                        const int32_t* nbr, const int32_t* order, void* out, hipStream_t stream) {
     clear_error();
-    spc_status st = check_common(dtype, n, n, cin, cout, K, feats, weight, bias, out, nbr, K != 1);
+    spc_status st = check_common(dtype, n, n, cin, cout, K, feats, weight, bias, out, nbr, order, K != 1);
     if (st != SPC_OK) return st;
-    ConvArgs a{feats, weight, bias, K == 1 ? nbr : nbr, out, int32_t(n), int32_t(n), K, cin, cout, cin, cout, 0, 0};
+    // a 1x1x1 map is the identity: skip reading it
+    ConvArgs a{feats, weight, bias, K == 1 ? nullptr : nbr, K == 1 ? nullptr : order, out, int32_t(n), int32_t(n),
+               K, cin, cout, cin, cout, 0, 0};
     return run_conv(dtype, a, true, stream);
 }
 
 extern "C" spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
                                           const void* weight, int32_t K, int32_t cout, const float* bias,
-                                          const int32_t* nbr_out, int64_t n_out, void* out, hipStream_t stream) {
+                                          const int32_t* nbr_out, const int32_t* order, int64_t n_out, void* out,
+                                          hipStream_t stream) {
     clear_error();
-    spc_status st = check_common(dtype, n_out, n_in, cin, cout, K, feats, weight, bias, out, nbr_out, true);
+    spc_status st = check_common(dtype, n_out, n_in, cin, cout, K, feats, weight, bias, out, nbr_out, order, true);
     if (st != SPC_OK) return st;
-    ConvArgs a{feats, weight, bias, nbr_out, out, int32_t(n_out), int32_t(n_in), K, cin, cout, cin, cout, 0, 0};
+    ConvArgs a{feats, weight, bias, nbr_out, order, out, int32_t(n_out), int32_t(n_in), K, cin, cout, cin, cout, 0, 0};
     return run_conv(dtype, a, true, stream);
 }
 
 extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int64_t n_out, int32_t cout,
                                          const void* weight, int32_t K, int32_t cin, const int32_t* map,
-                                         int32_t map_is_subm, int64_t n_in, void* din, hipStream_t stream) {
+                                         int32_t map_is_subm, const int32_t* order, int64_t n_in, void* din,
+                                         hipStream_t stream) {
     clear_error();
     const bool identity = (K == 1 && map == nullptr);
-    spc_status st = check_common(dtype, n_in, n_out, cin, cout, K, dout, weight, nullptr, din, map, !identity);
+    spc_status st = check_common(dtype, n_in, n_out, cin, cout, K, dout, weight, nullptr, din, map, order, !identity);
     if (st != SPC_OK) return st;
     if ((map_is_subm || identity) && n_out != n_in)
         return fail(SPC_ERR_ARG, "submanifold dinput needs n_out == n_in (%lld vs %lld)", (long long)n_out, (long long)n_in);
     // din rows gather dout rows: contraction over cout, output channels cin
-    ConvArgs a{dout, weight, nullptr, map, din, int32_t(n_in), int32_t(n_out), K, cout, cin, cin, cout,
-               map_is_subm ? 1 : 0, 0};
+    ConvArgs a{dout, weight, nullptr, map, identity ? nullptr : order, din, int32_t(n_in), int32_t(n_out), K, cout,
+               cin, cin, cout, map_is_subm ? 1 : 0, 0};
     return run_conv(dtype, a, false, stream);
 }

@@ -4,13 +4,14 @@
 //   dbias = sum over rows o of dy[o]                                 [cout]
 //
 // (the Hygon spconv-das README's dfilter, "Public Interface Support").  The
-// contraction runs over pairs, so each workgroup takes one offset, one
-// channel tile and one fixed-size chunk of that offset's CSR pair list; it
+// contraction runs over pairs.  The CSR pair lists are cut into chunks of
+// equal length (never straddling two offsets) and a persistent grid walks
+// them, so offsets with many pairs do not serialise the pass.  A chunk
 // gathers 64 pairs at a time, transposes them in registers into
 // channel-major LDS tiles (the MFMA fragments need 16 bytes of consecutive
-// pairs per channel) and accumulates fp32 on MFMA.  Each chunk writes a
-// partial tile; a second kernel sums the partials in chunk order, so the
-// result does not depend on scheduling.
+// pairs per channel) and accumulates fp32 on MFMA; it writes one partial
+// tile, and a second kernel sums each offset's partials in chunk order, so
+// the result does not depend on scheduling.
 #include <algorithm>
 
 #include "common.h"
@@ -21,8 +22,9 @@ namespace {
 constexpr int DT = 256;          // threads per workgroup (2 x 2 waves)
 constexpr int PS = 64;           // pairs staged per step
 constexpr int TMAX = 128;        // channel tile edge
-constexpr int TARGET_WG = 512;   // workgroups the split count aims for
-constexpr int MIN_PAIRS_PER_SPLIT = 1024;
+constexpr int TARGET_CHUNKS = 1024;   // pair chunks the chunk length aims for
+constexpr int MIN_CHUNK = 1024;       // pairs per chunk at least
+constexpr int MAX_WG = 512;           // persistent workgroups (per channel tile)
 
 struct DfArgs {
     const void* x;        // [n_in, cin]
@@ -30,8 +32,25 @@ struct DfArgs {
     const int32_t* ptr;   // [K+1] or NULL (identity pairs, K == 1)
     const int32_t* pin;
     const int32_t* pout;
-    float* part;          // [K, S, cin, cout]
-    int32_t n_in, n_out, cin, cout, K, S;
+    float* part;          // [max chunks, cin, cout]
+    int32_t n_in, n_out, cin, cout, K;
+};
+
+// Pair range of offset k and the common chunk length.  Every workgroup and
+// the reduction derive the same chunking from pair_ptr: chunks of CH pairs
+// (a multiple of PS, at least MIN_CHUNK, about P / TARGET_CHUNKS), never
+// straddling two offsets, numbered offset by offset.
+struct Chunks {
+    int64_t ch;
+    __device__ Chunks(const DfArgs& a) {
+        const int64_t P = a.ptr ? a.ptr[a.K] : a.n_in;
+        int64_t c = (P + TARGET_CHUNKS - 1) / TARGET_CHUNKS;
+        c = c < MIN_CHUNK ? MIN_CHUNK : c;
+        ch = (c + PS - 1) / PS * PS;
+    }
+    __device__ static int64_t beg(const DfArgs& a, int k) { return a.ptr ? a.ptr[k] : 0; }
+    __device__ static int64_t end(const DfArgs& a, int k) { return a.ptr ? a.ptr[k + 1] : a.n_in; }
+    __device__ int64_t count(const DfArgs& a, int k) const { return (end(a, k) - beg(a, k) + ch - 1) / ch; }
 };
 
 // Row stride (bytes) of a channel-major LDS tile: PS pairs plus 16 bytes of
@@ -39,185 +58,291 @@ struct DfArgs {
 template <typename TT>
 constexpr int lds_row() { return PS * int(sizeof(typename TT::storage)) + 16; }
 
-// Gathers E pairs x (E channels) of one operand and stores them transposed:
-// lds[ch][pair] with 16 consecutive bytes of pairs per channel.
+// One staging item: E consecutive pairs x E consecutive channels of one operand.
 template <typename TT>
-__device__ __forceinline__ void stage_transposed(char* lds, const typename TT::storage* src, const int32_t* rows,
-                                                 int C, int c0, int chunk, int pg) {
+struct Item {
+    u32x4 in[TT::E];
+};
+
+template <typename TT>
+__device__ __forceinline__ void load_item(Item<TT>& it, const DfArgs& a, int item, int xi_items, int TI, int TO,
+                                          int ci0, int co0, int64_t p0, int64_t p_end) {
+    using S = typename TT::storage;
     constexpr int E = TT::E;
-    u32x4 in[E];
+    constexpr int PG = PS / E;
+    const bool is_x = item < xi_items;
+    const int j = is_x ? item : item - xi_items;
+    const int pg = j % PG, ch = j / PG;
+    const S* src = is_x ? static_cast<const S*>(a.x) : static_cast<const S*>(a.dy);
+    const int C = is_x ? a.cin : a.cout;
+    const int c0 = (is_x ? ci0 : co0) + ch * E;
+    const int32_t* idx = is_x ? a.pin : a.pout;
+    const int32_t lim = is_x ? a.n_in : a.n_out;
+    // all pair indices first, then all rows: unconditional (clamped) loads so
+    // that the whole batch is in flight at once; invalid slots become zero
+    int32_t r[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        in[e] = zero4();
-        if (rows[e] >= 0) in[e] = ld16(src + int64_t(rows[e]) * C + c0 + chunk * E);
+        const int64_t p = p0 + pg * E + e;
+        const int64_t pc = p < p_end ? p : p_end - 1;
+        r[e] = a.ptr ? idx[pc] : int32_t(pc);
     }
-    char* dst = lds + (chunk * E) * lds_row<TT>() + pg * 16;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool ok = p0 + pg * E + e < p_end && (unsigned)r[e] < (unsigned)lim;
+        it.in[e] = ld16(src + int64_t(ok ? r[e] : 0) * C + c0);
+        if (!ok) it.in[e] = zero4();
+    }
+}
+
+// Writes a loaded item transposed: lds[channel][pair], 16 bytes of
+// consecutive pairs per channel.
+template <typename TT>
+__device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& it, int item, int xi_items) {
+    constexpr int E = TT::E;
+    constexpr int PG = PS / E;
+    const bool is_x = item < xi_items;
+    const int j = is_x ? item : item - xi_items;
+    const int pg = j % PG, ch = j / PG;
+    char* dst = (is_x ? xt : gt) + (ch * E) * lds_row<TT>() + pg * 16;
     if constexpr (E == 8) {
         typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
         u16x8 v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(u16x8, in[e]);
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(u16x8, it.in[e]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            u16x8 o = {v[0][j], v[1][j], v[2][j], v[3][j], v[4][j], v[5][j], v[6][j], v[7][j]};
-            st16(dst + j * lds_row<TT>(), __builtin_bit_cast(u32x4, o));
+        for (int c = 0; c < 8; ++c) {
+            u16x8 o = {v[0][c], v[1][c], v[2][c], v[3][c], v[4][c], v[5][c], v[6][c], v[7][c]};
+            st16(dst + c * lds_row<TT>(), __builtin_bit_cast(u32x4, o));
         }
     } else {
+        const u32x4* in = it.in;
         const uint32_t m[4][4] = {{in[0].x, in[0].y, in[0].z, in[0].w},
                                   {in[1].x, in[1].y, in[1].z, in[1].w},
                                   {in[2].x, in[2].y, in[2].z, in[2].w},
                                   {in[3].x, in[3].y, in[3].z, in[3].w}};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st16(dst + j * lds_row<TT>(), u32x4{m[0][j], m[1][j], m[2][j], m[3][j]});
+        for (int c = 0; c < 4; ++c) st16(dst + c * lds_row<TT>(), u32x4{m[0][c], m[1][c], m[2][c], m[3][c]});
     }
 }
 
+// Persistent workgroups walk the pair chunks (chunk j = blockIdx.x + t *
+// gridDim.x); each chunk's partial dW tile goes to part[j].  The next step's
+// first staging item is prefetched into registers during the MFMAs.
 template <typename TT>
 __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
-    using S = typename TT::storage;
     constexpr int E = TT::E;
     constexpr int ROW = lds_row<TT>();
     __shared__ __attribute__((aligned(16))) char xt[TMAX * ROW];  // [ci][pairs]
     __shared__ __attribute__((aligned(16))) char gt[TMAX * ROW];  // [co][pairs]
 
-    const int k = blockIdx.y, s = blockIdx.x;
     const int tiles_o = (a.cout + TMAX - 1) / TMAX;
-    const int ci0 = (blockIdx.z / tiles_o) * TMAX, co0 = (blockIdx.z % tiles_o) * TMAX;
+    const int ci0 = (blockIdx.y / tiles_o) * TMAX, co0 = (blockIdx.y % tiles_o) * TMAX;
     const int TI = min(TMAX, a.cin - ci0), TO = min(TMAX, a.cout - co0);
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
     const int wi = wave >> 1, wo = wave & 1;
     const int MI = (TI / 16 + 1) / 2, NO = (TO / 16 + 1) / 2;  // 16x16 blocks per wave (<= 4)
+    constexpr int PG = PS / E;
+    const int xi_items = PG * (TI / E), items = xi_items + PG * (TO / E);
 
-    int64_t pbeg, pend;
-    if (a.ptr) {
-        pbeg = a.ptr[k];
-        pend = a.ptr[k + 1];
-    } else {
-        pbeg = 0;
-        pend = a.n_in;
-    }
-    const int64_t total = pend - pbeg;
-    const int64_t chunk = ((total + a.S - 1) / a.S + PS - 1) / PS * PS;
-    const int64_t c_beg = min(pend, pbeg + s * chunk), c_end = min(pend, c_beg + chunk);
+    const Chunks chunks(a);
+    int64_t total = 0;
+    for (int k = 0; k < a.K; ++k) total += chunks.count(a, k);
 
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const S* x = static_cast<const S*>(a.x);
-    const S* dy = static_cast<const S*>(a.dy);
-    constexpr int PG = PS / E;  // pair groups per step
-    const int xi_items = PG * (TI / E), go_items = PG * (TO / E);
-
-    for (int64_t p0 = c_beg; p0 < c_end; p0 += PS) {
-        __syncthreads();  // the previous step's tiles are consumed
-        for (int it = threadIdx.x; it < xi_items + go_items; it += DT) {
-            const bool is_x = it < xi_items;
-            const int j = is_x ? it : it - xi_items;
-            const int pg = j % PG, ch = j / PG;
-            int32_t rows[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t p = p0 + pg * E + e;
-                int32_t r = -1;
-                if (p < c_end) r = a.ptr ? (is_x ? a.pin[p] : a.pout[p]) : int32_t(p);
-                if (is_x ? (unsigned)r >= (unsigned)a.n_in : (unsigned)r >= (unsigned)a.n_out) r = -1;
-                rows[e] = r;
-            }
-            if (is_x)
-                stage_transposed<TT>(xt, x, rows, a.cin, ci0, ch, pg);
-            else
-                stage_transposed<TT>(gt, dy, rows, a.cout, co0, ch, pg);
+    for (int64_t j = blockIdx.x; j < total; j += gridDim.x) {
+        // locate chunk j: offset k, pair range [c_beg, c_end)
+        int k = 0;
+        int64_t first = 0;
+        for (;; ++k) {
+            const int64_t c = chunks.count(a, k);
+            if (j < first + c) break;
+            first += c;
         }
-        __syncthreads();
+        const int64_t c_beg = Chunks::beg(a, k) + (j - first) * chunks.ch;
+        const int64_t c_end = min(Chunks::end(a, k), c_beg + chunks.ch);
+
+        f32x4_t acc[4][4];
 #pragma unroll
-        for (int ks = 0; ks < PS / (4 * E); ++ks) {
-            const int poff = (ks * 4 + lg) * 16;
-            u32x4 gf[4], xf[4];
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int no = 0; no < 4; ++no)
-                if (no < NO && (wo * NO + no) * 16 < TO) gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
+            for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        Item<TT> pre;
+        const int my = threadIdx.x;  // first item of this thread
+        if (my < items) load_item<TT>(pre, a, my, xi_items, TI, TO, ci0, co0, c_beg, c_end);
+        for (int64_t p0 = c_beg; p0 < c_end; p0 += PS) {
+            __syncthreads();  // the previous step's tiles are consumed
+            if (my < items) store_item<TT>(xt, gt, pre, my, xi_items);
+            for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32)
+                Item<TT> tmp;
+                load_item<TT>(tmp, a, it, xi_items, TI, TO, ci0, co0, p0, c_end);
+                store_item<TT>(xt, gt, tmp, it, xi_items);
+            }
+            __syncthreads();
+            if (my < items && p0 + PS < c_end) load_item<TT>(pre, a, my, xi_items, TI, TO, ci0, co0, p0 + PS, c_end);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                if (mi < MI && (wi * MI + mi) * 16 < TI) xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int ks = 0; ks < PS / (4 * E); ++ks) {
+                const int poff = (ks * 4 + lg) * 16;
+                u32x4 gf[4], xf[4];
 #pragma unroll
                 for (int no = 0; no < 4; ++no)
-                    if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
-                        acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
+                    if (no < NO && (wo * NO + no) * 16 < TO)
+                        gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    if (mi < MI && (wi * MI + mi) * 16 < TI)
+                        xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int no = 0; no < 4; ++no)
+                        if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
+                            acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
+            }
         }
+
+        // D[co][ci] per 16x16 tile: this lane holds co = lg*4 .. +3 of ci = lr
+        float* part = a.part + j * a.cin * a.cout;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int no = 0; no < 4; ++no) {
+                if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
+                const int ci = ci0 + (wi * MI + mi) * 16 + lr;
+                const int co = co0 + (wo * NO + no) * 16 + lg * 4;
+                *reinterpret_cast<f32x4_t*>(part + int64_t(ci) * a.cout + co) = acc[mi][no];
+            }
     }
-
-    // D[co][ci] per 16x16 tile: this lane holds co = lg*4 .. +3 of ci = lr
-    float* part = a.part + (int64_t(k) * a.S + s) * a.cin * a.cout;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int no = 0; no < 4; ++no) {
-            if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
-            const int ci = ci0 + (wi * MI + mi) * 16 + lr;
-            const int co = co0 + (wo * NO + no) * 16 + lg * 4;
-            *reinterpret_cast<f32x4_t*>(part + int64_t(ci) * a.cout + co) = acc[mi][no];
-        }
 }
 
-// out[g][j] = sum over s < S (in order) of part[(g*S + s)*L + j], 4 floats per thread.
-__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int S, int64_t L,
-                                                       int64_t groups, float* __restrict__ out) {
-    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (t * 4 >= L * groups) return;
-    const int64_t g = (t * 4) / L, j = (t * 4) % L;
+// dw[k] = sum of the partials of offset k's chunks, in chunk order (zero if
+// the offset has no pairs).  Four floats per thread.
+__global__ __launch_bounds__(256) void k_reduce_chunks(DfArgs a, float* __restrict__ dw) {
+    const int k = blockIdx.y;
+    const int64_t L = int64_t(a.cin) * a.cout;
+    const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (t >= L) return;
+    const Chunks chunks(a);
+    int64_t first = 0;
+    for (int kk = 0; kk < k; ++kk) first += chunks.count(a, kk);
+    const int64_t cnt = chunks.count(a, k);
+    // in chunk order; loads are issued in batches so that they overlap
+    constexpr int QB = 8;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) acc += *reinterpret_cast<const f32x4_t*>(part + (g * S + s) * L + j);
-    *reinterpret_cast<f32x4_t*>(out + g * L + j) = acc;
+    for (int64_t j0 = first; j0 < first + cnt; j0 += QB) {
+        f32x4_t v[QB];
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+            const int64_t j = j0 + u < first + cnt ? j0 + u : first + cnt - 1;
+            v[u] = *reinterpret_cast<const f32x4_t*>(a.part + j * L + t);
+        }
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+            if (j0 + u < first + cnt) acc += v[u];
+    }
+    *reinterpret_cast<f32x4_t*>(dw + int64_t(k) * L + t) = acc;
 }
 
-constexpr int COLSUM_ROWS = 1024;  // rows per dbias partial
 
-// part[r][c] = sum of dy rows [r*COLSUM_ROWS, ...) in column c (fp32).
+constexpr int COLSUM_BLOCKS = 256;  // dbias partials (one per block, fixed row ranges)
+
+// part[blk][c] = sum of dy rows of block blk's range in column c (fp32).  A
+// thread owns one 16-byte column chunk and a row lane; lanes step through
+// the rows with batched loads, then combine in lane order through LDS, so
+// the result does not depend on scheduling.
 template <typename TT>
 __global__ __launch_bounds__(256) void k_colsum(const typename TT::storage* __restrict__ dy, int32_t n, int32_t C,
                                                 float* __restrict__ part) {
-    const int r = blockIdx.x;
-    const int64_t lo = int64_t(r) * COLSUM_ROWS, hi = min<int64_t>(n, lo + COLSUM_ROWS);
-    for (int c = threadIdx.x; c < C; c += 256) {
-        float s = 0.f;
-        for (int64_t i = lo; i < hi; ++i) {
-            if constexpr (TT::id == SPC_F32) {
-                s += dy[i * C + c];
-            } else if constexpr (TT::id == SPC_BF16) {
-                s += __uint_as_float(uint32_t(dy[i * C + c]) << 16);
-            } else {
-                s += float(__builtin_bit_cast(_Float16, dy[i * C + c]));
+    using S = typename TT::storage;
+    constexpr int E = TT::E;
+    __shared__ float red[256][8];
+    const int CC = C / E;                    // 16-byte chunks per row (C is a multiple of 16)
+    const int64_t per = (int64_t(n) + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = min<int64_t>(n, per * blockIdx.x), hi = min<int64_t>(n, lo + per);
+    float* outp = part + int64_t(blockIdx.x) * C;
+    for (int c0 = 0; c0 < CC; c0 += 256) {   // column chunks handled by this pass
+        const int nch = min(256, CC - c0);
+        const int lanes = 256 / nch;         // row lanes
+        const int ch = threadIdx.x % nch, lane = threadIdx.x / nch;
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.f;
+        if (lane < lanes) {
+            constexpr int QB = 4;
+            for (int64_t r0 = lo + lane; r0 < hi; r0 += int64_t(lanes) * QB) {
+                u32x4 v[QB];
+#pragma unroll
+                for (int u = 0; u < QB; ++u) {
+                    const int64_t r = r0 + int64_t(u) * lanes;
+                    v[u] = ld16(dy + (r < hi ? r : lo) * C + (c0 + ch) * E);
+                }
+#pragma unroll
+                for (int u = 0; u < QB; ++u) {
+                    if (r0 + int64_t(u) * lanes >= hi) continue;
+                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if constexpr (TT::id == SPC_F32) {
+                            acc[e] += __uint_as_float(w[e]);
+                        } else {
+                            const uint16_t h = uint16_t(w[e / 2] >> (16 * (e & 1)));
+                            if constexpr (TT::id == SPC_BF16)
+                                acc[e] += __uint_as_float(uint32_t(h) << 16);
+                            else
+                                acc[e] += float(__builtin_bit_cast(_Float16, h));
+                        }
+                    }
+                }
             }
         }
-        part[int64_t(r) * C + c] = s;
+#pragma unroll
+        for (int e = 0; e < E; ++e) red[threadIdx.x][e] = acc[e];
+        __syncthreads();
+        if (threadIdx.x < nch) {  // lane order
+            float t[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) t[e] = 0.f;
+            for (int l = 0; l < lanes; ++l)
+#pragma unroll
+                for (int e = 0; e < E; ++e) t[e] += red[l * nch + threadIdx.x][e];
+#pragma unroll
+            for (int e = 0; e < E; ++e) outp[(c0 + threadIdx.x) * E + e] = t[e];
+        }
+        __syncthreads();
     }
 }
 
-int split_count(int64_t n_in, int64_t n_out, int32_t cin, int32_t cout, int32_t K) {
-    const int64_t pmax = std::min(n_in, n_out);
-    const int64_t tiles = ceil_div(cin, TMAX) * ceil_div(cout, TMAX);
-    int64_t s = ceil_div(TARGET_WG, int64_t(K) * tiles);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, pmax / MIN_PAIRS_PER_SPLIT));
-    return int(std::max<int64_t>(1, std::min<int64_t>(s, 256)));
+// out[j] = sum over s < S (in order) of part[s*L + j], batched loads.
+__global__ __launch_bounds__(256) void k_reduce_parts(const float* __restrict__ part, int S, int64_t L,
+                                                      float* __restrict__ out) {
+    const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (j >= L) return;
+    constexpr int QB = 8;
+    float acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += QB) {
+        float v[QB];
+#pragma unroll
+        for (int u = 0; u < QB; ++u) v[u] = part[int64_t(s0 + u < S ? s0 + u : S - 1) * L + j];
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+            if (s0 + u < S) acc += v[u];
+    }
+    out[j] = acc;
 }
 
 struct DfLayout {
-    int S;
+    int64_t max_chunks;
     int64_t rparts;  // dbias partial rows
     size_t off_dbias, total;
 };
 
+// Chunks never exceed P / CH + K <= TARGET_CHUNKS + K (CH >= P / TARGET_CHUNKS).
 DfLayout df_layout(int64_t n_in, int64_t n_out, int32_t cin, int32_t cout, int32_t K, bool dbias) {
     DfLayout l;
-    l.S = split_count(n_in, n_out, cin, cout, K);
-    l.rparts = dbias ? std::max<int64_t>(1, ceil_div(n_out, COLSUM_ROWS)) : 0;
-    l.off_dbias = align_up(size_t(K) * l.S * cin * cout * 4, 256);
+    l.max_chunks = TARGET_CHUNKS + K;
+    l.rparts = dbias ? COLSUM_BLOCKS : 0;
+    l.off_dbias = align_up(size_t(l.max_chunks) * cin * cout * 4, 256);
     l.total = align_up(l.off_dbias + size_t(l.rparts) * cout * 4, 256);
     return l;
 }
@@ -226,25 +351,20 @@ template <typename TT>
 spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_part, int64_t rparts,
                           hipStream_t stream) {
     const unsigned tiles = unsigned(ceil_div(a.cin, TMAX) * ceil_div(a.cout, TMAX));
-    hipLaunchKernelGGL(k_dfilter<TT>, dim3(unsigned(a.S), unsigned(a.K), tiles), dim3(DT), 0, stream, a);
+    const unsigned wgs = unsigned(std::max<int64_t>(64, MAX_WG / tiles));
+    hipLaunchKernelGGL(k_dfilter<TT>, dim3(wgs, tiles), dim3(DT), 0, stream, a);
     SPC_LAUNCHED("k_dfilter");
     const int64_t L = int64_t(a.cin) * a.cout;
-    hipLaunchKernelGGL(k_reduce_splits, dim3(unsigned(ceil_div(L * a.K / 4, 256))), dim3(256), 0, stream, a.part, a.S,
-                       L, int64_t(a.K), dw);
-    SPC_LAUNCHED("k_reduce_splits");
+    hipLaunchKernelGGL(k_reduce_chunks, dim3(unsigned(ceil_div(L / 4, 256)), unsigned(a.K)), dim3(256), 0, stream, a,
+                       dw);
+    SPC_LAUNCHED("k_reduce_chunks");
     if (dbias) {
-        if (a.n_out > 0) {
-            hipLaunchKernelGGL(k_colsum<TT>, dim3(unsigned(rparts)), dim3(256), 0, stream,
-                               static_cast<const typename TT::storage*>(a.dy), a.n_out, a.cout, bias_part);
-            SPC_LAUNCHED("k_colsum");
-        } else {
-            hipLaunchKernelGGL(k_colsum<TT>, dim3(1), dim3(256), 0, stream,
-                               static_cast<const typename TT::storage*>(a.dy), 0, a.cout, bias_part);
-            SPC_LAUNCHED("k_colsum");
-        }
-        hipLaunchKernelGGL(k_reduce_splits, dim3(unsigned(ceil_div(a.cout / 4, 256))), dim3(256), 0, stream, bias_part,
-                           int(std::max<int64_t>(rparts, 1)), int64_t(a.cout), int64_t(1), dbias);
-        SPC_LAUNCHED("k_reduce_splits");
+        hipLaunchKernelGGL(k_colsum<TT>, dim3(unsigned(rparts)), dim3(256), 0, stream,
+                           static_cast<const typename TT::storage*>(a.dy), a.n_out, a.cout, bias_part);
+        SPC_LAUNCHED("k_colsum");
+        hipLaunchKernelGGL(k_reduce_parts, dim3(unsigned(ceil_div(a.cout, 256))), dim3(256), 0, stream, bias_part,
+                           int(rparts), int64_t(a.cout), dbias);
+        SPC_LAUNCHED("k_reduce_parts");
     }
     return SPC_OK;
 }
@@ -287,7 +407,7 @@ extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, in
     if (!ws) return fail(SPC_ERR_ARG, "workspace is NULL");
     if (ws_bytes < l.total) return fail(SPC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
     DfArgs a{feats, dout, pair_ptr, pair_in, pair_out, static_cast<float*>(ws), int32_t(n_in), int32_t(n_out),
-             cin, cout, K, l.S};
+             cin, cout, K};
     float* bias_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.off_dbias);
     switch (dtype) {
         case SPC_F32: return launch_dfilter<F32>(a, dw, dbias, bias_part, l.rparts, stream);

@@ -1,20 +1,26 @@
 // Kernel-map construction on the GPU: hash build, per-offset probes, strided
-// output sites and CSR pair lists.
+// output sites, CSR pair lists and mask-sorted processing orders.
 //
 // Hash table: open addressing with linear probing over 64-bit slots that pack
 // (key << 32) | row, so one 8-byte load answers a probe and one 64-bit CAS
 // claims a slot (the single-slot table of spconv's hash.HashTable on the
 // context7 spconv page).  Keys are ((b*Z + z)*Y + y)*X + x, the packing of the
 // MLX sparse/conv.py page's build_indice_map, bounded below 2^32 so the
-// all-ones slot can mark "empty".  Capacity is a power of two >= 2N.
+// all-ones slot can mark "empty".  Capacity is a power of two >= 4N.
 //
 // Strided output sites are marked in a bitmap over the output grid; a
 // per-word exclusive prefix of popcounts then gives, for any output site, its
 // row in (b, z, y, x) order (rank = prefix[word] + popcount of the lower bits),
-// so sorted output coordinates need no sort and no second table.
+// so sorted output coordinates need no sort and no second table.  The
+// input-side map follows from the ranks, and the output-side map is its
+// transpose, scattered from it (no hash probes at all on the strided path;
+// the hash still detects duplicate inputs).
 //
-// Pair lists are compacted in (offset, output row) order with a per-block
-// count pass, one exclusive scan, and an ordered ballot/prefix write pass.
+// Maps are row-major [rows][K].  A row pass builds each row's neighbour mask
+// and the per-(offset, block) hit counts; pair lists are compacted in
+// (offset, row) order by one exclusive scan and an ordered ballot/prefix write
+// pass.  The processing order is a stable LSD radix sort of (mask, row) with
+// 8-bit digits: per pass a block histogram, one scan and a stable scatter.
 #include <stdio.h>
 
 #include <algorithm>
@@ -25,10 +31,17 @@ namespace spc {
 namespace {
 
 constexpr uint64_t EMPTY_SLOT = ~0ull;
-constexpr int KB = 256;          // threads (= rows) per block of the per-row kernels
-constexpr int MAX_K = 343;       // up to 7 x 7 x 7 offsets
+constexpr int KB = 256;          // threads per block of the per-row / per-entry kernels
 constexpr int WORDS_PER_THREAD = 8;
 constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_PER_THREAD = 16;
+constexpr int RS_ITEMS = 32;                 // keys per thread in the radix passes (few, large tiles:
+                                             // a block reads the histogram of every block)
+constexpr int RS_TILE = KB * RS_ITEMS;       // keys per radix block
+constexpr int RS_BITS = 9;                   // digit width of the radix passes
+constexpr int RS_BINS = 1 << RS_BITS;
+constexpr int MASK_BITS = 32;                // orders are built for K <= 32
+constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
 
 struct KGeom {
     int32_t batch, Z, Y, X;      // input grid
@@ -69,7 +82,7 @@ __device__ __forceinline__ void table_insert(uint64_t* table, uint32_t mask, uin
                                              uint32_t row, uint32_t* flags) {
     const unsigned long long slot = (static_cast<unsigned long long>(key) << 32) | row;
     uint32_t h = mix32(key) & mask;
-    // at most N of the >= 2N slots are ever taken, so an empty slot is always found
+    // at most N of the >= 4N slots are ever taken, so an empty slot is always found
     for (uint32_t step = 0; step <= mask; ++step) {
         unsigned long long prev =
             atomicCAS(reinterpret_cast<unsigned long long*>(table + h), EMPTY_SLOT, slot);
@@ -94,10 +107,40 @@ __device__ __forceinline__ int32_t table_find(const uint64_t* __restrict__ table
     return -1;
 }
 
-// Adds this wave's hit count for offset k to the block's LDS counter.
-__device__ __forceinline__ void count_hits(bool hit, int32_t* cnt, int k) {
-    const uint64_t b = __ballot(hit);
-    if ((threadIdx.x & (WAVE - 1)) == 0 && b) atomicAdd(cnt + k, __popcll(b));
+// Load of a[min(i, n - 1)] (n >= 1): an unconditional load, so a batch of
+// them issues back to back; the caller discards the value when i >= n.
+template <typename T>
+__device__ __forceinline__ T ld_clamped(const T* __restrict__ a, int64_t i, int64_t n) {
+    return a[i < n ? i : n - 1];
+}
+
+// Output-row count M as the later kernels see it: 0 when it exceeds the
+// caller's capacity (the host then reports SPC_ERR_CAPACITY).
+__device__ __forceinline__ int32_t rows_within(const uint32_t* hdr, int64_t cap) {
+    const uint32_t m = hdr[H_NOUT];
+    return int64_t(m) <= cap ? int32_t(m) : 0;
+}
+
+// Block-wide exclusive scan of one int per thread; returns the block total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    int incl = v;
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    if (lane == WAVE - 1) lds_waves[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < NT / WAVE; ++w) {
+        const int s = lds_waves[w];
+        if (w < wave) before += s;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return before + incl - v;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -111,6 +154,13 @@ __global__ void k_clear(uint64_t* __restrict__ table, int64_t cap, uint32_t* __r
     u32x4 ones = {~0u, ~0u, ~0u, ~0u};
     for (int64_t i = t; i < cap / 2; i += stride) st16(table + 2 * i, ones);
     for (int64_t i = t; i < nwords / 4; i += stride) st16(bitmap + 4 * i, zero4());
+}
+
+// Fills rows [0, M) of a [rows][K] map with -1 (M read on the device).
+__global__ void k_fill_map(int32_t* __restrict__ map, int K, int64_t cap, const uint32_t* hdr) {
+    const int64_t n = int64_t(rows_within(hdr, cap)) * K;
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) map[i] = -1;
 }
 
 // Inserts every in-range input row; flags bad and duplicate rows.  For a
@@ -151,43 +201,30 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
             }
 }
 
-// Submanifold probes: nbr[k*n + i] = row at coords[i] + d_k, else -1, with
-// d_k = (kz - KZ/2, ky - KY/2, kx - KX/2), z slowest.  Optionally counts the
-// hits of each offset in this block into counts[k*nblk + block].
+// Submanifold probes, one thread per map entry t = i*K + k: nbr[t] = row at
+// coords[i] + d_k, else -1, with d_k = (kz - KZ/2, ky - KY/2, kx - KX/2), z
+// slowest.  Consecutive threads write consecutive entries.
 __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coords, int32_t n, KGeom g,
                                                    const uint64_t* __restrict__ table, uint32_t mask,
-                                                   int32_t* __restrict__ nbr, int32_t* __restrict__ counts,
-                                                   const uint32_t* hdr, int32_t* coord_err) {
-    __shared__ int32_t cnt[MAX_K];
+                                                   int32_t* __restrict__ nbr, const uint32_t* hdr,
+                                                   int32_t* coord_err) {
     const int K = g.kz * g.ky * g.kx;
-    for (int k = threadIdx.x; k < K; k += KB) cnt[k] = 0;
-    if (coord_err && blockIdx.x == 0 && threadIdx.x == 0) *coord_err = int32_t(hdr[H_FLAGS]);
-    __syncthreads();
-    const int32_t i = blockIdx.x * KB + threadIdx.x;
-    const bool live = i < n;
-    int4 c = make_int4(-1, -1, -1, -1);
-    if (live) c = coords[i];
-    const bool ok = live && in_grid(c, g);
-    const int rz = g.kz / 2, ry = g.ky / 2, rx = g.kx / 2;
-    int k = 0;
-    for (int a = 0; a < g.kz; ++a) {
-        const int z = c.y + a - rz;
-        for (int b = 0; b < g.ky; ++b) {
-            const int y = c.z + b - ry;
-            for (int d = 0; d < g.kx; ++d, ++k) {
-                const int x = c.w + d - rx;
-                int32_t v = -1;
-                if (ok && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y &&
-                    (unsigned)x < (unsigned)g.X)
-                    v = table_find(table, mask, in_key(c.x, z, y, x, g));
-                if (live) nbr[int64_t(k) * n + i] = v;
-                if (counts) count_hits(v >= 0, cnt, k);
-            }
-        }
+    const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
+    if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (t >= int64_t(n) * K) return;
+    const int32_t i = int32_t(t / K);
+    const int k = int(t - int64_t(i) * K);
+    const int kx = k % g.kx, ky = (k / g.kx) % g.ky, kz = k / (g.kx * g.ky);
+    int32_t v = -1;
+    const int4 c = coords[i];
+    if (in_grid(c, g)) {
+        const int z = c.y + kz - g.kz / 2, y = c.z + ky - g.ky / 2, x = c.w + kx - g.kx / 2;
+        if (kz == g.kz / 2 && ky == g.ky / 2 && kx == g.kx / 2)
+            v = i;
+        else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X)
+            v = table_find(table, mask, in_key(c.x, z, y, x, g));
     }
-    if (!counts) return;
-    __syncthreads();
-    for (int kk = threadIdx.x; kk < K; kk += KB) counts[int64_t(kk) * gridDim.x + blockIdx.x] = cnt[kk];
+    nbr[t] = v;
 }
 
 // Popcount of each thread's WORDS_PER_THREAD bitmap words, summed per block.
@@ -211,60 +248,66 @@ __global__ __launch_bounds__(KB) void k_bitmap_count(const uint32_t* __restrict_
     }
 }
 
-// Block-wide exclusive scan of one int per thread; returns the block total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
-    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-    int incl = v;
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const int u = __shfl_up(incl, off);
-        if (lane >= off) incl += u;
-    }
-    if (lane == WAVE - 1) lds_waves[wave] = incl;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < NT / WAVE; ++w) {
-        const int s = lds_waves[w];
-        if (w < wave) before += s;
-        tot += s;
-    }
-    __syncthreads();
-    total = tot;
-    return before + incl - v;
-}
-
-// One-workgroup exclusive scan of data[0, L) in place (L < 2^31 total).
+// One-workgroup exclusive scan of data[0, L) in place, in chunks of
+// SCAN_THREADS * SCAN_PER_THREAD values staged through LDS (coalesced loads
+// and stores; each thread scans a contiguous run of the chunk).
 // With ptr != NULL, ptr[k] = data[k * nblk] (after the scan) for k < K and
-// ptr[K] = total: the CSR offsets of the (offset, block) count matrix.
+// ptr[K] = total: the CSR offsets of a (offset, block) count matrix.
 // With total_out != NULL the total is also stored there.
 __global__ __launch_bounds__(SCAN_THREADS) void k_scan(int32_t* __restrict__ data, int64_t L, int32_t* ptr,
                                                        int K, int64_t nblk, uint32_t* total_out) {
+    constexpr int CH = SCAN_THREADS * SCAN_PER_THREAD;
     __shared__ int waves[SCAN_THREADS / WAVE];
-    const int64_t per = (L + SCAN_THREADS - 1) / SCAN_THREADS;
-    const int64_t lo = min<int64_t>(L, per * threadIdx.x), hi = min<int64_t>(L, lo + per);
-    int s = 0;
-    for (int64_t j = lo; j < hi; ++j) s += data[j];
-    int total;
-    int run = block_exclusive_scan<SCAN_THREADS>(s, waves, total);
-    for (int64_t j = lo; j < hi; ++j) {
-        const int v = data[j];
-        data[j] = run;
-        run += v;
+    __shared__ int buf[CH];
+    int carry = 0;
+    for (int64_t base = 0; base < L; base += CH) {
+        {
+            int v[SCAN_PER_THREAD];
+#pragma unroll
+            for (int e = 0; e < SCAN_PER_THREAD; ++e) v[e] = ld_clamped(data, base + e * SCAN_THREADS + threadIdx.x, L);
+#pragma unroll
+            for (int e = 0; e < SCAN_PER_THREAD; ++e) {
+                const int j = e * SCAN_THREADS + threadIdx.x;
+                buf[j] = base + j < L ? v[e] : 0;
+            }
+        }
+        __syncthreads();
+        int v[SCAN_PER_THREAD];
+        int s = 0;
+#pragma unroll
+        for (int e = 0; e < SCAN_PER_THREAD; ++e) {
+            v[e] = buf[threadIdx.x * SCAN_PER_THREAD + e];
+            s += v[e];
+        }
+        int tot;
+        int run = carry + block_exclusive_scan<SCAN_THREADS>(s, waves, tot);
+#pragma unroll
+        for (int e = 0; e < SCAN_PER_THREAD; ++e) {
+            buf[threadIdx.x * SCAN_PER_THREAD + e] = run;
+            run += v[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < SCAN_PER_THREAD; ++e) {
+            const int j = e * SCAN_THREADS + threadIdx.x;
+            if (base + j < L) data[base + j] = buf[j];
+        }
+        carry += tot;
+        __syncthreads();
     }
-    __syncthreads();
     if (ptr) {
         for (int k = threadIdx.x; k < K; k += SCAN_THREADS) ptr[k] = nblk > 0 ? data[int64_t(k) * nblk] : 0;
-        if (threadIdx.x == 0) ptr[K] = total;
+        if (threadIdx.x == 0) ptr[K] = carry;
     }
-    if (total_out && threadIdx.x == 0) *total_out = uint32_t(total);
+    if (total_out && threadIdx.x == 0) *total_out = uint32_t(carry);
 }
 
 // Writes each word's exclusive rank prefix and the output coordinates of
-// its set bits, in (b, z, y, x) order.
+// its set bits, in (b, z, y, x) order (coordinates only if M <= cap).
 __global__ __launch_bounds__(KB) void k_bitmap_emit(const uint32_t* __restrict__ bitmap, int64_t nwords,
                                                     const int32_t* __restrict__ block_offs,
                                                     uint32_t* __restrict__ prefix, int4* __restrict__ out_coords,
-                                                    KGeom g) {
+                                                    int64_t cap, const uint32_t* hdr, KGeom g) {
     __shared__ int waves[KB / WAVE];
     const int64_t w0 = (int64_t(blockIdx.x) * KB + threadIdx.x) * WORDS_PER_THREAD;
     uint32_t w[WORDS_PER_THREAD] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -278,111 +321,307 @@ __global__ __launch_bounds__(KB) void k_bitmap_emit(const uint32_t* __restrict__
     int total;
     int run = block_offs[blockIdx.x] + block_exclusive_scan<KB>(s, waves, total);
     if (w0 >= nwords) return;
-    const int64_t plane = int64_t(g.oy) * g.ox, vol = plane * g.oz;
+    const bool emit = int64_t(hdr[H_NOUT]) <= cap;
+    const uint32_t plane = uint32_t(g.oy) * uint32_t(g.ox), vol = plane * uint32_t(g.oz);
     for (int j = 0; j < WORDS_PER_THREAD; ++j) {
         prefix[w0 + j] = uint32_t(run);
+        if (!emit) continue;
         uint32_t bits = w[j];
         while (bits) {
-            const int bit = __ffs(bits) - 1;
+            const uint32_t bit = __ffs(bits) - 1;
             bits &= bits - 1;
-            const int64_t key = (w0 + j) * 32 + bit;
-            const int b = int(key / vol);
-            const int64_t r = key - int64_t(b) * vol;
-            const int z = int(r / plane);
-            const int64_t r2 = r - int64_t(z) * plane;
-            out_coords[run++] = make_int4(b, z, int(r2 / g.ox), int(r2 % g.ox));
+            const uint32_t key = uint32_t(w0 + j) * 32u + bit;
+            const uint32_t b = key / vol, r = key - b * vol;
+            const uint32_t z = r / plane, r2 = r - z * plane;
+            const uint32_t y = r2 / uint32_t(g.ox), x = r2 - y * uint32_t(g.ox);
+            out_coords[run++] = make_int4(int(b), int(z), int(y), int(x));
         }
     }
 }
 
-// Strided maps.  Blocks [0, mblk) handle output rows: nbr[k*M + o] = input
-// row at o*stride - pad + k*dil, else -1 (and per-block hit counts).  Blocks
-// [mblk, ...) handle input rows: nbr_in[k*n + i] = rank of the output site
-// that input i reaches through offset k, else -1.
-__global__ __launch_bounds__(KB) void k_strided_maps(const int4* __restrict__ coords, int32_t n,
-                                                     const int4* __restrict__ out_coords, int32_t M,
-                                                     int32_t mblk, KGeom g,
-                                                     const uint64_t* __restrict__ table, uint32_t mask,
-                                                     const uint32_t* __restrict__ bitmap,
+// Strided maps, one thread per input-side entry t = i*K + k: the output site
+// o = (c + pad - k*dil) / stride (exact, inside the grid) has row
+// rank(o); nbr_in[t] = that row (or -1), and the output-side map gets the
+// transposed entry nbr[row*K + k] = i (it was filled with -1 before).
+__global__ __launch_bounds__(KB) void k_strided_maps(const int4* __restrict__ coords, int32_t n, int64_t cap,
+                                                     KGeom g, const uint32_t* __restrict__ bitmap,
                                                      const uint32_t* __restrict__ prefix,
                                                      int32_t* __restrict__ nbr, int32_t* __restrict__ nbr_in,
-                                                     int32_t* __restrict__ counts, const uint32_t* hdr,
-                                                     int32_t* coord_err) {
-    __shared__ int32_t cnt[MAX_K];
+                                                     const uint32_t* hdr, int32_t* coord_err) {
     const int K = g.kz * g.ky * g.kx;
-    if (coord_err && blockIdx.x == 0 && threadIdx.x == 0) *coord_err = int32_t(hdr[H_FLAGS]);
-    if (int32_t(blockIdx.x) < mblk) {
-        for (int k = threadIdx.x; k < K; k += KB) cnt[k] = 0;
-        __syncthreads();
-        const int32_t o = blockIdx.x * KB + threadIdx.x;
-        const bool live = o < M;
-        int4 c = make_int4(0, 0, 0, 0);
-        if (live) c = out_coords[o];
-        int k = 0;
-        for (int a = 0; a < g.kz; ++a) {
-            const int z = c.y * g.sz - g.pz + a * g.dz;
-            for (int b = 0; b < g.ky; ++b) {
-                const int y = c.z * g.sy - g.py + b * g.dy;
-                for (int d = 0; d < g.kx; ++d, ++k) {
-                    const int x = c.w * g.sx - g.px + d * g.dx;
-                    int32_t v = -1;
-                    if (live && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y &&
-                        (unsigned)x < (unsigned)g.X)
-                        v = table_find(table, mask, in_key(c.x, z, y, x, g));
-                    if (live) nbr[int64_t(k) * M + o] = v;
-                    if (counts) count_hits(v >= 0, cnt, k);
-                }
-            }
-        }
-        if (!counts) return;
-        __syncthreads();
-        for (int kk = threadIdx.x; kk < K; kk += KB) counts[int64_t(kk) * mblk + blockIdx.x] = cnt[kk];
-        return;
-    }
-    const int32_t i = (blockIdx.x - mblk) * KB + threadIdx.x;
-    if (i >= n) return;
+    const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
+    if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (t >= int64_t(n) * K || int64_t(hdr[H_NOUT]) > cap) return;
+    const int32_t i = int32_t(t / K);
+    const int k = int(t - int64_t(i) * K);
+    const int kx = k % g.kx, ky = (k / g.kx) % g.ky, kz = k / (g.kx * g.ky);
     const int4 c = coords[i];
-    const bool ok = in_grid(c, g);
-    int k = 0;
-    for (int a = 0; a < g.kz; ++a) {
-        const int nz = c.y + g.pz - a * g.dz;
-        const bool vz = nz >= 0 && nz % g.sz == 0 && nz / g.sz < g.oz;
-        for (int b = 0; b < g.ky; ++b) {
-            const int ny = c.z + g.py - b * g.dy;
-            const bool vy = ny >= 0 && ny % g.sy == 0 && ny / g.sy < g.oy;
-            for (int d = 0; d < g.kx; ++d, ++k) {
-                const int nx = c.w + g.px - d * g.dx;
-                const bool vx = nx >= 0 && nx % g.sx == 0 && nx / g.sx < g.ox;
-                int32_t v = -1;
-                if (ok && vz && vy && vx) {
-                    const uint32_t key = out_key(c.x, nz / g.sz, ny / g.sy, nx / g.sx, g);
-                    const uint32_t word = key >> 5, bit = key & 31u;
-                    v = int32_t(prefix[word] + __popc(bitmap[word] & ((1u << bit) - 1u)));
-                }
-                nbr_in[int64_t(k) * n + i] = v;
-            }
+    int32_t v = -1;
+    const int nz = c.y + g.pz - kz * g.dz, ny = c.z + g.py - ky * g.dy, nx = c.w + g.px - kx * g.dx;
+    if (in_grid(c, g) && nz >= 0 && ny >= 0 && nx >= 0 && nz % g.sz == 0 && ny % g.sy == 0 && nx % g.sx == 0) {
+        const int oz = nz / g.sz, oy = ny / g.sy, ox = nx / g.sx;
+        if (oz < g.oz && oy < g.oy && ox < g.ox) {
+            const uint32_t key = out_key(c.x, oz, oy, ox, g);
+            const uint32_t word = key >> 5, bit = key & 31u;
+            v = int32_t(prefix[word] + __popc(bitmap[word] & ((1u << bit) - 1u)));
+            nbr[int64_t(v) * K + k] = i;
         }
     }
+    if (nbr_in) nbr_in[t] = v;
 }
 
-// Ordered compaction of one (block of rows, offset) tile of the map into the
-// CSR pair lists at the scanned offset offs[k*nblk + block].
-__global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict__ nbr, int32_t rows,
+// One thread per map row: the neighbour mask (bit k set iff entry k >= 0,
+// for K <= 32) into keys[row], and per offset the block's hit count into
+// counts[k*nblk + block] (wave counts summed with LDS atomics, one barrier).
+// The block's rows are first copied to LDS with coalesced loads (for
+// K <= ROWPASS_KMAX); a row stride of K words is conflict-free for odd K.
+// rows < 0: read M from the header.
+constexpr int ROWPASS_KMAX = 27;
+
+__global__ __launch_bounds__(KB) void k_row_pass(const int32_t* __restrict__ map, int32_t rows, int K,
+                                                 int64_t cap, const uint32_t* hdr, uint32_t* __restrict__ keys,
+                                                 int32_t* __restrict__ counts) {
+    __shared__ int32_t stage[KB * ROWPASS_KMAX];
+    __shared__ int32_t cnt[MAX_K];
+    if (rows < 0) rows = rows_within(hdr, cap);
+    const int32_t row0 = blockIdx.x * KB;
+    const int32_t r = row0 + threadIdx.x;
+    const bool live = r < rows;
+    const bool staged = K <= ROWPASS_KMAX;
+    for (int k = threadIdx.x; k < K; k += KB) cnt[k] = 0;
+    if (staged && row0 < rows) {
+        const int64_t lo = int64_t(row0) * K, hi = int64_t(min(rows, row0 + KB)) * K;
+        int32_t v[ROWPASS_KMAX];
+#pragma unroll
+        for (int e = 0; e < ROWPASS_KMAX; ++e) v[e] = ld_clamped(map, lo + e * KB + threadIdx.x, hi);
+#pragma unroll
+        for (int e = 0; e < ROWPASS_KMAX; ++e)
+            if (lo + e * KB + threadIdx.x < hi) stage[e * KB + threadIdx.x] = v[e];
+    }
+    __syncthreads();
+    const int32_t* row = staged ? stage + threadIdx.x * K : map + int64_t(r) * K;
+    uint32_t m = 0;
+    for (int k = 0; k < K; ++k) {
+        const bool hit = live && row[k] >= 0;
+        if (hit && k < MASK_BITS) m |= 1u << k;
+        if (counts) {
+            const uint64_t b = __ballot(hit);
+            if ((threadIdx.x & (WAVE - 1)) == 0 && b) atomicAdd(cnt + k, int(__popcll(b)));
+        }
+    }
+    if (keys && live) keys[r] = m;
+    if (!counts) return;
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += KB) counts[int64_t(k) * gridDim.x + blockIdx.x] = cnt[k];
+}
+
+// Ordered compaction of one block of map rows into the CSR pair lists: for
+// each offset k, the block's hits go to the scanned offset offs[k*nblk +
+// block] in ascending row order.  With masks (K <= 32) the ranks of all
+// offsets come from one ballot each and a single barrier; otherwise one
+// block scan per offset.  rows < 0: read M from the header.
+__global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict__ map, int32_t rows, int K,
+                                                      int64_t cap, const uint32_t* hdr,
+                                                      const uint32_t* __restrict__ masks,
                                                       const int32_t* __restrict__ offs,
                                                       int32_t* __restrict__ pair_in,
                                                       int32_t* __restrict__ pair_out) {
     __shared__ int waves[KB / WAVE];
-    const int k = blockIdx.y;
+    __shared__ int wcnt[MASK_BITS][KB / WAVE];
+    if (rows < 0) rows = rows_within(hdr, cap);
     const int32_t o = blockIdx.x * KB + threadIdx.x;
-    int32_t v = -1;
-    if (o < rows) v = nbr[int64_t(k) * rows + o];
-    int total;
-    const int pos = block_exclusive_scan<KB>(v >= 0 ? 1 : 0, waves, total);
-    if (v >= 0) {
-        const int64_t at = int64_t(offs[int64_t(k) * gridDim.x + blockIdx.x]) + pos;
-        pair_in[at] = v;
-        pair_out[at] = o;
+    const bool live = o < rows;
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    if (masks) {
+        __shared__ int32_t stage[KB * ROWPASS_KMAX];
+        const uint32_t m = live ? masks[o] : 0u;
+        const uint64_t lt = (1ull << lane) - 1ull;
+        const int32_t row0 = blockIdx.x * KB;
+        if (row0 < rows) {
+            const int64_t lo = int64_t(row0) * K, hi = int64_t(min(rows, row0 + KB)) * K;
+            int32_t v[ROWPASS_KMAX];
+#pragma unroll
+            for (int e = 0; e < ROWPASS_KMAX; ++e) v[e] = ld_clamped(map, lo + e * KB + threadIdx.x, hi);
+#pragma unroll
+            for (int e = 0; e < ROWPASS_KMAX; ++e)
+                if (lo + e * KB + threadIdx.x < hi) stage[e * KB + threadIdx.x] = v[e];
+        }
+        for (int k = 0; k < K; ++k) {
+            const uint64_t b = __ballot((m >> k) & 1u);
+            if (lane == 0) wcnt[k][wave] = __popcll(b);
+        }
+        __syncthreads();
+        for (int k = 0; k < K; ++k) {  // uniform loop: every lane takes part in the ballots
+            const bool hit = (m >> k) & 1u;
+            const uint64_t b = __ballot(hit);
+            if (!hit) continue;
+            int before = 0;
+            for (int w = 0; w < wave; ++w) before += wcnt[k][w];
+            const int64_t at = int64_t(offs[int64_t(k) * gridDim.x + blockIdx.x]) + before + __popcll(b & lt);
+            pair_in[at] = stage[threadIdx.x * K + k];
+            pair_out[at] = o;
+        }
+        return;
     }
+    for (int k = 0; k < K; ++k) {
+        const int32_t v = live ? map[int64_t(o) * K + k] : -1;
+        int total;
+        const int pos = block_exclusive_scan<KB>(v >= 0 ? 1 : 0, waves, total);
+        if (v >= 0) {
+            const int64_t at = int64_t(offs[int64_t(k) * gridDim.x + blockIdx.x]) + pos;
+            pair_in[at] = v;
+            pair_out[at] = o;
+        }
+    }
+}
+
+// Lanes of this wave whose (valid) digit equals this lane's, from RS_BITS ballots.
+__device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d) {
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < RS_BITS; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(valid && bit);
+        peers &= bit ? bb : ~bb;
+    }
+    return peers;
+}
+
+// Radix sort.  A block owns RS_TILE consecutive keys; wave w of the block
+// owns the contiguous run [w * RS_TILE / 4, (w + 1) * RS_TILE / 4), taken 64
+// at a time, so the block's keys are visited in index order per wave.
+__device__ __forceinline__ int32_t rs_index(int r) {
+    constexpr int PER_WAVE = RS_TILE / (KB / WAVE);
+    return int32_t(blockIdx.x) * RS_TILE + (threadIdx.x / WAVE) * PER_WAVE + r * WAVE + (threadIdx.x & (WAVE - 1));
+}
+
+// Pass histogram: hist[d*nblk + block] = number of the block's keys whose
+// digit (key >> shift) & (RS_BINS-1) is d.  rows < 0: M from the header.
+__global__ __launch_bounds__(KB) void k_rs_hist(const uint32_t* __restrict__ keys, int32_t rows, int64_t cap,
+                                                const uint32_t* hdr, int shift, int32_t* __restrict__ hist) {
+    __shared__ int32_t h[RS_BINS];
+    if (rows < 0) rows = rows_within(hdr, cap);
+    if (rows == 0) return;
+    for (int d = threadIdx.x; d < RS_BINS; d += KB) h[d] = 0;
+    uint32_t dig[RS_ITEMS];
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) dig[r] = ld_clamped(keys, rs_index(r), rows);  // all in flight
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r)
+        dig[r] = rs_index(r) < rows ? (dig[r] >> shift) & (RS_BINS - 1) : RS_BINS;
+    __syncthreads();
+    const uint64_t lt = (1ull << (threadIdx.x & (WAVE - 1))) - 1ull;
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const bool valid = dig[r] < RS_BINS;
+        const uint64_t peers = digit_peers(valid, dig[r] & (RS_BINS - 1));  // one atomic per digit and wave
+        if (valid && (peers & lt) == 0) atomicAdd(h + dig[r], int(__popcll(peers)));
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < RS_BINS; d += KB) hist[int64_t(d) * gridDim.x + blockIdx.x] = h[d];
+}
+
+// Pass scatter, stable.  The block first derives its slot base per digit from
+// the histogram matrix (all keys of smaller digits, plus this digit's keys in
+// earlier blocks), then the base of each wave (this digit's keys in earlier
+// waves of the block); each wave then ranks its keys among equal digits with
+// RS_BITS ballots and writes them in order, without further barriers.
+// vals_in == NULL means the identity (row index).
+__global__ __launch_bounds__(KB) void k_rs_scatter(const uint32_t* __restrict__ keys_in,
+                                                   const int32_t* __restrict__ vals_in, int32_t rows, int64_t cap,
+                                                   const uint32_t* hdr, int shift, const int32_t* __restrict__ hist,
+                                                   uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+    constexpr int NW = KB / WAVE;
+    constexpr int BPT = RS_BINS / KB;  // bins per thread (contiguous)
+    constexpr int PER_WAVE = RS_TILE / NW;
+    __shared__ int32_t base[NW][RS_BINS];
+    __shared__ uint32_t skey[RS_TILE];
+    __shared__ int32_t sval[RS_TILE];
+    __shared__ int waves[NW];
+    if (rows < 0) rows = rows_within(hdr, cap);
+    if (rows == 0) return;
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    const int32_t tile0 = blockIdx.x * RS_TILE;
+    // 0. the block's keys and values, in index order, into LDS (coalesced,
+    //    unconditional loads so that they are all in flight together)
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const int j = r * KB + threadIdx.x;
+        skey[j] = ld_clamped(keys_in, tile0 + j, rows);
+        sval[j] = vals_in ? ld_clamped(vals_in, tile0 + j, rows) : tile0 + j;
+    }
+    for (int w = 0; w < NW; ++w)
+        for (int j = threadIdx.x; j < RS_BINS; j += KB) base[w][j] = 0;
+    // 1. per-digit totals and this block's position among the blocks
+    //    (batches of independent loads keep the histogram reads pipelined)
+    constexpr int QB = 16;
+    int before[BPT], tot[BPT], local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int d = threadIdx.x * BPT + j;
+        const int32_t* row = hist + int64_t(d) * gridDim.x;
+        int b = 0, t = 0;
+        for (int q0 = 0; q0 < int(gridDim.x); q0 += QB) {
+            int v[QB];
+#pragma unroll
+            for (int u = 0; u < QB; ++u) v[u] = q0 + u < int(gridDim.x) ? row[q0 + u] : 0;
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                b += q0 + u < int(blockIdx.x) ? v[u] : 0;
+                t += v[u];
+            }
+        }
+        before[j] = b;
+        tot[j] = t;
+        local += t;
+    }
+    int total;
+    int digit_start = block_exclusive_scan<KB>(local, waves, total);  // (its barriers also publish LDS)
+    // 2. per-wave digit counts; wave w owns keys [w*PER_WAVE, (w+1)*PER_WAVE) of the block
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const int j = wave * PER_WAVE + r * WAVE + lane;
+        const bool valid = tile0 + j < rows;
+        const uint32_t d = (skey[j] >> shift) & (RS_BINS - 1);
+        const uint64_t peers = digit_peers(valid, d);  // one atomic per digit and wave
+        if (valid && (peers & lt) == 0) atomicAdd(&base[wave][d], int(__popcll(peers)));
+    }
+    __syncthreads();
+    // 3. wave bases: digit start + earlier blocks + earlier waves of this block
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int d = threadIdx.x * BPT + j;
+        int run = digit_start + before[j];
+        for (int w = 0; w < NW; ++w) {
+            const int c = base[w][d];
+            base[w][d] = run;
+            run += c;
+        }
+        digit_start += tot[j];
+    }
+    __syncthreads();
+    // 4. each wave writes its keys in order
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const int j = wave * PER_WAVE + r * WAVE + lane;
+        const bool valid = tile0 + j < rows;
+        const uint32_t key = skey[j];
+        const uint32_t d = (key >> shift) & (RS_BINS - 1);
+        const uint64_t peers = digit_peers(valid, d);
+        if (valid) {
+            const int rank = __popcll(peers & lt);
+            const int pos = base[wave][d] + rank;
+            keys_out[pos] = key;
+            vals_out[pos] = sval[j];
+            if (rank == 0) base[wave][d] += __popcll(peers);
+        }
+    }
+}
+
+// Identity order (used when K > 32 leaves no mask to sort by).
+__global__ void k_iota(int32_t* __restrict__ out, int32_t rows, int64_t cap, const uint32_t* hdr) {
+    if (rows < 0) rows = rows_within(hdr, cap);
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < rows; i += stride) out[i] = int32_t(i);
 }
 
 // ---------------------------------------------------------------- host side
@@ -396,10 +635,12 @@ struct Plan {
     int64_t out_vol;             // strided output grid volume
     int64_t nwords;              // bitmap words (multiple of WORDS_PER_THREAD)
     int64_t m_max;               // upper bound of the output row count
-    int64_t cblk;                // count-matrix blocks per offset (max over phases)
+    int64_t rows_max;            // max(n, m_max)
+    int64_t cblk;                // count-matrix blocks per offset
+    int64_t rblk;                // radix blocks
     int64_t bm_blocks;           // bitmap count/emit blocks
     // workspace offsets
-    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, total;
+    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_keys, off_vals, off_hist, total;
 };
 
 spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
@@ -413,10 +654,8 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
             return fail(SPC_ERR_UNSUPPORTED, "ksize[%d]=%d: supported kernel sizes are 1..7", a, g.ksize[a]);
         if (g.subm && g.ksize[a] % 2 == 0)
             return fail(SPC_ERR_ARG, "submanifold ksize[%d]=%d must be odd", a, g.ksize[a]);
-        if (!g.subm) {
-            if (g.stride[a] <= 0 || g.dil[a] <= 0 || g.pad[a] < 0)
-                return fail(SPC_ERR_ARG, "axis %d: stride=%d dil=%d pad=%d invalid", a, g.stride[a], g.dil[a], g.pad[a]);
-        }
+        if (!g.subm && (g.stride[a] <= 0 || g.dil[a] <= 0 || g.pad[a] < 0))
+            return fail(SPC_ERR_ARG, "axis %d: stride=%d dil=%d pad=%d invalid", a, g.stride[a], g.dil[a], g.pad[a]);
     }
     KGeom& k = p.g;
     k.batch = g.batch;
@@ -448,20 +687,26 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     if (int64_t(p.K) * n_in >= (int64_t(1) << 31))
         return fail(SPC_ERR_UNSUPPORTED, "K*n_in=%lld must be below 2^31", (long long)(int64_t(p.K) * n_in));
     p.n = n_in;
+    // load factor <= 1/4 keeps unsuccessful probes (most of them) near one load
     p.cap_log2 = 6;
-    while ((int64_t(1) << p.cap_log2) < 2 * n_in) ++p.cap_log2;
+    while ((int64_t(1) << p.cap_log2) < 4 * n_in) ++p.cap_log2;
     p.cap = int64_t(1) << p.cap_log2;
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
     p.nwords = g.subm ? 0 : ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb;
     p.bm_blocks = p.nwords / wpb;
     p.m_max = g.subm ? n_in : std::min<int64_t>(int64_t(p.K) * n_in, p.out_vol);
-    p.cblk = std::max<int64_t>(ceil_div(n_in, KB), ceil_div(p.m_max, KB));
+    p.rows_max = std::max(n_in, p.m_max);
+    p.cblk = ceil_div(p.rows_max, KB);
+    p.rblk = ceil_div(p.rows_max, RS_TILE);
     size_t off = 256;
     p.off_table = off;   off = align_up(off + size_t(p.cap) * 8, 256);
     p.off_counts = off;  off = align_up(off + size_t(p.K) * p.cblk * 4, 256);
     p.off_bitmap = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_prefix = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_bsums = off;   off = align_up(off + size_t(p.bm_blocks) * 4 + 4, 256);
+    p.off_keys = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two key buffers
+    p.off_vals = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two value buffers
+    p.off_hist = off;    off = align_up(off + size_t(RS_BINS) * p.rblk * 4, 256);
     p.total = off;
     return SPC_OK;
 }
@@ -469,6 +714,76 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
 inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 1 << 16) {
     int64_t b = ceil_div(std::max<int64_t>(work, 1), per_block);
     return unsigned(std::min<int64_t>(std::max<int64_t>(b, 1), cap));
+}
+
+struct Scratch {
+    uint32_t* hdr;
+    int32_t* counts;
+    uint32_t* keys[2];
+    int32_t* vals[2];
+    int32_t* hist;
+};
+
+// Row pass: masks into keys (K <= 32, NULL ok) and per-block counts (NULL ok).
+spc_status row_pass(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
+                    const Scratch& s, uint32_t* keys, int32_t* counts, hipStream_t stream) {
+    const int64_t blk = ceil_div(rows_cap, KB);
+    if (blk == 0) return SPC_OK;
+    hipLaunchKernelGGL(k_row_pass, dim3(unsigned(blk)), dim3(KB), 0, stream, map, rows_dev,
+                       p.K, cap, s.hdr, p.K <= MASK_BITS ? keys : nullptr, counts);
+    SPC_LAUNCHED("k_row_pass");
+    return SPC_OK;
+}
+
+// Stable LSD radix sort of the rows of `map` by neighbour mask into `order`
+// (the identity for K > 32).  keys_ready: s.keys[0] already holds the masks.
+// rows_dev < 0 means M from the header; grids are sized for rows_cap rows.
+spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
+                     const Scratch& s, bool keys_ready, int32_t* order, hipStream_t stream) {
+    const int K = p.K;
+    if (K > MASK_BITS) {
+        hipLaunchKernelGGL(k_iota, dim3(grid_for(rows_cap, KB, 4096)), dim3(KB), 0, stream, order, rows_dev, cap,
+                           s.hdr);
+        SPC_LAUNCHED("k_iota");
+        return SPC_OK;
+    }
+    if (rows_cap == 0) return SPC_OK;
+    if (!keys_ready) {
+        spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.keys[0], nullptr, stream);
+        if (st != SPC_OK) return st;
+    }
+    const unsigned nb = unsigned(ceil_div(rows_cap, RS_TILE));
+    const int passes = (K + RS_BITS - 1) / RS_BITS;
+    int cur = 0;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = RS_BITS * pass;
+        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(KB), 0, stream, s.keys[cur], rows_dev, cap, s.hdr, shift, s.hist);
+        SPC_LAUNCHED("k_rs_hist");
+        const bool last = pass + 1 == passes;
+        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(KB), 0, stream, s.keys[cur], pass == 0 ? nullptr : s.vals[cur],
+                           rows_dev, cap, s.hdr, shift, s.hist, s.keys[cur ^ 1], last ? order : s.vals[cur ^ 1]);
+        SPC_LAUNCHED("k_rs_scatter");
+        cur ^= 1;
+    }
+    return SPC_OK;
+}
+
+// Row pass (masks and counts), scan and ordered compaction of a map into CSR
+// pairs.  Leaves the masks in s.keys[0] (K <= 32).
+spc_status map_pairs(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
+                     const Scratch& s, int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, hipStream_t stream) {
+    const int64_t blk = ceil_div(rows_cap, KB);
+    spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.keys[0], s.counts, stream);
+    if (st != SPC_OK) return st;
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, s.counts, int64_t(p.K) * blk, pair_ptr, p.K,
+                       blk, (uint32_t*)nullptr);
+    SPC_LAUNCHED("k_scan");
+    if (blk > 0) {
+        hipLaunchKernelGGL(k_compact_pairs, dim3(unsigned(blk)), dim3(KB), 0, stream, map, rows_dev, p.K, cap, s.hdr,
+                           p.K <= ROWPASS_KMAX ? s.keys[0] : nullptr, s.counts, pair_in, pair_out);
+        SPC_LAUNCHED("k_compact_pairs");
+    }
+    return SPC_OK;
 }
 
 }  // namespace
@@ -508,6 +823,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                                      int32_t* out_coords, int64_t out_cap, int64_t* n_out,
                                      int32_t* nbr, int32_t* nbr_in,
                                      int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
+                                     int32_t* order, int32_t* order_in,
                                      int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream) {
     clear_error();
     Plan p;
@@ -524,96 +840,104 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     if (pairs && pair_cap < int64_t(p.K) * n_in) return fail(SPC_ERR_ARG, "pair_cap=%lld < K*n_in=%lld", (long long)pair_cap, (long long)(int64_t(p.K) * n_in));
     if (!strided_count_only && !nbr) return fail(SPC_ERR_ARG, "nbr is NULL");
     if (!subm && !strided_count_only && out_cap < 0) return fail(SPC_ERR_ARG, "out_cap < 0");
-    const void* ptrs[] = {coords, out_coords, nbr, nbr_in, pair_ptr, pair_in, pair_out, coord_err, ws};
+    if (subm && order_in) return fail(SPC_ERR_ARG, "order_in is for strided maps only");
+    if (order_in && !nbr_in && n_in > 0) return fail(SPC_ERR_ARG, "order_in needs nbr_in");
+    const void* ptrs[] = {coords, out_coords, nbr, nbr_in, pair_ptr, pair_in, pair_out, order, order_in, coord_err, ws};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
 
     char* base = static_cast<char*>(ws);
-    uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
+    Scratch s;
+    s.hdr = reinterpret_cast<uint32_t*>(base);
+    s.counts = reinterpret_cast<int32_t*>(base + p.off_counts);
+    s.keys[0] = reinterpret_cast<uint32_t*>(base + p.off_keys);
+    s.keys[1] = s.keys[0] + p.rows_max;
+    s.vals[0] = reinterpret_cast<int32_t*>(base + p.off_vals);
+    s.vals[1] = s.vals[0] + p.rows_max;
+    s.hist = reinterpret_cast<int32_t*>(base + p.off_hist);
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
-    int32_t* counts = reinterpret_cast<int32_t*>(base + p.off_counts);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(base + p.off_prefix);
     int32_t* bsums = reinterpret_cast<int32_t*>(base + p.off_bsums);
     const int4* c4 = reinterpret_cast<const int4*>(coords);
     const int32_t n = int32_t(n_in);
     const uint32_t mask = uint32_t(p.cap - 1);
-    const unsigned nblk = unsigned(std::max<int64_t>(ceil_div(n, KB), 1));
+    const int32_t nblk = int32_t(ceil_div(n, KB));
+    const int64_t entries = int64_t(n) * p.K;
 
     hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max(p.cap / 2, p.nwords / 4), KB, 4096)), dim3(KB), 0, stream,
-                       table, p.cap, bitmap, p.nwords, hdr);
+                       table, p.cap, bitmap, p.nwords, s.hdr);
     SPC_LAUNCHED("k_clear");
+    if (n > 0) {
+        if (subm)
+            hipLaunchKernelGGL(k_insert<false>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, bitmap, s.hdr);
+        else
+            hipLaunchKernelGGL(k_insert<true>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, bitmap, s.hdr);
+        SPC_LAUNCHED("k_insert");
+    }
 
     if (subm) {
-        if (n > 0) {
-            hipLaunchKernelGGL(k_insert<false>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask,
-                               bitmap, hdr);
-            SPC_LAUNCHED("k_insert");
-        }
-        hipLaunchKernelGGL(k_subm_probe, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, nbr,
-                           pairs ? counts : nullptr, hdr, coord_err);
+        hipLaunchKernelGGL(k_subm_probe, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
+                           stream, c4, n, p.g, table, mask, nbr, s.hdr, coord_err);
         SPC_LAUNCHED("k_subm_probe");
         if (pairs) {
-            const int64_t cb = n > 0 ? int64_t(nblk) : 0;
-            hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, counts, int64_t(p.K) * cb,
-                               pair_ptr, p.K, cb, (uint32_t*)nullptr);
-            SPC_LAUNCHED("k_scan");
-            if (n > 0) {
-                hipLaunchKernelGGL(k_compact_pairs, dim3(nblk, p.K), dim3(KB), 0, stream, nbr, n, counts,
-                                   pair_in, pair_out);
-                SPC_LAUNCHED("k_compact_pairs");
-            }
+            st = map_pairs(p, nbr, n, n, n, s, pair_ptr, pair_in, pair_out, stream);
+            if (st != SPC_OK) return st;
+        }
+        if (order) {
+            st = sort_rows(p, nbr, n, n, n, s, pairs, order, stream);
+            if (st != SPC_OK) return st;
         }
         *n_out = n_in;
         return SPC_OK;
     }
 
-    // strided: output sites into the bitmap, then count them
-    if (n > 0) {
-        hipLaunchKernelGGL(k_insert<true>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, bitmap, hdr);
-        SPC_LAUNCHED("k_insert");
-    }
+    // strided: output sites into the bitmap, then count them (total -> hdr)
     if (p.bm_blocks > 0) {
         hipLaunchKernelGGL(k_bitmap_count, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums);
         SPC_LAUNCHED("k_bitmap_count");
     }
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, bsums, p.bm_blocks, (int32_t*)nullptr, 0,
-                       int64_t(0), hdr + H_NOUT);
+                       int64_t(0), s.hdr + H_NOUT);
     SPC_LAUNCHED("k_scan");
     uint32_t host_hdr[2] = {0, 0};
-    SPC_HIP(hipMemcpyAsync(host_hdr, hdr, sizeof(host_hdr), hipMemcpyDeviceToHost, stream));
+    if (!strided_count_only) {
+        // Everything after the count is sized by the caller's capacity and reads
+        // M on the device, so the stream is synchronised only once, at the end.
+        const int64_t cap = std::min<int64_t>(out_cap, p.m_max);
+        if (p.bm_blocks > 0) {
+            hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords,
+                               bsums, prefix, reinterpret_cast<int4*>(out_coords), int64_t(out_cap), s.hdr, p.g);
+            SPC_LAUNCHED("k_bitmap_emit");
+        }
+        hipLaunchKernelGGL(k_fill_map, dim3(grid_for(cap * p.K, KB, 4096)), dim3(KB), 0, stream, nbr, p.K,
+                           int64_t(out_cap), s.hdr);
+        SPC_LAUNCHED("k_fill_map");
+        hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
+                           stream, c4, n, int64_t(out_cap), p.g, bitmap, prefix, nbr, nbr_in, s.hdr, coord_err);
+        SPC_LAUNCHED("k_strided_maps");
+        if (pairs) {
+            st = map_pairs(p, nbr, -1, cap, int64_t(out_cap), s, pair_ptr, pair_in, pair_out, stream);
+            if (st != SPC_OK) return st;
+        }
+        if (order) {
+            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, pairs, order, stream);
+            if (st != SPC_OK) return st;
+        }
+        if (order_in) {
+            st = sort_rows(p, nbr_in, n, n, n, s, false, order_in, stream);
+            if (st != SPC_OK) return st;
+        }
+    }
+    SPC_HIP(hipMemcpyAsync(host_hdr, s.hdr, sizeof(host_hdr), hipMemcpyDeviceToHost, stream));
     SPC_HIP(hipStreamSynchronize(stream));
     const int64_t M = host_hdr[H_NOUT];
     *n_out = M;
-    if (host_hdr[H_FLAGS]) {
-        if (coord_err) SPC_HIP(hipMemcpyAsync(coord_err, hdr, 4, hipMemcpyDeviceToDevice, stream));
+    if (host_hdr[H_FLAGS] & (SPC_COORD_OUT_OF_RANGE | SPC_COORD_DUPLICATE))
         return fail(SPC_ERR_COORD, "input coordinates: %s%s",
                     (host_hdr[H_FLAGS] & SPC_COORD_OUT_OF_RANGE) ? "out of range " : "",
                     (host_hdr[H_FLAGS] & SPC_COORD_DUPLICATE) ? "duplicate" : "");
-    }
-    if (strided_count_only) return SPC_OK;
-    if (M > out_cap) return fail(SPC_ERR_CAPACITY, "%lld output sites exceed out_cap=%lld", (long long)M, (long long)out_cap);
-
-    if (p.bm_blocks > 0) {
-        hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums,
-                           prefix, reinterpret_cast<int4*>(out_coords), p.g);
-        SPC_LAUNCHED("k_bitmap_emit");
-    }
-    const int32_t mblk = int32_t(ceil_div(M, KB));
-    const int32_t iblk = nbr_in ? int32_t(ceil_div(n, KB)) : 0;
-    hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max(mblk + iblk, 1))), dim3(KB), 0, stream, c4, n,
-                       reinterpret_cast<const int4*>(out_coords), int32_t(M), mblk, p.g, table, mask, bitmap, prefix,
-                       nbr, nbr_in, pairs ? counts : nullptr, hdr, coord_err);
-    SPC_LAUNCHED("k_strided_maps");
-    if (pairs) {
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, counts, int64_t(p.K) * mblk, pair_ptr,
-                           p.K, int64_t(mblk), (uint32_t*)nullptr);
-        SPC_LAUNCHED("k_scan");
-        if (mblk > 0) {
-            hipLaunchKernelGGL(k_compact_pairs, dim3(unsigned(mblk), p.K), dim3(KB), 0, stream, nbr, int32_t(M), counts,
-                               pair_in, pair_out);
-            SPC_LAUNCHED("k_compact_pairs");
-        }
-    }
+    if (!strided_count_only && M > out_cap)
+        return fail(SPC_ERR_CAPACITY, "%lld output sites exceed out_cap=%lld", (long long)M, (long long)out_cap);
     return SPC_OK;
 }

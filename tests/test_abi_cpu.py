@@ -75,7 +75,8 @@ def test_build_kmap_host_checks():
     def call(**kw):
         a = args(**kw)
         return L.spc_build_kmap(ctypes.byref(g), a["coords"], 10, None, 0, ctypes.byref(n_out), a["nbr"], None,
-                                a["pp"], a["pi"], a["po"], a["cap"], None, a["ws"], a["wsb"], None)
+                                a["pp"], a["pi"], a["po"], a["cap"], None, a.get("order_in"), None, a["ws"],
+                                a["wsb"], None)
     assert call(ws=None) == B.SPC_ERR_ARG
     assert call(wsb=16) == B.SPC_ERR_WORKSPACE
     assert call(coords=None) == B.SPC_ERR_ARG
@@ -84,12 +85,13 @@ def test_build_kmap_host_checks():
     assert call(pp=FAKE) == B.SPC_ERR_ARG                       # pair lists: all or none
     assert call(pp=FAKE, pi=FAKE, po=FAKE, cap=10) == B.SPC_ERR_ARG  # pair_cap < K * n
     assert "pair_cap" in B.lib().spc_last_error().decode()
+    assert call(order_in=FAKE) == B.SPC_ERR_ARG                 # order_in is for strided maps
 
 
 def test_conv_host_checks():
     L = B.lib()
     fwd = lambda dt, cin, cout, K, nbr=FAKE, x=FAKE: L.spc_subm_conv_fwd(dt, x, 100, cin, FAKE, K, cout, None,
-                                                                        nbr, FAKE, None)
+                                                                        nbr, None, FAKE, None)
     assert fwd(2, 24, 32, 27) == B.SPC_ERR_UNSUPPORTED          # cin not a multiple of 16
     assert fwd(2, 32, 8, 27) == B.SPC_ERR_UNSUPPORTED
     assert fwd(7, 32, 32, 27) == B.SPC_ERR_ARG                  # dtype
@@ -97,9 +99,10 @@ def test_conv_host_checks():
     assert fwd(2, 32, 32, 27, nbr=None) == B.SPC_ERR_ARG        # map required for K > 1
     assert fwd(2, 32, 32, 27, x=MISALIGNED) == B.SPC_ERR_ARG
     # zero rows: valid, nothing launched
-    assert L.spc_subm_conv_fwd(2, None, 0, 32, FAKE, 27, 32, None, None, FAKE, None) == B.SPC_OK
+    assert L.spc_subm_conv_fwd(2, None, 0, 32, FAKE, 27, 32, None, None, None, FAKE, None) == B.SPC_OK
     # submanifold dinput needs n_out == n_in
-    assert L.spc_conv_bwd_input(1, FAKE, 10, 64, FAKE, 27, 64, FAKE, 1, 11, FAKE, None) == B.SPC_ERR_ARG
+    assert L.spc_conv_bwd_input(1, FAKE, 10, 64, FAKE, 27, 64, FAKE, 1, None, 11, FAKE, None) == B.SPC_ERR_ARG
+    assert L.spc_subm_conv_fwd(2, FAKE, 100, 32, FAKE, 27, 32, None, FAKE, MISALIGNED, FAKE, None) == B.SPC_ERR_ARG
     b = ctypes.c_size_t()
     assert L.spc_conv_bwd_filter_workspace(1000, 1000, 64, 64, 27, 1, ctypes.byref(b)) == B.SPC_OK and b.value > 0
     # dfilter: identity pairs only for K == 1, workspace size enforced

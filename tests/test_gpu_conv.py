@@ -23,19 +23,20 @@ def _subm_case(seed, side, fill, batch, k, cin, cout, dtype, bias=True):
     return c, t
 
 
-def run_subm_layer(c, batch, shape, k, t, dtype, train=True, what=""):
+def run_subm_layer(c, batch, shape, k, t, dtype, train=True, what="", ordered=True):
     """Forward (and dinput / dfilter / dbias) of one submanifold layer vs the oracle."""
-    print(f"subm conv {what} n={c.shape[0]} k={k} {tuple(t['weight'].shape)} {dtype}", flush=True)
-    km = spc.build_kmap(cuda(c), batch, shape, k, pairs=train)
+    print(f"subm conv {what} n={c.shape[0]} k={k} {tuple(t['weight'].shape)} {dtype} ordered={ordered}", flush=True)
+    km = spc.build_kmap(cuda(c), batch, shape, k, pairs=train, orders=ordered)
     nbr_ref = O.subm_kmap(c, shape, k)
     x, w = cuda(t["feats"]), cuda(t["weight"])
     b = cuda(t["bias"]) if t.get("bias") is not None else None
-    out = spc.subm_conv_fwd(x, w, b, km["nbr"] if k > 1 else None)
+    order = km.get("order") if k > 1 else None
+    out = spc.subm_conv_fwd(x, w, b, km["nbr"] if k > 1 else None, order)
     errs = {"fwd": assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr_ref), TOL[dtype], "fwd")}
     if not train:
         return errs
     g = cuda(t["grad"])
-    din = spc.conv_bwd_input(g, w, km["nbr"] if k > 1 else None, True, c.shape[0])
+    din = spc.conv_bwd_input(g, w, km["nbr"] if k > 1 else None, True, c.shape[0], order)
     errs["din"] = assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], nbr_ref, c.shape[0]), TOL[dtype], "din")
     pp, pi, po = (km["pair_ptr"], km["pair_in"], km["pair_out"]) if k > 1 else (None, None, None)
     dw, db = spc.conv_bwd_filter(x, g, k ** 3, pp, pi, po, want_dbias=True)
@@ -58,7 +59,7 @@ def test_subm_small(dtype, seed, side, fill, batch, k, cin, cout):
     if dtype == torch.float32 and cin > 128:
         pytest.skip("fp32 contraction is limited to 128 channels")
     c, t = _subm_case(seed, side, fill, batch, k, cin, cout, dtype)
-    run_subm_layer(c, batch, (side,) * 3, k, t, dtype)
+    run_subm_layer(c, batch, (side,) * 3, k, t, dtype, ordered=seed % 2 == 1)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -67,7 +68,7 @@ def test_single_voxel_and_empty(dtype):
     t = W.small_layer(3, c, 16, 32, 27, dtype)
     run_subm_layer(c, 1, (4, 4, 4), 3, t, dtype)
     out = spc.subm_conv_fwd(cuda(t["feats"][:0]), cuda(t["weight"]), None,
-                            torch.empty((27, 0), dtype=torch.int32, device="cuda"))
+                            torch.empty((0, 27), dtype=torch.int32, device="cuda"))
     assert out.shape == (0, 32)
 
 
@@ -78,14 +79,16 @@ def test_single_voxel_and_empty(dtype):
 def test_strided_small(dtype, shape, k, s, p, d, cin, cout):
     c = W.tiny_grid(W.rng(40 + k + s), min(shape), 0.25, 2)
     print(f"strided conv n={c.shape[0]} {shape} k={k} s={s} {dtype}", flush=True)
-    km = spc.build_kmap(cuda(c), 2, shape, k, s, p, d, subm=False)
+    km = spc.build_kmap(cuda(c), 2, shape, k, s, p, d, subm=False, orders=True)
     ref = O.strided_kmap(c, 2, shape, k, s, p, d)
     M = ref["out_coords"].shape[0]
     t = W.small_layer(50, c, cin, cout, k ** 3, dtype, n_out=M)
     x, w, b, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"]), cuda(t["grad"])
-    out = spc.sparse_conv_fwd(x, w, b, km["nbr"], km["n_out"])
+    out = spc.sparse_conv_fwd(x, w, b, km["nbr"], km["n_out"], km["order"])
     assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], ref["nbr_out"]), TOL[dtype], "fwd")
-    din = spc.conv_bwd_input(g, w, km["nbr_in"], False, c.shape[0])
+    out2 = spc.sparse_conv_fwd(x, w, b, km["nbr"], km["n_out"])
+    assert torch.equal(out, out2)          # the processing order never changes a result
+    din = spc.conv_bwd_input(g, w, km["nbr_in"], False, c.shape[0], km["order_in"])
     assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], ref["nbr_out"], c.shape[0]), TOL[dtype], "din")
     dw, db = spc.conv_bwd_filter(x, g, k ** 3, km["pair_ptr"], km["pair_in"], km["pair_out"], want_dbias=True)
     assert_close(dw, OC.conv_bwd_filter(t["feats"], t["grad"], ref["nbr_out"]), TOL_DW, "dw")
@@ -94,10 +97,14 @@ def test_strided_small(dtype, shape, k, s, p, d, cin, cout):
 
 def test_deterministic():
     c, t = _subm_case(8, 20, 0.3, 2, 3, 64, 64, torch.bfloat16)
-    km = spc.build_kmap(cuda(c), 2, (20,) * 3, 3)
+    km = spc.build_kmap(cuda(c), 2, (20,) * 3, 3, orders=True)
     x, w, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["grad"])
     o1, o2 = spc.subm_conv_fwd(x, w, None, km["nbr"]), spc.subm_conv_fwd(x, w, None, km["nbr"])
     assert torch.equal(o1, o2)
+    # the processing order regroups rows into tiles but never changes a result
+    assert torch.equal(o1, spc.subm_conv_fwd(x, w, None, km["nbr"], km["order"]))
+    d1 = spc.conv_bwd_input(g, w, km["nbr"], True, c.shape[0])
+    assert torch.equal(d1, spc.conv_bwd_input(g, w, km["nbr"], True, c.shape[0], km["order"]))
     a = spc.conv_bwd_filter(x, g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"], True)
     b = spc.conv_bwd_filter(x, g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"], True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
@@ -120,10 +127,10 @@ def test_workload_lidar_fp16():
 def test_workload_shells_bf16_k3_then_k1():
     w = W.workload("subm_k3_k1_bf16_shells128")
     print(f"{w.name} n={w.n}", flush=True)
-    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, pairs=False)
+    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, pairs=False, orders=True)
     nbr_ref = O.subm_kmap(w.coords, w.shape, 3)
     x, wt, w1 = cuda(w.feats), cuda(w.weight), cuda(w.extra["weight_k1"])
-    y = spc.subm_conv_fwd(x, wt, None, km["nbr"])
+    y = spc.subm_conv_fwd(x, wt, None, km["nbr"], km["order"])
     y_ref = OC.conv_fwd(w.feats, w.weight, None, nbr_ref)
     assert_close(y, y_ref, TOL[w.dtype], "k3")
     # layer 2 (k=1) consumes the GPU's own bf16 layer-1 output; the oracle gets the same values
@@ -133,15 +140,15 @@ def test_workload_shells_bf16_k3_then_k1():
 
 def test_workload_strided_lidar_fp16():
     w = W.workload("strided_k3s2_f16_lidar120k")
-    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False)
+    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
     ref = O.strided_kmap(w.coords, w.batch, w.shape, 3, 2, 1, 1)
     M = km["n_out"]
     print(f"{w.name} n={w.n} M={M}", flush=True)
     g = W.grad_for(w.extra["grad_rng"], M, w.cout, w.dtype)
     x, wt, gd = cuda(w.feats), cuda(w.weight), cuda(g)
-    out = spc.sparse_conv_fwd(x, wt, None, km["nbr"], M)
+    out = spc.sparse_conv_fwd(x, wt, None, km["nbr"], M, km["order"])
     assert_close(out, OC.conv_fwd(w.feats, w.weight, None, ref["nbr_out"]), TOL[w.dtype], "fwd")
-    din = spc.conv_bwd_input(gd, wt, km["nbr_in"], False, w.n)
+    din = spc.conv_bwd_input(gd, wt, km["nbr_in"], False, w.n, km["order_in"])
     assert_close(din, OC.conv_bwd_input(g, w.weight, ref["nbr_out"], w.n), TOL[w.dtype], "din")
     dw, _ = spc.conv_bwd_filter(x, gd, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
     assert_close(dw, OC.conv_bwd_filter(w.feats, g, ref["nbr_out"]), TOL_DW, "dw")

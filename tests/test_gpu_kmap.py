@@ -16,27 +16,42 @@ from tests.parity import cuda, host, pairs_equal
 pytestmark = pytest.mark.gpu
 
 
-def check_subm(coords, batch, shape, k, pairs=True):
+def mask_order(map_kn):
+    """Rows sorted by neighbour mask (bit k set iff map[k][row] >= 0), ties by row."""
+    K, n = map_kn.shape
+    if K > 32:
+        return np.arange(n)
+    m = np.zeros(n, np.int64)
+    for k in range(K):
+        m |= (map_kn[k] >= 0).astype(np.int64) << k
+    return np.argsort(m, kind="stable")
+
+
+def check_subm(coords, batch, shape, k, pairs=True, orders=True):
     print(f"subm kmap n={coords.shape[0]} shape={shape} k={k}", flush=True)
-    res = spc.build_kmap(cuda(coords), batch, shape, k, subm=True, pairs=pairs)
+    res = spc.build_kmap(cuda(coords), batch, shape, k, subm=True, pairs=pairs, orders=orders)
     ref = O.subm_kmap(coords, shape, k)
     assert res["n_out"] == coords.shape[0]
-    assert np.array_equal(host(res["nbr"]), ref)
+    assert np.array_equal(host(res["nbr"]), ref.T)
     assert int(host(res["coord_err"])[0]) == 0
     if pairs:
         pairs_equal(res, *O.pairs_from_map(ref))
+    if orders:
+        assert np.array_equal(host(res["order"]), mask_order(ref))
     return res
 
 
 def check_strided(coords, batch, shape, k, s, p, d, out_cap=None):
     print(f"strided kmap n={coords.shape[0]} shape={shape} k={k} s={s} p={p} d={d}", flush=True)
-    res = spc.build_kmap(cuda(coords), batch, shape, k, s, p, d, subm=False, out_cap=out_cap)
+    res = spc.build_kmap(cuda(coords), batch, shape, k, s, p, d, subm=False, out_cap=out_cap, orders=True)
     ref = O.strided_kmap(coords, batch, shape, k, s, p, d)
     assert res["n_out"] == ref["out_coords"].shape[0]
     assert np.array_equal(host(res["out_coords"]), ref["out_coords"])
-    assert np.array_equal(host(res["nbr"]), ref["nbr_out"])
-    assert np.array_equal(host(res["nbr_in"]), ref["nbr_in"])
+    assert np.array_equal(host(res["nbr"]), ref["nbr_out"].T)
+    assert np.array_equal(host(res["nbr_in"]), ref["nbr_in"].T)
     pairs_equal(res, *O.pairs_from_map(ref["nbr_out"]))
+    assert np.array_equal(host(res["order"]), mask_order(ref["nbr_out"]))
+    assert np.array_equal(host(res["order_in"]), mask_order(ref["nbr_in"]))
     return res
 
 
@@ -72,7 +87,7 @@ def test_subm_flags_bad_coordinates():
     res = spc.build_kmap(cuda(c), 1, shape, 3)
     assert int(host(res["coord_err"])[0]) == spc.binding.COORD_OUT_OF_RANGE
     nbr = host(res["nbr"])
-    assert nbr[13, 0] == 0 and (nbr[:, 1:] == -1).all()      # bad rows are left out
+    assert nbr[0, 13] == 0 and (nbr[1:, :] == -1).all()      # bad rows are left out
 
 
 @pytest.mark.parametrize("seed,shape,fill,batch,k,s,p,d", [
@@ -95,7 +110,7 @@ def test_strided_lidar_workload():
     w = W.workload("strided_k3s2_f16_lidar120k")
     res = check_strided(w.coords, w.batch, w.shape, 3, 2, 1, 1)
     # the same call with an exact capacity (no counting pass) gives the same maps
-    res2 = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=res["n_out"])
+    res2 = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=res["n_out"], orders=True)
     assert torch.equal(res["nbr"], res2["nbr"]) and torch.equal(res["out_coords"], res2["out_coords"])
 
 
@@ -106,6 +121,7 @@ def test_strided_golden_empty_output():
     assert res["n_out"] == g["expected_n_out"]
     assert int(host(res["pair_ptr"])[-1]) == 0
     assert (host(res["nbr_in"]) == -1).all()
+    assert res["nbr"].shape == (0, 27)
 
 
 def test_strided_capacity_and_errors():
@@ -123,6 +139,9 @@ def test_strided_capacity_and_errors():
 def test_kmap_repeatable():
     w = W.workload("subm_k3_f16_lidar120k")
     c = cuda(w.coords)
-    a = spc.build_kmap(c, w.batch, w.shape, 3)
-    b = spc.build_kmap(c, w.batch, w.shape, 3)
-    assert torch.equal(a["nbr"], b["nbr"]) and torch.equal(a["pair_in"], b["pair_in"])
+    a = spc.build_kmap(c, w.batch, w.shape, 3, orders=True)
+    b = spc.build_kmap(c, w.batch, w.shape, 3, orders=True)
+    P = int(a["pair_ptr"][-1])
+    assert torch.equal(a["nbr"], b["nbr"]) and torch.equal(a["pair_ptr"], b["pair_ptr"])
+    assert torch.equal(a["pair_in"][:P], b["pair_in"][:P]) and torch.equal(a["pair_out"][:P], b["pair_out"][:P])
+    assert torch.equal(a["order"], b["order"])
