@@ -20,7 +20,8 @@
 // and the per-(offset, block) hit counts; pair lists are compacted in
 // (offset, row) order by one exclusive scan and an ordered ballot/prefix write
 // pass.  The processing order is a stable LSD radix sort of (mask, row) with
-// 8-bit digits: per pass a block histogram, one scan and a stable scatter.
+// 9-bit digits: per pass a block histogram whose last block scans the
+// histogram matrix into slot offsets, and a stable scatter.
 #include <stdio.h>
 
 #include <algorithm>
@@ -35,9 +36,11 @@ constexpr int KB = 256;          // threads per block of the per-row / per-entry
 constexpr int WORDS_PER_THREAD = 8;
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER_THREAD = 16;
-constexpr int RS_ITEMS = 32;                 // keys per thread in the radix passes (few, large tiles:
-                                             // a block reads the histogram of every block)
-constexpr int RS_TILE = KB * RS_ITEMS;       // keys per radix block
+constexpr int RS_THREADS = 512;              // threads per radix block (one per digit in the spine)
+constexpr int RS_ITEMS = 4;                  // keys per thread in the radix passes
+constexpr int RS_TILE = RS_THREADS * RS_ITEMS;  // keys per radix block
+constexpr int RS_GROUP = 16;                 // radix blocks per group of the two-level offset sums
+constexpr int RS_MAX_PASSES = 4;             // K <= 32 bits of mask, 9 bits per pass
 constexpr int RS_BITS = 9;                   // digit width of the radix passes
 constexpr int RS_BINS = 1 << RS_BITS;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
@@ -145,15 +148,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
 
 // ---------------------------------------------------------------- kernels
 
-// Fills the table with the empty marker, zeroes the bitmap and the header.
+// Fills the table with the empty marker; zeroes the bitmap, the header and
+// `zero` (nzero ints, a multiple of 4).
 __global__ void k_clear(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ bitmap,
-                        int64_t nwords, uint32_t* __restrict__ hdr) {
+                        int64_t nwords, uint32_t* __restrict__ hdr, int32_t* __restrict__ zero, int64_t nzero) {
     const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     if (t < H_WORDS) hdr[t] = 0u;
     u32x4 ones = {~0u, ~0u, ~0u, ~0u};
     for (int64_t i = t; i < cap / 2; i += stride) st16(table + 2 * i, ones);
     for (int64_t i = t; i < nwords / 4; i += stride) st16(bitmap + 4 * i, zero4());
+    for (int64_t i = t; i < nzero / 4; i += stride) st16(zero + 4 * i, zero4());
 }
 
 // Fills rows [0, M) of a [rows][K] map with -1 (M read on the device).
@@ -488,131 +493,126 @@ __device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d) {
 }
 
 // Radix sort.  A block owns RS_TILE consecutive keys; wave w of the block
-// owns the contiguous run [w * RS_TILE / 4, (w + 1) * RS_TILE / 4), taken 64
-// at a time, so the block's keys are visited in index order per wave.
-__device__ __forceinline__ int32_t rs_index(int r) {
-    constexpr int PER_WAVE = RS_TILE / (KB / WAVE);
-    return int32_t(blockIdx.x) * RS_TILE + (threadIdx.x / WAVE) * PER_WAVE + r * WAVE + (threadIdx.x & (WAVE - 1));
-}
+// owns the contiguous run [w * RS_TILE / NW, (w + 1) * RS_TILE / NW), taken
+// 64 at a time, so the block's keys are visited in index order per wave.
+constexpr int RS_WAVES = RS_THREADS / WAVE;
+constexpr int RS_PER_WAVE = RS_TILE / RS_WAVES;
+static_assert(RS_THREADS == RS_BINS, "one thread per digit");
 
-// Pass histogram: hist[d*nblk + block] = number of the block's keys whose
-// digit (key >> shift) & (RS_BINS-1) is d.  rows < 0: M from the header.
-__global__ __launch_bounds__(KB) void k_rs_hist(const uint32_t* __restrict__ keys, int32_t rows, int64_t cap,
-                                                const uint32_t* hdr, int shift, int32_t* __restrict__ hist) {
+// Pass histogram.  Every block counts the digits (key >> shift) &
+// (RS_BINS-1) of its tile into hist[d*nb + block] and adds them to the sums
+// of its group of RS_GROUP blocks, gsum[d*ng + block/RS_GROUP] (zeroed
+// beforehand).  rows < 0: M from the header.
+__global__ __launch_bounds__(RS_THREADS) void k_rs_hist(const uint32_t* __restrict__ keys, int32_t rows, int64_t cap,
+                                                        const uint32_t* hdr, int shift, int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ gsum, int ng) {
     __shared__ int32_t h[RS_BINS];
     if (rows < 0) rows = rows_within(hdr, cap);
-    if (rows == 0) return;
-    for (int d = threadIdx.x; d < RS_BINS; d += KB) h[d] = 0;
-    uint32_t dig[RS_ITEMS];
+    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
+    if (tile0 >= rows) return;  // uniform per block; later blocks are never read
+    const int t = threadIdx.x;
+    uint32_t k[RS_ITEMS];
 #pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) dig[r] = ld_clamped(keys, rs_index(r), rows);  // all in flight
+    for (int r = 0; r < RS_ITEMS; ++r) k[r] = ld_clamped(keys, tile0 + r * RS_THREADS + t, rows);
+    h[t] = 0;
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < RS_ITEMS; ++r)
-        dig[r] = rs_index(r) < rows ? (dig[r] >> shift) & (RS_BINS - 1) : RS_BINS;
+        if (tile0 + r * RS_THREADS + t < rows) atomicAdd(h + ((k[r] >> shift) & (RS_BINS - 1)), 1);
     __syncthreads();
-    const uint64_t lt = (1ull << (threadIdx.x & (WAVE - 1))) - 1ull;
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const bool valid = dig[r] < RS_BINS;
-        const uint64_t peers = digit_peers(valid, dig[r] & (RS_BINS - 1));  // one atomic per digit and wave
-        if (valid && (peers & lt) == 0) atomicAdd(h + dig[r], int(__popcll(peers)));
-    }
-    __syncthreads();
-    for (int d = threadIdx.x; d < RS_BINS; d += KB) hist[int64_t(d) * gridDim.x + blockIdx.x] = h[d];
+    const int c = h[t];
+    hist[int64_t(t) * gridDim.x + blockIdx.x] = c;
+    if (c) atomicAdd(gsum + int64_t(t) * ng + blockIdx.x / RS_GROUP, c);
 }
 
-// Pass scatter, stable.  The block first derives its slot base per digit from
-// the histogram matrix (all keys of smaller digits, plus this digit's keys in
-// earlier blocks), then the base of each wave (this digit's keys in earlier
-// waves of the block); each wave then ranks its keys among equal digits with
-// RS_BITS ballots and writes them in order, without further barriers.
-// vals_in == NULL means the identity (row index).
-__global__ __launch_bounds__(KB) void k_rs_scatter(const uint32_t* __restrict__ keys_in,
-                                                   const int32_t* __restrict__ vals_in, int32_t rows, int64_t cap,
-                                                   const uint32_t* hdr, int shift, const int32_t* __restrict__ hist,
-                                                   uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
-    constexpr int NW = KB / WAVE;
-    constexpr int BPT = RS_BINS / KB;  // bins per thread (contiguous)
-    constexpr int PER_WAVE = RS_TILE / NW;
-    __shared__ int32_t base[NW][RS_BINS];
+// Pass scatter, stable.  Slot base of digit d for this block: keys of
+// smaller digits, plus digit-d keys of earlier groups (group sums) and of
+// earlier blocks of this group (histogram columns); each wave adds the
+// counts of earlier waves of the block, then ranks its keys among equal
+// digits with RS_BITS ballots (computed once, for counting and writing) and
+// writes them in order.  vals_in == NULL means the identity (row index).
+__global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(const uint32_t* __restrict__ keys_in,
+                                                           const int32_t* __restrict__ vals_in, int32_t rows,
+                                                           int64_t cap, const uint32_t* hdr, int shift,
+                                                           const int32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ gsum, int ng,
+                                                           uint32_t* __restrict__ keys_out,
+                                                           int32_t* __restrict__ vals_out) {
+    __shared__ int32_t base[RS_WAVES][RS_BINS];
     __shared__ uint32_t skey[RS_TILE];
     __shared__ int32_t sval[RS_TILE];
-    __shared__ int waves[NW];
     if (rows < 0) rows = rows_within(hdr, cap);
-    if (rows == 0) return;
-    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-    const int32_t tile0 = blockIdx.x * RS_TILE;
+    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
+    if (tile0 >= rows) return;  // uniform per block
+    const int t = threadIdx.x, lane = t & (WAVE - 1), wave = t / WAVE;
     // 0. the block's keys and values, in index order, into LDS (coalesced,
     //    unconditional loads so that they are all in flight together)
 #pragma unroll
     for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = r * KB + threadIdx.x;
+        const int j = r * RS_THREADS + t;
         skey[j] = ld_clamped(keys_in, tile0 + j, rows);
         sval[j] = vals_in ? ld_clamped(vals_in, tile0 + j, rows) : tile0 + j;
     }
-    for (int w = 0; w < NW; ++w)
-        for (int j = threadIdx.x; j < RS_BINS; j += KB) base[w][j] = 0;
-    // 1. per-digit totals and this block's position among the blocks
-    //    (batches of independent loads keep the histogram reads pipelined)
-    constexpr int QB = 16;
-    int before[BPT], tot[BPT], local = 0;
+    // digit t: totals over the groups and the part before this block
+    const int me = int(blockIdx.x), g_me = me / RS_GROUP, b0 = g_me * RS_GROUP;
+    int tot = 0, before = 0;
+    {
+        const int32_t* gs = gsum + int64_t(t) * ng;
+        const int32_t* hc = hist + int64_t(t) * gridDim.x;
+        int hv[RS_GROUP];
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int d = threadIdx.x * BPT + j;
-        const int32_t* row = hist + int64_t(d) * gridDim.x;
-        int b = 0, t = 0;
-        for (int q0 = 0; q0 < int(gridDim.x); q0 += QB) {
-            int v[QB];
+        for (int u = 0; u < RS_GROUP; ++u) hv[u] = ld_clamped(hc, b0 + u, int64_t(me) + 1);
+        for (int q0 = 0; q0 < ng; q0 += RS_GROUP) {
+            int v[RS_GROUP];
 #pragma unroll
-            for (int u = 0; u < QB; ++u) v[u] = q0 + u < int(gridDim.x) ? row[q0 + u] : 0;
+            for (int u = 0; u < RS_GROUP; ++u) v[u] = ld_clamped(gs, q0 + u, ng);
 #pragma unroll
-            for (int u = 0; u < QB; ++u) {
-                b += q0 + u < int(blockIdx.x) ? v[u] : 0;
-                t += v[u];
+            for (int u = 0; u < RS_GROUP; ++u) {
+                tot += q0 + u < ng ? v[u] : 0;
+                before += q0 + u < g_me ? v[u] : 0;
             }
         }
-        before[j] = b;
-        tot[j] = t;
-        local += t;
-    }
-    int total;
-    int digit_start = block_exclusive_scan<KB>(local, waves, total);  // (its barriers also publish LDS)
-    // 2. per-wave digit counts; wave w owns keys [w*PER_WAVE, (w+1)*PER_WAVE) of the block
-    const uint64_t lt = (1ull << lane) - 1ull;
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = wave * PER_WAVE + r * WAVE + lane;
-        const bool valid = tile0 + j < rows;
-        const uint32_t d = (skey[j] >> shift) & (RS_BINS - 1);
-        const uint64_t peers = digit_peers(valid, d);  // one atomic per digit and wave
-        if (valid && (peers & lt) == 0) atomicAdd(&base[wave][d], int(__popcll(peers)));
-    }
-    __syncthreads();
-    // 3. wave bases: digit start + earlier blocks + earlier waves of this block
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int d = threadIdx.x * BPT + j;
-        int run = digit_start + before[j];
-        for (int w = 0; w < NW; ++w) {
-            const int c = base[w][d];
-            base[w][d] = run;
-            run += c;
-        }
-        digit_start += tot[j];
+        for (int u = 0; u < RS_GROUP; ++u) before += b0 + u < me ? hv[u] : 0;
+    }
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) base[w][t] = 0;
+    __shared__ int waves[RS_WAVES];
+    int total;
+    const int32_t my_off = block_exclusive_scan<RS_THREADS>(tot, waves, total) + before;
+    // (the scan's barriers also publish the LDS keys and the cleared bases)
+    // 1. per-wave digit counts; wave w owns keys [w*RS_PER_WAVE, (w+1)*RS_PER_WAVE) of the block
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint64_t peers[RS_ITEMS];
+    uint32_t dig[RS_ITEMS];
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const int j = wave * RS_PER_WAVE + r * WAVE + lane;
+        const bool valid = tile0 + j < rows;
+        dig[r] = (skey[j] >> shift) & (RS_BINS - 1);
+        peers[r] = digit_peers(valid, dig[r]);
+        if (valid && (peers[r] & lt) == 0) base[wave][dig[r]] += int(__popcll(peers[r]));  // one leader per digit
     }
     __syncthreads();
-    // 4. each wave writes its keys in order
+    // 2. wave bases: block base + earlier waves of this block
+    int run = my_off;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+        const int c = base[w][t];
+        base[w][t] = run;
+        run += c;
+    }
+    __syncthreads();
+    // 3. each wave writes its keys in order
+#pragma unroll
     for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = wave * PER_WAVE + r * WAVE + lane;
-        const bool valid = tile0 + j < rows;
-        const uint32_t key = skey[j];
-        const uint32_t d = (key >> shift) & (RS_BINS - 1);
-        const uint64_t peers = digit_peers(valid, d);
-        if (valid) {
-            const int rank = __popcll(peers & lt);
-            const int pos = base[wave][d] + rank;
-            keys_out[pos] = key;
+        const int j = wave * RS_PER_WAVE + r * WAVE + lane;
+        if (tile0 + j < rows) {
+            const int rank = __popcll(peers[r] & lt);
+            const int pos = base[wave][dig[r]] + rank;
+            keys_out[pos] = skey[j];
             vals_out[pos] = sval[j];
-            if (rank == 0) base[wave][d] += __popcll(peers);
+            if (rank == 0) base[wave][dig[r]] += __popcll(peers[r]);
         }
     }
 }
@@ -640,7 +640,8 @@ struct Plan {
     int64_t rblk;                // radix blocks
     int64_t bm_blocks;           // bitmap count/emit blocks
     // workspace offsets
-    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_keys, off_vals, off_hist, total;
+    int64_t rgroups;             // radix block groups
+    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_keys, off_vals, off_hist, off_gsum, total;
 };
 
 spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
@@ -707,6 +708,8 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     p.off_keys = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two key buffers
     p.off_vals = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two value buffers
     p.off_hist = off;    off = align_up(off + size_t(RS_BINS) * p.rblk * 4, 256);
+    p.rgroups = ceil_div(p.rblk, RS_GROUP);
+    p.off_gsum = off;    off = align_up(off + size_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups * 4, 256);
     p.total = off;
     return SPC_OK;
 }
@@ -722,6 +725,7 @@ struct Scratch {
     uint32_t* keys[2];
     int32_t* vals[2];
     int32_t* hist;
+    int32_t* gsum;               // [2 sorts][RS_MAX_PASSES][RS_BINS][groups], zeroed by k_clear
 };
 
 // Row pass: masks into keys (K <= 32, NULL ok) and per-block counts (NULL ok).
@@ -736,10 +740,11 @@ spc_status row_pass(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t
 }
 
 // Stable LSD radix sort of the rows of `map` by neighbour mask into `order`
-// (the identity for K > 32).  keys_ready: s.keys[0] already holds the masks.
+// (the identity for K > 32).  keys_ready: s.keys[0] already holds the masks;
+// slot (0 or 1) picks the group sums, so two sorts of one call do not share them.
 // rows_dev < 0 means M from the header; grids are sized for rows_cap rows.
 spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
-                     const Scratch& s, bool keys_ready, int32_t* order, hipStream_t stream) {
+                     const Scratch& s, bool keys_ready, int slot, int32_t* order, hipStream_t stream) {
     const int K = p.K;
     if (K > MASK_BITS) {
         hipLaunchKernelGGL(k_iota, dim3(grid_for(rows_cap, KB, 4096)), dim3(KB), 0, stream, order, rows_dev, cap,
@@ -753,15 +758,19 @@ spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_
         if (st != SPC_OK) return st;
     }
     const unsigned nb = unsigned(ceil_div(rows_cap, RS_TILE));
+    const int ng = int(ceil_div(nb, RS_GROUP));
     const int passes = (K + RS_BITS - 1) / RS_BITS;
     int cur = 0;
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = RS_BITS * pass;
-        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(KB), 0, stream, s.keys[cur], rows_dev, cap, s.hdr, shift, s.hist);
+        int32_t* gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
+        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, s.keys[cur], rows_dev, cap, s.hdr, shift,
+                           s.hist, gsum, ng);
         SPC_LAUNCHED("k_rs_hist");
         const bool last = pass + 1 == passes;
-        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(KB), 0, stream, s.keys[cur], pass == 0 ? nullptr : s.vals[cur],
-                           rows_dev, cap, s.hdr, shift, s.hist, s.keys[cur ^ 1], last ? order : s.vals[cur ^ 1]);
+        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, s.keys[cur],
+                           pass == 0 ? nullptr : s.vals[cur], rows_dev, cap, s.hdr, shift, s.hist, gsum, ng,
+                           s.keys[cur ^ 1], last ? order : s.vals[cur ^ 1]);
         SPC_LAUNCHED("k_rs_scatter");
         cur ^= 1;
     }
@@ -855,6 +864,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     s.vals[0] = reinterpret_cast<int32_t*>(base + p.off_vals);
     s.vals[1] = s.vals[0] + p.rows_max;
     s.hist = reinterpret_cast<int32_t*>(base + p.off_hist);
+    s.gsum = reinterpret_cast<int32_t*>(base + p.off_gsum);
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(base + p.off_prefix);
@@ -865,8 +875,9 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     const int32_t nblk = int32_t(ceil_div(n, KB));
     const int64_t entries = int64_t(n) * p.K;
 
-    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max(p.cap / 2, p.nwords / 4), KB, 4096)), dim3(KB), 0, stream,
-                       table, p.cap, bitmap, p.nwords, s.hdr);
+    const int64_t nzero = (order || order_in) ? int64_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups : 0;
+    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({p.cap / 2, p.nwords / 4, nzero / 4}), KB, 4096)), dim3(KB), 0,
+                       stream, table, p.cap, bitmap, p.nwords, s.hdr, s.gsum, nzero);
     SPC_LAUNCHED("k_clear");
     if (n > 0) {
         if (subm)
@@ -885,7 +896,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             if (st != SPC_OK) return st;
         }
         if (order) {
-            st = sort_rows(p, nbr, n, n, n, s, pairs, order, stream);
+            st = sort_rows(p, nbr, n, n, n, s, pairs, 0, order, stream);
             if (st != SPC_OK) return st;
         }
         *n_out = n_in;
@@ -921,11 +932,11 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             if (st != SPC_OK) return st;
         }
         if (order) {
-            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, pairs, order, stream);
+            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, pairs, 0, order, stream);
             if (st != SPC_OK) return st;
         }
         if (order_in) {
-            st = sort_rows(p, nbr_in, n, n, n, s, false, order_in, stream);
+            st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, stream);
             if (st != SPC_OK) return st;
         }
     }
