@@ -32,6 +32,8 @@ constexpr int NW = CT / WAVE;    // waves per workgroup
 constexpr int WAIT_VMCNT0 = 0x0F70;
 constexpr int KTILE = 28;        // offsets whose map rows are staged at once (a 3x3x3 kernel in one go)
 
+__device__ __attribute__((aligned(16))) const float kZero4[4] = {0.f, 0.f, 0.f, 0.f};
+
 struct ConvArgs {
     const void* x;       // gathered operand [n_src, CK]
     const void* w;       // weights [K, cin, cout]
@@ -192,11 +194,26 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BM]
     int32_t* flags = tile + KTILE * BM;                                // [KTILE]
     int32_t* list = flags + KTILE;                                     // [KTILE + 1]
+    int32_t* rsrc = list + KTILE + 1;                                  // [BM] output row of tile row r, or -1
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = blockIdx.x * BM, col0 = blockIdx.y * BN;
     const int KC = a.kch / 4;  // MFMA steps along CK
+
+    // map staging: thread t owns tile row t % BM and the run of KPT offsets
+    // starting at (t / BM) * KPT
+    static_assert(CT % BM == 0, "whole rows per staging thread group");
+    constexpr int KQ = CT / BM, KPT = (KTILE + KQ - 1) / KQ;
+    const int sr = threadIdx.x % BM, sq = threadIdx.x / BM;
+    int32_t ssrc;  // source row of tile row sr (the processing order applied), or -1
+    {
+        const int row = row0 + sr;
+        const int rc = row < a.n_rows ? row : a.n_rows - 1;
+        const int32_t s0 = a.order ? a.order[rc] : rc;
+        ssrc = row < a.n_rows && (unsigned)s0 < (unsigned)a.n_rows ? s0 : -1;
+        if (sq == 0) rsrc[sr] = ssrc;
+    }
 
     f32x4_t acc[RB][NB];
 #pragma unroll
@@ -212,16 +229,26 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
         __syncthreads();  // earlier readers of tile / list / slabs are done
         if (threadIdx.x < KTILE) flags[threadIdx.x] = 0;
         __syncthreads();
-        for (int idx = threadIdx.x; idx < kt * BM; idx += CT) {
-            const int k = idx / BM, r = idx - k * BM, row = row0 + r;
-            int32_t v = -1;
-            if (row < a.n_rows) {
-                const int32_t src = a.order ? a.order[row] : row;
-                if ((unsigned)src < (unsigned)a.n_rows) v = a.map ? a.map[int64_t(src) * a.K + kt0 + k] : src;
+        {
+            // all of this thread's map entries in flight at once: unguarded
+            // loads from one base (an invalid row reads row 0, entries past
+            // the chunk re-read its last one) whose results are then dropped
+            const int kb = sq * KPT, lim = kt - 1 - kb;  // lim < 0: no offset of this chunk here
+            const int l2 = lim >= 0 ? lim : 0;
+            const int32_t* p = a.map ? a.map + int64_t(ssrc < 0 ? 0 : ssrc) * a.K + kt0 + (lim >= 0 ? kb : 0)
+                                     : nullptr;
+            int32_t v[KPT];
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) v[u] = p ? p[u <= l2 ? u : l2] : ssrc;
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) {
+                if (u <= lim) {
+                    int32_t val = ssrc >= 0 ? v[u] : -1;
+                    if ((unsigned)val >= (unsigned)a.n_src) val = -1;
+                    tile[(kb + u) * BM + sr] = val;
+                    if (val >= 0) flags[kb + u] = 1;
+                }
             }
-            if ((unsigned)v >= (unsigned)a.n_src) v = -1;
-            tile[idx] = v;
-            if (v >= 0) flags[k] = 1;
         }
         __syncthreads();
         if (wave == 0) {  // compact list of the offsets that hit this tile
@@ -275,25 +302,23 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     }
 
     // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
-    // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels
+    // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels.  The
+    // bias is loaded before the first store (on CDNA the vector memory counter
+    // also counts stores, so a load issued after them would wait for them).
     S* y = static_cast<S*>(a.y);
+    const float* bp = a.bias ? a.bias + col0 + lg * 4 : kZero4;  // no bias: every channel reads zeros
+    const int bstep = a.bias ? 16 : 0;
+    f32x4_t bv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(bp + nb * bstep);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        int row = row0 + (wave * RB + rb) * 16 + lr;
-        if (row >= a.n_rows) continue;
-        if (a.order) {
-            row = a.order[row];
-            if ((unsigned)row >= (unsigned)a.n_rows) continue;
-        }
+        const int row = rsrc[(wave * RB + rb) * 16 + lr];
+        if (row < 0) continue;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int ch = col0 + nb * 16 + lg * 4;
-            f32x4_t v = acc[rb][nb];
-            if (a.bias) {
-                const f32x4_t b = *reinterpret_cast<const f32x4_t*>(a.bias + ch);
-                v += b;
-            }
-            store4<TT>(y + int64_t(row) * a.CN + ch, v);
+            store4<TT>(y + int64_t(row) * a.CN + ch, acc[rb][nb] + bv[nb]);
         }
     }
 }
@@ -305,7 +330,7 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB_DEFAULT * 16;
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
-    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 1) * 4;
+    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 1) * 4 + BM * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
