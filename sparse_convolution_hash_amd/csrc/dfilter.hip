@@ -4,14 +4,15 @@
 //   dbias = sum over rows o of dy[o]                                 [cout]
 //
 // (the Hygon spconv-das README's dfilter, "Public Interface Support").  The
-// contraction runs over pairs.  The CSR pair lists are cut into chunks of
-// equal length (never straddling two offsets) and a persistent grid walks
-// them, so offsets with many pairs do not serialise the pass.  A chunk
-// gathers 64 pairs at a time, transposes them in registers into
-// channel-major LDS tiles (the MFMA fragments need 16 bytes of consecutive
-// pairs per channel) and accumulates fp32 on MFMA; it writes one partial
-// tile, and a second kernel sums each offset's partials in chunk order, so
-// the result does not depend on scheduling.
+// contraction runs over pairs.  The CSR pair list is cut into one segment of
+// equal length per workgroup; a workgroup walks its segment in steps of up
+// to 64 pairs (a step never straddles two offsets), gathers each step's rows
+// and transposes them in registers into channel-major LDS tiles (the MFMA
+// fragments need 16 bytes of consecutive pairs per channel), accumulates
+// fp32 on MFMA, and writes one partial tile per offset it touches.  Pair
+// indices are fetched two steps ahead and rows one step ahead.  A second
+// kernel sums each offset's partials in segment order, so the result does
+// not depend on scheduling.
 #include <algorithm>
 
 #include "common.h"
@@ -22,9 +23,7 @@ namespace {
 constexpr int DT = 256;          // threads per workgroup (2 x 2 waves)
 constexpr int PS = 64;           // pairs staged per step
 constexpr int TMAX = 128;        // channel tile edge
-constexpr int TARGET_CHUNKS = 1024;   // pair chunks the chunk length aims for
-constexpr int MIN_CHUNK = 1024;       // pairs per chunk at least
-constexpr int MAX_WG = 512;           // persistent workgroups (per channel tile)
+constexpr int MAX_WG = 512;           // segments (workgroups) over all channel tiles
 
 struct DfArgs {
     const void* x;        // [n_in, cin]
@@ -32,26 +31,35 @@ struct DfArgs {
     const int32_t* ptr;   // [K+1] or NULL (identity pairs, K == 1)
     const int32_t* pin;
     const int32_t* pout;
-    float* part;          // [max chunks, cin, cout]
+    float* part;          // [nseg + K, cin, cout] partial tiles
     int32_t n_in, n_out, cin, cout, K;
+    int32_t nseg;         // segments of the pair list (workgroups per channel tile)
 };
 
-// Pair range of offset k and the common chunk length.  Every workgroup and
-// the reduction derive the same chunking from pair_ptr: chunks of CH pairs
-// (a multiple of PS, at least MIN_CHUNK, about P / TARGET_CHUNKS), never
-// straddling two offsets, numbered offset by offset.
-struct Chunks {
-    int64_t ch;
-    __device__ Chunks(const DfArgs& a) {
-        const int64_t P = a.ptr ? a.ptr[a.K] : a.n_in;
-        int64_t c = (P + TARGET_CHUNKS - 1) / TARGET_CHUNKS;
-        c = c < MIN_CHUNK ? MIN_CHUNK : c;
-        ch = (c + PS - 1) / PS * PS;
-    }
-    __device__ static int64_t beg(const DfArgs& a, int k) { return a.ptr ? a.ptr[k] : 0; }
-    __device__ static int64_t end(const DfArgs& a, int k) { return a.ptr ? a.ptr[k + 1] : a.n_in; }
-    __device__ int64_t count(const DfArgs& a, int k) const { return (end(a, k) - beg(a, k) + ch - 1) / ch; }
+// Pair ranges.  Segment b is [b*seg, (b+1)*seg) of the pair list, with seg a
+// multiple of PS and about P / nseg; the same numbers are derived from
+// pair_ptr by every workgroup and by the reduction.
+__device__ __forceinline__ int64_t pairs_total(const DfArgs& a) { return a.ptr ? a.ptr[a.K] : a.n_in; }
+__device__ __forceinline__ int64_t off_beg(const DfArgs& a, int k) { return a.ptr ? a.ptr[k] : 0; }
+__device__ __forceinline__ int64_t off_end(const DfArgs& a, int k) { return a.ptr ? a.ptr[k + 1] : a.n_in; }
+__device__ __forceinline__ int64_t seg_len(const DfArgs& a, int64_t P) {
+    const int64_t s = (P + a.nseg - 1) / a.nseg;
+    return s < PS ? PS : (s + PS - 1) / PS * PS;
+}
+
+// One step: pairs [b, e) of offset k (e > b), or none (k < 0).
+struct Step {
+    int64_t b, e;
+    int k;
 };
+
+// The step starting at pair p of segment end s1, from offset k on.
+__device__ __forceinline__ Step step_at(const DfArgs& a, int64_t p, int k, int64_t s1) {
+    if (p >= s1) return Step{0, 0, -1};
+    while (off_end(a, k) <= p) ++k;  // p < s1 <= P: ends inside the offsets
+    const int64_t e0 = off_end(a, k), e1 = p + PS;
+    return Step{p, min(min(e0, e1), s1), k};
+}
 
 // Row stride (bytes) of a channel-major LDS tile: PS pairs plus 16 bytes of
 // padding so that consecutive channels fall in different banks.
@@ -64,32 +72,47 @@ struct Item {
     u32x4 in[TT::E];
 };
 
+// Item geometry: item j of a step is E consecutive pairs (group pg) x E
+// consecutive channels (block ch) of x (j < xi_items) or of dy.
+struct ItemGeo {
+    bool is_x;
+    int pg, ch;
+    __device__ ItemGeo(int item, int xi_items, int E) {
+        is_x = item < xi_items;
+        const int j = is_x ? item : item - xi_items;
+        pg = j % (PS / E);
+        ch = j / (PS / E);
+    }
+};
+
+// Pair indices (rows of x or dy) of an item's pairs in step st: unguarded
+// loads from clamped, valid positions of the step.
 template <typename TT>
-__device__ __forceinline__ void load_item(Item<TT>& it, const DfArgs& a, int item, int xi_items, int TI, int TO,
-                                          int ci0, int co0, int64_t p0, int64_t p_end) {
-    using S = typename TT::storage;
+__device__ __forceinline__ void load_idx(int32_t (&r)[TT::E], const DfArgs& a, const ItemGeo& g, const Step& st) {
     constexpr int E = TT::E;
-    constexpr int PG = PS / E;
-    const bool is_x = item < xi_items;
-    const int j = is_x ? item : item - xi_items;
-    const int pg = j % PG, ch = j / PG;
-    const S* src = is_x ? static_cast<const S*>(a.x) : static_cast<const S*>(a.dy);
-    const int C = is_x ? a.cin : a.cout;
-    const int c0 = (is_x ? ci0 : co0) + ch * E;
-    const int32_t* idx = is_x ? a.pin : a.pout;
-    const int32_t lim = is_x ? a.n_in : a.n_out;
-    // all pair indices first, then all rows: unconditional (clamped) loads so
-    // that the whole batch is in flight at once; invalid slots become zero
-    int32_t r[E];
+    const int32_t* idx = g.is_x ? a.pin : a.pout;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int64_t p = p0 + pg * E + e;
-        const int64_t pc = p < p_end ? p : p_end - 1;
+        const int64_t p = st.b + g.pg * E + e;
+        const int64_t pc = p < st.e ? p : st.e - 1;
         r[e] = a.ptr ? idx[pc] : int32_t(pc);
     }
+}
+
+// The item's rows for step st, from indices r: unguarded loads (an invalid
+// slot reads row 0 and is then zeroed).
+template <typename TT>
+__device__ __forceinline__ void load_rows(Item<TT>& it, const int32_t (&r)[TT::E], const DfArgs& a, const ItemGeo& g,
+                                          int ci0, int co0, const Step& st) {
+    using S = typename TT::storage;
+    constexpr int E = TT::E;
+    const S* src = g.is_x ? static_cast<const S*>(a.x) : static_cast<const S*>(a.dy);
+    const int C = g.is_x ? a.cin : a.cout;
+    const int c0 = (g.is_x ? ci0 : co0) + g.ch * E;
+    const int32_t lim = g.is_x ? a.n_in : a.n_out;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const bool ok = p0 + pg * E + e < p_end && (unsigned)r[e] < (unsigned)lim;
+        const bool ok = st.b + g.pg * E + e < st.e && (unsigned)r[e] < (unsigned)lim;
         it.in[e] = ld16(src + int64_t(ok ? r[e] : 0) * C + c0);
         if (!ok) it.in[e] = zero4();
     }
@@ -126,9 +149,9 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
     }
 }
 
-// Persistent workgroups walk the pair chunks (chunk j = blockIdx.x + t *
-// gridDim.x); each chunk's partial dW tile goes to part[j].  The next step's
-// first staging item is prefetched into registers during the MFMAs.
+// Workgroup b walks segment b of the pair list in steps; each offset it
+// touches gets one partial tile, part[b + k] (b + k is distinct for every
+// (segment, offset) pair a walk can meet, as both only grow along it).
 template <typename TT>
 __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     constexpr int E = TT::E;
@@ -146,104 +169,120 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     constexpr int PG = PS / E;
     const int xi_items = PG * (TI / E), items = xi_items + PG * (TO / E);
 
-    const Chunks chunks(a);
-    int64_t total = 0;
-    for (int k = 0; k < a.K; ++k) total += chunks.count(a, k);
+    const int64_t P = pairs_total(a), seg = seg_len(a, P);
+    const int64_t s0 = int64_t(blockIdx.x) * seg, s1 = min(P, s0 + seg);
+    if (s0 >= s1 || a.n_in == 0 || a.n_out == 0) return;  // (no rows: no valid pair either)
 
-    for (int64_t j = blockIdx.x; j < total; j += gridDim.x) {
-        // locate chunk j: offset k, pair range [c_beg, c_end)
-        int k = 0;
-        int64_t first = 0;
-        for (;; ++k) {
-            const int64_t c = chunks.count(a, k);
-            if (j < first + c) break;
-            first += c;
+    // this thread's pipelined item (threads beyond the items load a copy of
+    // the last one and do not store it)
+    const int my = threadIdx.x;
+    const bool has_item = my < items;
+    const ItemGeo geo(has_item ? my : items - 1, xi_items, E);
+
+    Step cur = step_at(a, s0, 0, s1);
+    Step nxt = step_at(a, cur.e, cur.k, s1);
+    Item<TT> pre;
+    int32_t rn[E];  // indices of step nxt
+    {
+        int32_t r0[E];
+        load_idx<TT>(r0, a, geo, cur);
+        load_rows<TT>(pre, r0, a, geo, ci0, co0, cur);
+        if (nxt.k >= 0) load_idx<TT>(rn, a, geo, nxt);
+    }
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    while (cur.k >= 0) {
+        const Step nx2 = nxt.k >= 0 ? step_at(a, nxt.e, nxt.k, s1) : Step{0, 0, -1};
+        __syncthreads();  // the previous step's tiles are consumed
+        if (has_item) store_item<TT>(xt, gt, pre, my, xi_items);
+        for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32): not pipelined
+            const ItemGeo g2(it, xi_items, E);
+            int32_t r2[E];
+            Item<TT> tmp;
+            load_idx<TT>(r2, a, g2, cur);
+            load_rows<TT>(tmp, r2, a, g2, ci0, co0, cur);
+            store_item<TT>(xt, gt, tmp, it, xi_items);
         }
-        const int64_t c_beg = Chunks::beg(a, k) + (j - first) * chunks.ch;
-        const int64_t c_end = min(Chunks::end(a, k), c_beg + chunks.ch);
-
-        f32x4_t acc[4][4];
+        __syncthreads();
+        if (nxt.k >= 0) {
+            load_rows<TT>(pre, rn, a, geo, ci0, co0, nxt);
+            if (nx2.k >= 0) load_idx<TT>(rn, a, geo, nx2);
+        }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int ks = 0; ks < PS / (4 * E); ++ks) {
+            const int poff = (ks * 4 + lg) * 16;
+            u32x4 gf[4], xf[4];
 #pragma unroll
-            for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        Item<TT> pre;
-        const int my = threadIdx.x;  // first item of this thread
-        if (my < items) load_item<TT>(pre, a, my, xi_items, TI, TO, ci0, co0, c_beg, c_end);
-        for (int64_t p0 = c_beg; p0 < c_end; p0 += PS) {
-            __syncthreads();  // the previous step's tiles are consumed
-            if (my < items) store_item<TT>(xt, gt, pre, my, xi_items);
-            for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32)
-                Item<TT> tmp;
-                load_item<TT>(tmp, a, it, xi_items, TI, TO, ci0, co0, p0, c_end);
-                store_item<TT>(xt, gt, tmp, it, xi_items);
-            }
-            __syncthreads();
-            if (my < items && p0 + PS < c_end) load_item<TT>(pre, a, my, xi_items, TI, TO, ci0, co0, p0 + PS, c_end);
+            for (int no = 0; no < 4; ++no)
+                if (no < NO && (wo * NO + no) * 16 < TO)
+                    gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
 #pragma unroll
-            for (int ks = 0; ks < PS / (4 * E); ++ks) {
-                const int poff = (ks * 4 + lg) * 16;
-                u32x4 gf[4], xf[4];
+            for (int mi = 0; mi < 4; ++mi)
+                if (mi < MI && (wi * MI + mi) * 16 < TI)
+                    xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int no = 0; no < 4; ++no)
-                    if (no < NO && (wo * NO + no) * 16 < TO)
-                        gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    if (mi < MI && (wi * MI + mi) * 16 < TI)
-                        xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int no = 0; no < 4; ++no)
-                        if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
-                            acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
-            }
+                    if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
+                        acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
         }
-
-        // D[co][ci] per 16x16 tile: this lane holds co = lg*4 .. +3 of ci = lr
-        float* part = a.part + j * a.cin * a.cout;
+        if (nxt.k != cur.k) {
+            // last step of offset cur.k in this segment: D[co][ci] per 16x16
+            // tile, this lane holds co = lg*4 .. +3 of ci = lr
+            float* part = a.part + (int64_t(blockIdx.x) + cur.k) * a.cin * a.cout;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int no = 0; no < 4; ++no) {
-                if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
-                const int ci = ci0 + (wi * MI + mi) * 16 + lr;
-                const int co = co0 + (wo * NO + no) * 16 + lg * 4;
-                *reinterpret_cast<f32x4_t*>(part + int64_t(ci) * a.cout + co) = acc[mi][no];
-            }
+                for (int no = 0; no < 4; ++no) {
+                    if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
+                    const int ci = ci0 + (wi * MI + mi) * 16 + lr;
+                    const int co = co0 + (wo * NO + no) * 16 + lg * 4;
+                    *reinterpret_cast<f32x4_t*>(part + int64_t(ci) * a.cout + co) = acc[mi][no];
+                    acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        cur = nxt;
+        nxt = nx2;
     }
 }
 
-// dw[k] = sum of the partials of offset k's chunks, in chunk order (zero if
-// the offset has no pairs).  Four floats per thread.
-__global__ __launch_bounds__(256) void k_reduce_chunks(DfArgs a, float* __restrict__ dw) {
+// dw[k] = sum of offset k's partials, in segment order (zero if the offset
+// has no pairs).  A block takes 256 floats of one offset; its four thread
+// groups sum every fourth segment, and the groups are combined in order.
+__global__ __launch_bounds__(256) void k_reduce_segs(DfArgs a, float* __restrict__ dw) {
+    __shared__ f32x4_t red[4][64];
     const int k = blockIdx.y;
-    const int64_t L = int64_t(a.cin) * a.cout;
-    const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (t >= L) return;
-    const Chunks chunks(a);
-    int64_t first = 0;
-    for (int kk = 0; kk < k; ++kk) first += chunks.count(a, kk);
-    const int64_t cnt = chunks.count(a, k);
-    // in chunk order; loads are issued in batches so that they overlap
-    constexpr int QB = 8;
+    const int64_t L = int64_t(a.cin) * a.cout;  // a multiple of 256
+    const int q = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int64_t e0 = int64_t(blockIdx.x) * 256 + q * 4;
+    const int64_t P = pairs_total(a), seg = seg_len(a, P);
+    const int64_t beg = off_beg(a, k), end = off_end(a, k);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t j0 = first; j0 < first + cnt; j0 += QB) {
-        f32x4_t v[QB];
+    if (end > beg && a.n_in > 0 && a.n_out > 0) {
+        const int64_t bf = beg / seg, bl = (end - 1) / seg;
+        constexpr int QB = 8;
+        for (int64_t b0 = bf + g; b0 <= bl; b0 += 4 * QB) {
+            f32x4_t v[QB];
 #pragma unroll
-        for (int u = 0; u < QB; ++u) {
-            const int64_t j = j0 + u < first + cnt ? j0 + u : first + cnt - 1;
-            v[u] = *reinterpret_cast<const f32x4_t*>(a.part + j * L + t);
+            for (int u = 0; u < QB; ++u) {
+                const int64_t b = b0 + 4 * u <= bl ? b0 + 4 * u : bl;
+                v[u] = *reinterpret_cast<const f32x4_t*>(a.part + (b + k) * L + e0);
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+                if (b0 + 4 * u <= bl) acc += v[u];
         }
-#pragma unroll
-        for (int u = 0; u < QB; ++u)
-            if (j0 + u < first + cnt) acc += v[u];
     }
-    *reinterpret_cast<f32x4_t*>(dw + int64_t(k) * L + t) = acc;
+    red[g][q] = acc;
+    __syncthreads();
+    if (g == 0) *reinterpret_cast<f32x4_t*>(dw + int64_t(k) * L + e0) = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
 }
-
 
 constexpr int COLSUM_BLOCKS = 256;  // dbias partials (one per block, fixed row ranges)
 
@@ -337,10 +376,10 @@ struct DfLayout {
     size_t off_dbias, total;
 };
 
-// Chunks never exceed P / CH + K <= TARGET_CHUNKS + K (CH >= P / TARGET_CHUNKS).
+// Partial slots: b + k over segments b < nseg <= MAX_WG and offsets k < K.
 DfLayout df_layout(int64_t n_in, int64_t n_out, int32_t cin, int32_t cout, int32_t K, bool dbias) {
     DfLayout l;
-    l.max_chunks = TARGET_CHUNKS + K;
+    l.max_chunks = MAX_WG + K;
     l.rparts = dbias ? COLSUM_BLOCKS : 0;
     l.off_dbias = align_up(size_t(l.max_chunks) * cin * cout * 4, 256);
     l.total = align_up(l.off_dbias + size_t(l.rparts) * cout * 4, 256);
@@ -351,13 +390,13 @@ template <typename TT>
 spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_part, int64_t rparts,
                           hipStream_t stream) {
     const unsigned tiles = unsigned(ceil_div(a.cin, TMAX) * ceil_div(a.cout, TMAX));
-    const unsigned wgs = unsigned(std::max<int64_t>(64, MAX_WG / tiles));
-    hipLaunchKernelGGL(k_dfilter<TT>, dim3(wgs, tiles), dim3(DT), 0, stream, a);
+    DfArgs b = a;
+    b.nseg = int32_t(std::max<int64_t>(64, MAX_WG / tiles));
+    hipLaunchKernelGGL(k_dfilter<TT>, dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
     SPC_LAUNCHED("k_dfilter");
     const int64_t L = int64_t(a.cin) * a.cout;
-    hipLaunchKernelGGL(k_reduce_chunks, dim3(unsigned(ceil_div(L / 4, 256)), unsigned(a.K)), dim3(256), 0, stream, a,
-                       dw);
-    SPC_LAUNCHED("k_reduce_chunks");
+    hipLaunchKernelGGL(k_reduce_segs, dim3(unsigned(L / 256), unsigned(a.K)), dim3(256), 0, stream, b, dw);
+    SPC_LAUNCHED("k_reduce_segs");
     if (dbias) {
         hipLaunchKernelGGL(k_colsum<TT>, dim3(unsigned(rparts)), dim3(256), 0, stream,
                            static_cast<const typename TT::storage*>(a.dy), a.n_out, a.cout, bias_part);
@@ -407,7 +446,7 @@ extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, in
     if (!ws) return fail(SPC_ERR_ARG, "workspace is NULL");
     if (ws_bytes < l.total) return fail(SPC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
     DfArgs a{feats, dout, pair_ptr, pair_in, pair_out, static_cast<float*>(ws), int32_t(n_in), int32_t(n_out),
-             cin, cout, K};
+             cin, cout, K, 0};
     float* bias_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.off_dbias);
     switch (dtype) {
         case SPC_F32: return launch_dfilter<F32>(a, dw, dbias, bias_part, l.rparts, stream);
