@@ -24,6 +24,7 @@ constexpr int DT = 256;          // threads per workgroup (2 x 2 waves)
 constexpr int PS = 64;           // pairs staged per step
 constexpr int TMAX = 128;        // channel tile edge
 constexpr int MAX_WG = 512;           // segments (workgroups) over all channel tiles
+constexpr int MAX_K = 343;            // offsets (pair_ptr is staged in LDS)
 
 struct DfArgs {
     const void* x;        // [n_in, cin]
@@ -42,6 +43,13 @@ struct DfArgs {
 __device__ __forceinline__ int64_t pairs_total(const DfArgs& a) { return a.ptr ? a.ptr[a.K] : a.n_in; }
 __device__ __forceinline__ int64_t off_beg(const DfArgs& a, int k) { return a.ptr ? a.ptr[k] : 0; }
 __device__ __forceinline__ int64_t off_end(const DfArgs& a, int k) { return a.ptr ? a.ptr[k + 1] : a.n_in; }
+
+// pair_ptr (or the identity's [0, n_in]) in LDS: the step walk reads it
+// there, so it never waits on the vector memory counter of the prefetches.
+__device__ __forceinline__ void stage_ptr(int32_t* sptr, const DfArgs& a) {
+    for (int k = threadIdx.x; k <= a.K; k += blockDim.x) sptr[k] = a.ptr ? a.ptr[k] : (k == 0 ? 0 : a.n_in);
+    __syncthreads();
+}
 __device__ __forceinline__ int64_t seg_len(const DfArgs& a, int64_t P) {
     const int64_t s = (P + a.nseg - 1) / a.nseg;
     return s < PS ? PS : (s + PS - 1) / PS * PS;
@@ -53,11 +61,12 @@ struct Step {
     int k;
 };
 
-// The step starting at pair p of segment end s1, from offset k on.
-__device__ __forceinline__ Step step_at(const DfArgs& a, int64_t p, int k, int64_t s1) {
+// The step starting at pair p of segment end s1, from offset k on (sptr:
+// pair_ptr staged in LDS).
+__device__ __forceinline__ Step step_at(const int32_t* sptr, int64_t p, int k, int64_t s1) {
     if (p >= s1) return Step{0, 0, -1};
-    while (off_end(a, k) <= p) ++k;  // p < s1 <= P: ends inside the offsets
-    const int64_t e0 = off_end(a, k), e1 = p + PS;
+    while (sptr[k + 1] <= p) ++k;  // p < s1 <= P: ends inside the offsets
+    const int64_t e0 = sptr[k + 1], e1 = p + PS;
     return Step{p, min(min(e0, e1), s1), k};
 }
 
@@ -70,6 +79,7 @@ constexpr int lds_row() { return PS * int(sizeof(typename TT::storage)) + 16; }
 template <typename TT>
 struct Item {
     u32x4 in[TT::E];
+    uint32_t ok;  // bit e: slot e holds a real row (else it is zeroed when stored)
 };
 
 // Item geometry: item j of a step is E consecutive pairs (group pg) x E
@@ -87,7 +97,7 @@ struct ItemGeo {
 
 // Pair indices (rows of x or dy) of an item's pairs in step st: unguarded
 // loads from clamped, valid positions of the step.
-template <typename TT>
+template <typename TT, bool IDENT>
 __device__ __forceinline__ void load_idx(int32_t (&r)[TT::E], const DfArgs& a, const ItemGeo& g, const Step& st) {
     constexpr int E = TT::E;
     const int32_t* idx = g.is_x ? a.pin : a.pout;
@@ -95,12 +105,16 @@ __device__ __forceinline__ void load_idx(int32_t (&r)[TT::E], const DfArgs& a, c
     for (int e = 0; e < E; ++e) {
         const int64_t p = st.b + g.pg * E + e;
         const int64_t pc = p < st.e ? p : st.e - 1;
-        r[e] = a.ptr ? idx[pc] : int32_t(pc);
+        if constexpr (IDENT)
+            r[e] = int32_t(pc);
+        else
+            r[e] = idx[pc];
     }
 }
 
 // The item's rows for step st, from indices r: unguarded loads (an invalid
-// slot reads row 0 and is then zeroed).
+// slot reads row 0 and is zeroed when stored, not here: a select right after
+// the loads would wait for them).
 template <typename TT>
 __device__ __forceinline__ void load_rows(Item<TT>& it, const int32_t (&r)[TT::E], const DfArgs& a, const ItemGeo& g,
                                           int ci0, int co0, const Step& st) {
@@ -110,11 +124,12 @@ __device__ __forceinline__ void load_rows(Item<TT>& it, const int32_t (&r)[TT::E
     const int C = g.is_x ? a.cin : a.cout;
     const int c0 = (g.is_x ? ci0 : co0) + g.ch * E;
     const int32_t lim = g.is_x ? a.n_in : a.n_out;
+    it.ok = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const bool ok = st.b + g.pg * E + e < st.e && (unsigned)r[e] < (unsigned)lim;
         it.in[e] = ld16(src + int64_t(ok ? r[e] : 0) * C + c0);
-        if (!ok) it.in[e] = zero4();
+        it.ok |= uint32_t(ok) << e;
     }
 }
 
@@ -128,18 +143,20 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
     const int j = is_x ? item : item - xi_items;
     const int pg = j % PG, ch = j / PG;
     char* dst = (is_x ? xt : gt) + (ch * E) * lds_row<TT>() + pg * 16;
+    u32x4 in[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) in[e] = (it.ok >> e) & 1u ? it.in[e] : zero4();
     if constexpr (E == 8) {
         typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
         u16x8 v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(u16x8, it.in[e]);
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(u16x8, in[e]);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             u16x8 o = {v[0][c], v[1][c], v[2][c], v[3][c], v[4][c], v[5][c], v[6][c], v[7][c]};
             st16(dst + c * lds_row<TT>(), __builtin_bit_cast(u32x4, o));
         }
     } else {
-        const u32x4* in = it.in;
         const uint32_t m[4][4] = {{in[0].x, in[0].y, in[0].z, in[0].w},
                                   {in[1].x, in[1].y, in[1].z, in[1].w},
                                   {in[2].x, in[2].y, in[2].z, in[2].w},
@@ -152,12 +169,14 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
 // Workgroup b walks segment b of the pair list in steps; each offset it
 // touches gets one partial tile, part[b + k] (b + k is distinct for every
 // (segment, offset) pair a walk can meet, as both only grow along it).
-template <typename TT>
+// IDENT: K == 1 with the identity pairs (i, i), no pair lists.
+template <typename TT, bool IDENT>
 __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     constexpr int E = TT::E;
     constexpr int ROW = lds_row<TT>();
     __shared__ __attribute__((aligned(16))) char xt[TMAX * ROW];  // [ci][pairs]
     __shared__ __attribute__((aligned(16))) char gt[TMAX * ROW];  // [co][pairs]
+    __shared__ int32_t sptr[MAX_K + 1];
 
     const int tiles_o = (a.cout + TMAX - 1) / TMAX;
     const int ci0 = (blockIdx.y / tiles_o) * TMAX, co0 = (blockIdx.y % tiles_o) * TMAX;
@@ -172,6 +191,7 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     const int64_t P = pairs_total(a), seg = seg_len(a, P);
     const int64_t s0 = int64_t(blockIdx.x) * seg, s1 = min(P, s0 + seg);
     if (s0 >= s1 || a.n_in == 0 || a.n_out == 0) return;  // (no rows: no valid pair either)
+    stage_ptr(sptr, a);
 
     // this thread's pipelined item (threads beyond the items load a copy of
     // the last one and do not store it)
@@ -179,15 +199,18 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     const bool has_item = my < items;
     const ItemGeo geo(has_item ? my : items - 1, xi_items, E);
 
-    Step cur = step_at(a, s0, 0, s1);
-    Step nxt = step_at(a, cur.e, cur.k, s1);
+    // rows one step ahead, pair indices two steps ahead (two index buffers
+    // swap roles every step, by unrolling, as a register copy would wait
+    // for its pending load)
+    Step cur = step_at(sptr, s0, 0, s1);
+    Step nxt = step_at(sptr, cur.e, cur.k, s1);
     Item<TT> pre;
-    int32_t rn[E];  // indices of step nxt
+    int32_t ia[E], ib[E];  // indices of step nxt (ia before an even step, ib before an odd one)
     {
         int32_t r0[E];
-        load_idx<TT>(r0, a, geo, cur);
+        load_idx<TT, IDENT>(r0, a, geo, cur);
+        if (nxt.k >= 0) load_idx<TT, IDENT>(ia, a, geo, nxt);
         load_rows<TT>(pre, r0, a, geo, ci0, co0, cur);
-        if (nxt.k >= 0) load_idx<TT>(rn, a, geo, nxt);
     }
 
     f32x4_t acc[4][4];
@@ -196,22 +219,24 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
 #pragma unroll
         for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    while (cur.k >= 0) {
-        const Step nx2 = nxt.k >= 0 ? step_at(a, nxt.e, nxt.k, s1) : Step{0, 0, -1};
+    // one step: cur's rows are in `pre`, which is then refilled with nxt's
+    // rows from indices `use`; the indices of the step after go to `fill`
+    auto step = [&](const int32_t (&use)[E], int32_t (&fill)[E]) {
+        const Step nx2 = nxt.k >= 0 ? step_at(sptr, nxt.e, nxt.k, s1) : Step{0, 0, -1};
         __syncthreads();  // the previous step's tiles are consumed
         if (has_item) store_item<TT>(xt, gt, pre, my, xi_items);
         for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32): not pipelined
             const ItemGeo g2(it, xi_items, E);
             int32_t r2[E];
             Item<TT> tmp;
-            load_idx<TT>(r2, a, g2, cur);
+            load_idx<TT, IDENT>(r2, a, g2, cur);
             load_rows<TT>(tmp, r2, a, g2, ci0, co0, cur);
             store_item<TT>(xt, gt, tmp, it, xi_items);
         }
         __syncthreads();
         if (nxt.k >= 0) {
-            load_rows<TT>(pre, rn, a, geo, ci0, co0, nxt);
-            if (nx2.k >= 0) load_idx<TT>(rn, a, geo, nx2);
+            load_rows<TT>(pre, use, a, geo, ci0, co0, nxt);
+            if (nx2.k >= 0) load_idx<TT, IDENT>(fill, a, geo, nx2);
         }
 #pragma unroll
         for (int ks = 0; ks < PS / (4 * E); ++ks) {
@@ -249,6 +274,11 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
         }
         cur = nxt;
         nxt = nx2;
+    };
+    while (cur.k >= 0) {
+        step(ia, ib);
+        if (cur.k < 0) break;
+        step(ib, ia);
     }
 }
 
@@ -392,7 +422,10 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
     const unsigned tiles = unsigned(ceil_div(a.cin, TMAX) * ceil_div(a.cout, TMAX));
     DfArgs b = a;
     b.nseg = int32_t(std::max<int64_t>(64, MAX_WG / tiles));
-    hipLaunchKernelGGL(k_dfilter<TT>, dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
+    if (a.ptr)
+        hipLaunchKernelGGL((k_dfilter<TT, false>), dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
+    else
+        hipLaunchKernelGGL((k_dfilter<TT, true>), dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
     SPC_LAUNCHED("k_dfilter");
     const int64_t L = int64_t(a.cin) * a.cout;
     hipLaunchKernelGGL(k_reduce_segs, dim3(unsigned(L / 256), unsigned(a.K)), dim3(256), 0, stream, b, dw);
