@@ -198,7 +198,10 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
-    const int row0 = blockIdx.x * BM, col0 = blockIdx.y * BN;
+    // tiles run last-first: in a processing order sorted by neighbour mask
+    // the tiles with the most offsets come last, and starting them first
+    // keeps them off the end of the launch
+    const int row0 = (gridDim.x - 1 - blockIdx.x) * BM, col0 = blockIdx.y * BN;
     const int KC = a.kch / 4;  // MFMA steps along CK
 
     // map staging: thread t owns tile row t % BM and the run of KPT offsets
