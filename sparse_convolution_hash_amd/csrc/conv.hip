@@ -245,11 +245,12 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             for (int u = 0; u < KPT; ++u) v[u] = p ? p[u <= l2 ? u : l2] : ssrc;
 #pragma unroll
             for (int u = 0; u < KPT; ++u) {
-                if (u <= lim) {
+                if (u <= lim) {  // uniform over the wave (a wave's threads share sq)
                     int32_t val = ssrc >= 0 ? v[u] : -1;
                     if ((unsigned)val >= (unsigned)a.n_src) val = -1;
                     tile[(kb + u) * BM + sr] = val;
-                    if (val >= 0) flags[kb + u] = 1;
+                    // one flag write per wave: lanes writing one LDS word serialise
+                    if (__any(val >= 0) && lane == 0) flags[kb + u] = 1;
                 }
             }
         }
