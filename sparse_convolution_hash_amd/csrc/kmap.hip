@@ -68,6 +68,11 @@ __device__ __forceinline__ uint32_t mix32(uint32_t k) {
     return k;
 }
 
+// Home slot of a key: the four keys of one block of x (key >> 2) hash together
+// and take four adjacent slots (32 bytes, inside one cache line), so the
+// probes of neighbours along x, made by consecutive threads, share lines.
+__device__ __forceinline__ uint32_t home_slot(uint32_t key) { return (mix32(key >> 2) << 2) | (key & 3u); }
+
 __device__ __forceinline__ bool in_grid(const int4 c, const KGeom& g) {
     return (unsigned)c.x < (unsigned)g.batch && (unsigned)c.y < (unsigned)g.Z &&
            (unsigned)c.z < (unsigned)g.Y && (unsigned)c.w < (unsigned)g.X;
@@ -84,7 +89,7 @@ __device__ __forceinline__ uint32_t out_key(int b, int z, int y, int x, const KG
 __device__ __forceinline__ void table_insert(uint64_t* table, uint32_t mask, uint32_t key,
                                              uint32_t row, uint32_t* flags) {
     const unsigned long long slot = (static_cast<unsigned long long>(key) << 32) | row;
-    uint32_t h = mix32(key) & mask;
+    uint32_t h = home_slot(key) & mask;
     // at most N of the >= 4N slots are ever taken, so an empty slot is always found
     for (uint32_t step = 0; step <= mask; ++step) {
         unsigned long long prev =
@@ -100,7 +105,7 @@ __device__ __forceinline__ void table_insert(uint64_t* table, uint32_t mask, uin
 
 __device__ __forceinline__ int32_t table_find(const uint64_t* __restrict__ table, uint32_t mask,
                                               uint32_t key) {
-    uint32_t h = mix32(key) & mask;
+    uint32_t h = home_slot(key) & mask;
     for (uint32_t step = 0; step <= mask; ++step) {
         const uint64_t v = table[h];
         if (v == EMPTY_SLOT) return -1;
