@@ -32,7 +32,6 @@ constexpr int NW = CT / WAVE;    // waves per workgroup
 constexpr int WAIT_VMCNT0 = 0x0F70;
 constexpr int KTILE = 28;        // offsets whose map rows are staged at once (a 3x3x3 kernel in one go)
 
-__device__ __attribute__((aligned(16))) const float kZero4[4] = {0.f, 0.f, 0.f, 0.f};
 
 struct ConvArgs {
     const void* x;       // gathered operand [n_src, CK]
@@ -193,8 +192,9 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     const int slab_bytes = a.kch * (BN * 16 + 16);
     int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BM]
     int32_t* flags = tile + KTILE * BM;                                // [KTILE]
-    int32_t* list = flags + KTILE;                                     // [KTILE + 1]
-    int32_t* rsrc = list + KTILE + 1;                                  // [BM] output row of tile row r, or -1
+    int32_t* list = flags + KTILE;                                     // [KTILE + 4] (count at KTILE; keeps 16-B alignment)
+    int32_t* rsrc = list + KTILE + 4;                                  // [BM] output row of tile row r, or -1
+    float* sbias = reinterpret_cast<float*>(rsrc + BM);                // [BN] bias of this column block, or 0
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
@@ -203,6 +203,9 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // keeps them off the end of the launch
     const int row0 = (gridDim.x - 1 - blockIdx.x) * BM, col0 = blockIdx.y * BN;
     const int KC = a.kch / 4;  // MFMA steps along CK
+
+    // the bias (or zeros) into LDS now, so the epilogue reads no global memory
+    if (threadIdx.x < BN) sbias[threadIdx.x] = a.bias ? a.bias[col0 + threadIdx.x] : 0.f;
 
     // map staging: thread t owns tile row t % BM and the run of KPT offsets
     // starting at (t / BM) * KPT
@@ -306,15 +309,11 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     }
 
     // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
-    // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels.  The
-    // bias is loaded before the first store (on CDNA the vector memory counter
-    // also counts stores, so a load issued after them would wait for them).
+    // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels
     S* y = static_cast<S*>(a.y);
-    const float* bp = a.bias ? a.bias + col0 + lg * 4 : kZero4;  // no bias: every channel reads zeros
-    const int bstep = a.bias ? 16 : 0;
     f32x4_t bv[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(bp + nb * bstep);
+    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(sbias + nb * 16 + lg * 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int row = rsrc[(wave * RB + rb) * 16 + lr];
@@ -334,7 +333,9 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB_DEFAULT * 16;
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
-    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 1) * 4 + BM * 4;
+    static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
+    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 4) * 4 + BM * 4 +
+                       BN * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
