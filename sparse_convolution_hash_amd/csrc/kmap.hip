@@ -53,7 +53,26 @@ struct KGeom {
     int32_t pz, py, px;
     int32_t dz, dy, dx;
     int32_t oz, oy, ox;          // output grid (equal to the input grid for subm)
+    // reciprocals for division by these invariants (qdiv; 0 for a divisor of 1):
+    // K, the strides, and the output grid's x extent, plane and volume
+    uint64_t mK, msz, msy, msx, mox, mplane, mvol;
 };
+
+// ceil(2^64 / d) for d >= 2, 0 for d == 1 (see qdiv)
+inline uint64_t recip64(uint64_t d) { return d <= 1 ? 0 : ~uint64_t(0) / d + 1; }
+
+// floor(n / d) from m = recip64(d): n * m / 2^64 exceeds n / d by less than
+// n / 2^64 < 2^-32 < 1 / d, which never carries past the next integer.
+__device__ __forceinline__ uint32_t qdiv(uint32_t n, uint64_t m) {
+    return m ? uint32_t(__umul64hi(uint64_t(n), m)) : n;
+}
+
+// Offsets k < K as packed (kz << 6 | ky << 3 | kx), z slowest, into LDS.
+__device__ __forceinline__ void offset_table(uint32_t* ktab, const KGeom& g, int K) {
+    for (int k = threadIdx.x; k < K; k += blockDim.x)
+        ktab[k] = uint32_t((k / (g.kx * g.ky)) << 6 | ((k / g.kx) % g.ky) << 3 | (k % g.kx));
+    __syncthreads();
+}
 
 // Header at the start of the workspace.
 enum { H_FLAGS = 0, H_NOUT = 1, H_WORDS = 64 };
@@ -193,15 +212,18 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
     int nz = 0, ny = 0, nx = 0;
     for (int k = 0; k < g.kz; ++k) {
         const int num = c.y + g.pz - k * g.dz;
-        if (num >= 0 && num % g.sz == 0 && num / g.sz < g.oz && nz < 8) oz[nz++] = num / g.sz;
+        const int q = num >= 0 ? int(qdiv(uint32_t(num), g.msz)) : -1;
+        if (q >= 0 && q * g.sz == num && q < g.oz && nz < 8) oz[nz++] = q;
     }
     for (int k = 0; k < g.ky; ++k) {
         const int num = c.z + g.py - k * g.dy;
-        if (num >= 0 && num % g.sy == 0 && num / g.sy < g.oy && ny < 8) oy[ny++] = num / g.sy;
+        const int q = num >= 0 ? int(qdiv(uint32_t(num), g.msy)) : -1;
+        if (q >= 0 && q * g.sy == num && q < g.oy && ny < 8) oy[ny++] = q;
     }
     for (int k = 0; k < g.kx; ++k) {
         const int num = c.w + g.px - k * g.dx;
-        if (num >= 0 && num % g.sx == 0 && num / g.sx < g.ox && nx < 8) ox[nx++] = num / g.sx;
+        const int q = num >= 0 ? int(qdiv(uint32_t(num), g.msx)) : -1;
+        if (q >= 0 && q * g.sx == num && q < g.ox && nx < 8) ox[nx++] = q;
     }
     for (int a = 0; a < nz; ++a)
         for (int b = 0; b < ny; ++b)
@@ -218,13 +240,16 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
                                                    const uint64_t* __restrict__ table, uint32_t mask,
                                                    int32_t* __restrict__ nbr, const uint32_t* hdr,
                                                    int32_t* coord_err) {
+    __shared__ uint32_t ktab[MAX_K];
     const int K = g.kz * g.ky * g.kx;
+    offset_table(ktab, g, K);
     const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
     if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
     if (t >= int64_t(n) * K) return;
-    const int32_t i = int32_t(t / K);
+    const int32_t i = int32_t(qdiv(uint32_t(t), g.mK));  // K * n < 2^31
     const int k = int(t - int64_t(i) * K);
-    const int kx = k % g.kx, ky = (k / g.kx) % g.ky, kz = k / (g.kx * g.ky);
+    const uint32_t kk = ktab[k];
+    const int kx = kk & 7, ky = (kk >> 3) & 7, kz = kk >> 6;
     int32_t v = -1;
     const int4 c = coords[i];
     if (in_grid(c, g)) {
@@ -335,15 +360,27 @@ __global__ __launch_bounds__(KB) void k_bitmap_emit(const uint32_t* __restrict__
     const uint32_t plane = uint32_t(g.oy) * uint32_t(g.ox), vol = plane * uint32_t(g.oz);
     for (int j = 0; j < WORDS_PER_THREAD; ++j) {
         prefix[w0 + j] = uint32_t(run);
-        if (!emit) continue;
         uint32_t bits = w[j];
+        if (!emit || !bits) continue;
+        // the word's first site, decoded once; its bits are consecutive x
+        const uint32_t key0 = uint32_t(w0 + j) * 32u;
+        const uint32_t b0 = qdiv(key0, g.mvol), r = key0 - b0 * vol;
+        const uint32_t z0 = qdiv(r, g.mplane), r2 = r - z0 * plane;
+        const uint32_t y0 = qdiv(r2, g.mox), x0 = r2 - y0 * uint32_t(g.ox);
         while (bits) {
             const uint32_t bit = __ffs(bits) - 1;
             bits &= bits - 1;
-            const uint32_t key = uint32_t(w0 + j) * 32u + bit;
-            const uint32_t b = key / vol, r = key - b * vol;
-            const uint32_t z = r / plane, r2 = r - z * plane;
-            const uint32_t y = r2 / uint32_t(g.ox), x = r2 - y * uint32_t(g.ox);
+            uint32_t x = x0 + bit, y = y0, z = z0, b = b0;
+            while (x >= uint32_t(g.ox)) {  // carry into y, z, b
+                x -= uint32_t(g.ox);
+                if (++y == uint32_t(g.oy)) {
+                    y = 0;
+                    if (++z == uint32_t(g.oz)) {
+                        z = 0;
+                        ++b;
+                    }
+                }
+            }
             out_coords[run++] = make_int4(int(b), int(z), int(y), int(x));
         }
     }
@@ -358,18 +395,23 @@ __global__ __launch_bounds__(KB) void k_strided_maps(const int4* __restrict__ co
                                                      const uint32_t* __restrict__ prefix,
                                                      int32_t* __restrict__ nbr, int32_t* __restrict__ nbr_in,
                                                      const uint32_t* hdr, int32_t* coord_err) {
+    __shared__ uint32_t ktab[MAX_K];
     const int K = g.kz * g.ky * g.kx;
+    offset_table(ktab, g, K);
     const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
     if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
     if (t >= int64_t(n) * K || int64_t(hdr[H_NOUT]) > cap) return;
-    const int32_t i = int32_t(t / K);
+    const int32_t i = int32_t(qdiv(uint32_t(t), g.mK));  // K * n < 2^31
     const int k = int(t - int64_t(i) * K);
-    const int kx = k % g.kx, ky = (k / g.kx) % g.ky, kz = k / (g.kx * g.ky);
+    const uint32_t kk = ktab[k];
+    const int kx = kk & 7, ky = (kk >> 3) & 7, kz = kk >> 6;
     const int4 c = coords[i];
     int32_t v = -1;
     const int nz = c.y + g.pz - kz * g.dz, ny = c.z + g.py - ky * g.dy, nx = c.w + g.px - kx * g.dx;
-    if (in_grid(c, g) && nz >= 0 && ny >= 0 && nx >= 0 && nz % g.sz == 0 && ny % g.sy == 0 && nx % g.sx == 0) {
-        const int oz = nz / g.sz, oy = ny / g.sy, ox = nx / g.sx;
+    const int oz = nz >= 0 ? int(qdiv(uint32_t(nz), g.msz)) : -1;
+    const int oy = ny >= 0 ? int(qdiv(uint32_t(ny), g.msy)) : -1;
+    const int ox = nx >= 0 ? int(qdiv(uint32_t(nx), g.msx)) : -1;
+    if (in_grid(c, g) && oz >= 0 && oy >= 0 && ox >= 0 && oz * g.sz == nz && oy * g.sy == ny && ox * g.sx == nx) {
         if (oz < g.oz && oy < g.oy && ox < g.ox) {
             const uint32_t key = out_key(c.x, oz, oy, ox, g);
             const uint32_t word = key >> 5, bit = key & 31u;
@@ -684,6 +726,13 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     }
     // an input reaches at most ksize <= 7 outputs per axis (k_insert keeps 8 slots)
     p.K = k.kz * k.ky * k.kx;
+    k.mK = recip64(uint64_t(p.K));
+    k.msz = recip64(uint64_t(k.sz));
+    k.msy = recip64(uint64_t(k.sy));
+    k.msx = recip64(uint64_t(k.sx));
+    k.mox = recip64(uint64_t(k.ox));
+    k.mplane = recip64(uint64_t(k.oy) * uint64_t(k.ox));
+    k.mvol = recip64(uint64_t(k.oz) * uint64_t(k.oy) * uint64_t(k.ox));
     const uint64_t in_vol = uint64_t(g.batch) * k.Z * k.Y * k.X;
     if (in_vol >= (uint64_t(1) << 32))
         return fail(SPC_ERR_UNSUPPORTED, "batch*Z*Y*X = %llu must be below 2^32", (unsigned long long)in_vol);
