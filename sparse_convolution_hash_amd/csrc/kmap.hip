@@ -225,12 +225,22 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         const int q = num >= 0 ? int(qdiv(uint32_t(num), g.msx)) : -1;
         if (q >= 0 && q * g.sx == num && q < g.ox && nx < 8) ox[nx++] = q;
     }
+    // sites along x share a bitmap word mostly: one atomic per word touched
     for (int a = 0; a < nz; ++a)
-        for (int b = 0; b < ny; ++b)
+        for (int b = 0; b < ny; ++b) {
+            const uint32_t base = out_key(c.x, oz[a], oy[b], 0, g);
+            uint32_t word = ~0u, bits = 0;
             for (int d = 0; d < nx; ++d) {
-                const uint32_t key = out_key(c.x, oz[a], oy[b], ox[d], g);
-                atomicOr(bitmap + (key >> 5), 1u << (key & 31u));
+                const uint32_t key = base + uint32_t(ox[d]);
+                if ((key >> 5) != word) {
+                    if (bits) atomicOr(bitmap + word, bits);
+                    word = key >> 5;
+                    bits = 0;
+                }
+                bits |= 1u << (key & 31u);
             }
+            if (bits) atomicOr(bitmap + word, bits);
+        }
 }
 
 // Submanifold probes, one thread per map entry t = i*K + k: nbr[t] = row at
