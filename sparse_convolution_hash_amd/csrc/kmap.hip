@@ -698,7 +698,8 @@ struct Plan {
     int64_t bm_blocks;           // bitmap count/emit blocks
     // workspace offsets
     int64_t rgroups;             // radix block groups
-    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_keys, off_vals, off_hist, off_gsum, total;
+    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, total;
+    size_t sort_slot_bytes;      // per sort: keys x2, values x2, histogram matrix
 };
 
 spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
@@ -769,9 +770,9 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     p.off_bitmap = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_prefix = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_bsums = off;   off = align_up(off + size_t(p.bm_blocks) * 4 + 4, 256);
-    p.off_keys = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two key buffers
-    p.off_vals = off;    off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // two value buffers
-    p.off_hist = off;    off = align_up(off + size_t(RS_BINS) * p.rblk * 4, 256);
+    p.off_masks = off;   off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // neighbour masks, per sort
+    p.sort_slot_bytes = align_up(size_t(p.rows_max) * 4 * 4 + size_t(RS_BINS) * p.rblk * 4, 256);
+    p.off_sort = off;    off += 2 * p.sort_slot_bytes;                            // sort buffers, per sort
     p.rgroups = ceil_div(p.rblk, RS_GROUP);
     p.off_gsum = off;    off = align_up(off + size_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups * 4, 256);
     p.total = off;
@@ -783,12 +784,19 @@ inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 1 << 16)
     return unsigned(std::min<int64_t>(std::max<int64_t>(b, 1), cap));
 }
 
-struct Scratch {
-    uint32_t* hdr;
-    int32_t* counts;
+// Buffers of one radix sort (the two sorts of a call run concurrently, so
+// each has its own).
+struct SortBuf {
     uint32_t* keys[2];
     int32_t* vals[2];
     int32_t* hist;
+};
+
+struct Scratch {
+    uint32_t* hdr;
+    int32_t* counts;
+    uint32_t* mask[2];           // neighbour masks of the rows, per sort slot
+    SortBuf sort[2];
     int32_t* gsum;               // [2 sorts][RS_MAX_PASSES][RS_BINS][groups], zeroed by k_clear
 };
 
@@ -804,11 +812,13 @@ spc_status row_pass(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t
 }
 
 // Stable LSD radix sort of the rows of `map` by neighbour mask into `order`
-// (the identity for K > 32).  keys_ready: s.keys[0] already holds the masks;
-// slot (0 or 1) picks the group sums, so two sorts of one call do not share them.
-// rows_dev < 0 means M from the header; grids are sized for rows_cap rows.
+// (the identity for K > 32), with sort slot `slot`'s buffers and group sums.
+// masks_ready: s.mask[slot] already holds the masks (else a row pass makes
+// them).  The masks are only read, so a concurrent pair compaction may read
+// them too.  rows_dev < 0 means M from the header; grids are sized for
+// rows_cap rows.
 spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
-                     const Scratch& s, bool keys_ready, int slot, int32_t* order, hipStream_t stream) {
+                     const Scratch& s, bool masks_ready, int slot, int32_t* order, hipStream_t stream) {
     const int K = p.K;
     if (K > MASK_BITS) {
         hipLaunchKernelGGL(k_iota, dim3(grid_for(rows_cap, KB, 4096)), dim3(KB), 0, stream, order, rows_dev, cap,
@@ -817,43 +827,79 @@ spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_
         return SPC_OK;
     }
     if (rows_cap == 0) return SPC_OK;
-    if (!keys_ready) {
-        spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.keys[0], nullptr, stream);
+    if (!masks_ready) {
+        spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.mask[slot], nullptr, stream);
         if (st != SPC_OK) return st;
     }
+    const SortBuf& sb = s.sort[slot];
     const unsigned nb = unsigned(ceil_div(rows_cap, RS_TILE));
     const int ng = int(ceil_div(nb, RS_GROUP));
     const int passes = (K + RS_BITS - 1) / RS_BITS;
-    int cur = 0;
+    const uint32_t* kin = s.mask[slot];
+    const int32_t* vin = nullptr;
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = RS_BITS * pass;
         int32_t* gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
-        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, s.keys[cur], rows_dev, cap, s.hdr, shift,
-                           s.hist, gsum, ng);
+        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, kin, rows_dev, cap, s.hdr, shift,
+                           sb.hist, gsum, ng);
         SPC_LAUNCHED("k_rs_hist");
         const bool last = pass + 1 == passes;
-        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, s.keys[cur],
-                           pass == 0 ? nullptr : s.vals[cur], rows_dev, cap, s.hdr, shift, s.hist, gsum, ng,
-                           s.keys[cur ^ 1], last ? order : s.vals[cur ^ 1]);
+        uint32_t* kout = sb.keys[pass & 1];
+        int32_t* vout = last ? order : sb.vals[pass & 1];
+        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, kin, vin, rows_dev, cap, s.hdr, shift,
+                           sb.hist, gsum, ng, kout, vout);
         SPC_LAUNCHED("k_rs_scatter");
-        cur ^= 1;
+        kin = kout;
+        vin = vout;
     }
     return SPC_OK;
 }
 
-// Row pass (masks and counts), scan and ordered compaction of a map into CSR
-// pairs.  Leaves the masks in s.keys[0] (K <= 32).
+// Concurrent work of one call: a side stream (per host thread and device,
+// default priority) forked from and joined back into the caller's stream.
+struct Side {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+spc_status side_for_device(Side** out) {
+    static thread_local Side sides[64];
+    int dev = 0;
+    SPC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(SPC_ERR_UNSUPPORTED, "device %d", dev);
+    Side& sd = sides[dev];
+    if (!sd.stream) {
+        SPC_HIP(hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking));
+        SPC_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
+        SPC_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
+    }
+    *out = &sd;
+    return SPC_OK;
+}
+
+spc_status fork_to(Side* sd, hipStream_t stream) {
+    SPC_HIP(hipEventRecord(sd->fork, stream));
+    SPC_HIP(hipStreamWaitEvent(sd->stream, sd->fork, 0));
+    return SPC_OK;
+}
+
+spc_status join_from(Side* sd, hipStream_t stream) {
+    SPC_HIP(hipEventRecord(sd->join, sd->stream));
+    SPC_HIP(hipStreamWaitEvent(stream, sd->join, 0));
+    return SPC_OK;
+}
+
+// Scan and ordered compaction of a map into CSR pairs, from the counts (and,
+// for K <= 27, the masks in s.mask[0]) of a row pass already enqueued.
 spc_status map_pairs(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
                      const Scratch& s, int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, hipStream_t stream) {
     const int64_t blk = ceil_div(rows_cap, KB);
-    spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.keys[0], s.counts, stream);
-    if (st != SPC_OK) return st;
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, s.counts, int64_t(p.K) * blk, pair_ptr, p.K,
                        blk, (uint32_t*)nullptr);
     SPC_LAUNCHED("k_scan");
     if (blk > 0) {
         hipLaunchKernelGGL(k_compact_pairs, dim3(unsigned(blk)), dim3(KB), 0, stream, map, rows_dev, p.K, cap, s.hdr,
-                           p.K <= ROWPASS_KMAX ? s.keys[0] : nullptr, s.counts, pair_in, pair_out);
+                           p.K <= ROWPASS_KMAX ? s.mask[0] : nullptr, s.counts, pair_in, pair_out);
         SPC_LAUNCHED("k_compact_pairs");
     }
     return SPC_OK;
@@ -923,11 +969,17 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     Scratch s;
     s.hdr = reinterpret_cast<uint32_t*>(base);
     s.counts = reinterpret_cast<int32_t*>(base + p.off_counts);
-    s.keys[0] = reinterpret_cast<uint32_t*>(base + p.off_keys);
-    s.keys[1] = s.keys[0] + p.rows_max;
-    s.vals[0] = reinterpret_cast<int32_t*>(base + p.off_vals);
-    s.vals[1] = s.vals[0] + p.rows_max;
-    s.hist = reinterpret_cast<int32_t*>(base + p.off_hist);
+    s.mask[0] = reinterpret_cast<uint32_t*>(base + p.off_masks);
+    s.mask[1] = s.mask[0] + p.rows_max;
+    for (int q = 0; q < 2; ++q) {
+        char* b = base + p.off_sort + q * p.sort_slot_bytes;
+        SortBuf& sb = s.sort[q];
+        sb.keys[0] = reinterpret_cast<uint32_t*>(b);
+        sb.keys[1] = sb.keys[0] + p.rows_max;
+        sb.vals[0] = reinterpret_cast<int32_t*>(sb.keys[1] + p.rows_max);
+        sb.vals[1] = sb.vals[0] + p.rows_max;
+        sb.hist = sb.vals[1] + p.rows_max;
+    }
     s.gsum = reinterpret_cast<int32_t*>(base + p.off_gsum);
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);
@@ -955,12 +1007,19 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         hipLaunchKernelGGL(k_subm_probe, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
                            stream, c4, n, p.g, table, mask, nbr, s.hdr, coord_err);
         SPC_LAUNCHED("k_subm_probe");
+        if (pairs || order) {
+            // one row pass: the masks (for the order and the compaction) and the counts
+            st = row_pass(p, nbr, n, n, n, s, s.mask[0], pairs ? s.counts : nullptr, stream);
+            if (st != SPC_OK) return st;
+        }
+        // (a side stream for the sort does not pay here: the compaction it
+        // would overlap is short next to the cost of the fork and join)
         if (pairs) {
             st = map_pairs(p, nbr, n, n, n, s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
         }
         if (order) {
-            st = sort_rows(p, nbr, n, n, n, s, pairs, 0, order, stream);
+            st = sort_rows(p, nbr, n, n, n, s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }
         *n_out = n_in;
@@ -991,18 +1050,26 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
                            stream, c4, n, int64_t(out_cap), p.g, bitmap, prefix, nbr, nbr_in, s.hdr, coord_err);
         SPC_LAUNCHED("k_strided_maps");
+        // the input-side order (its own row pass and sort) runs beside the rest
+        Side* sd = nullptr;
+        if (order_in) {
+            if ((st = side_for_device(&sd)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
+            st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, sd->stream);
+            if (st != SPC_OK) return st;
+        }
+        if (pairs || order) {
+            st = row_pass(p, nbr, -1, cap, int64_t(out_cap), s, s.mask[0], pairs ? s.counts : nullptr, stream);
+            if (st != SPC_OK) return st;
+        }
         if (pairs) {
             st = map_pairs(p, nbr, -1, cap, int64_t(out_cap), s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
         }
         if (order) {
-            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, pairs, 0, order, stream);
+            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }
-        if (order_in) {
-            st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, stream);
-            if (st != SPC_OK) return st;
-        }
+        if (sd && (st = join_from(sd, stream)) != SPC_OK) return st;
     }
     SPC_HIP(hipMemcpyAsync(host_hdr, s.hdr, sizeof(host_hdr), hipMemcpyDeviceToHost, stream));
     SPC_HIP(hipStreamSynchronize(stream));

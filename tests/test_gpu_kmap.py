@@ -145,3 +145,18 @@ def test_kmap_repeatable():
     assert torch.equal(a["nbr"], b["nbr"]) and torch.equal(a["pair_ptr"], b["pair_ptr"])
     assert torch.equal(a["pair_in"][:P], b["pair_in"][:P]) and torch.equal(a["pair_out"][:P], b["pair_out"][:P])
     assert torch.equal(a["order"], b["order"])
+
+
+def test_strided_kmap_on_a_user_stream():
+    # the input-side order is built on a side stream forked from the caller's:
+    # the result on a caller-made stream matches the default stream's bit for bit
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    c = cuda(w.coords)
+    ref = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        res = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
+    st.synchronize()
+    for key in ("out_coords", "nbr", "nbr_in", "pair_ptr", "order", "order_in"):
+        assert torch.equal(res[key], ref[key]), key
