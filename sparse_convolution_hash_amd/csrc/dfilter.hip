@@ -169,9 +169,13 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
 // Workgroup b walks segment b of the pair list in steps; each offset it
 // touches gets one partial tile, part[b + k] (b + k is distinct for every
 // (segment, offset) pair a walk can meet, as both only grow along it).
-// IDENT: K == 1 with the identity pairs (i, i), no pair lists.
-template <typename TT, bool IDENT>
+// IDENT: K == 1 with the identity pairs (i, i), no pair lists.  MIM x NOM:
+// the most 16x16 blocks a wave holds (channel tiles of up to 32*MIM x
+// 32*NOM).  DEPTH: steps of rows in flight (2 fits the registers only with
+// small accumulator tiles); pair indices are fetched one step earlier still.
+template <typename TT, bool IDENT, int MIM, int NOM, int DEPTH>
 __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
+    static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps of rows in flight");
     constexpr int E = TT::E;
     constexpr int ROW = lds_row<TT>();
     __shared__ __attribute__((aligned(16))) char xt[TMAX * ROW];  // [ci][pairs]
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
     const int wi = wave >> 1, wo = wave & 1;
-    const int MI = (TI / 16 + 1) / 2, NO = (TO / 16 + 1) / 2;  // 16x16 blocks per wave (<= 4)
+    const int MI = (TI / 16 + 1) / 2, NO = (TO / 16 + 1) / 2;  // 16x16 blocks per wave (<= MIM, NOM)
     constexpr int PG = PS / E;
     const int xi_items = PG * (TI / E), items = xi_items + PG * (TO / E);
 
@@ -199,32 +203,37 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     const bool has_item = my < items;
     const ItemGeo geo(has_item ? my : items - 1, xi_items, E);
 
-    // rows one step ahead, pair indices two steps ahead (two index buffers
-    // swap roles every step, by unrolling, as a register copy would wait
-    // for its pending load)
+    f32x4_t acc[MIM][NOM];
+#pragma unroll
+    for (int mi = 0; mi < MIM; ++mi)
+#pragma unroll
+        for (int no = 0; no < NOM; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // the step pipeline: cur (rows landed or landing), then DEPTH - 1 more
+    // steps of rows in flight, then one step of pair indices in flight
     Step cur = step_at(sptr, s0, 0, s1);
     Step nxt = step_at(sptr, cur.e, cur.k, s1);
-    Item<TT> pre;
-    int32_t ia[E], ib[E];  // indices of step nxt (ia before an even step, ib before an odd one)
+    Step nx2 = (DEPTH == 2 && nxt.k >= 0) ? step_at(sptr, nxt.e, nxt.k, s1) : Step{0, 0, -1};
+    Item<TT> ra, rb;       // rows (rb only for DEPTH 2)
+    int32_t ia[E], ib[E];  // pair indices of the step whose rows are loaded next
     {
-        int32_t r0[E];
+        int32_t r0[E], r1[E];
         load_idx<TT, IDENT>(r0, a, geo, cur);
-        if (nxt.k >= 0) load_idx<TT, IDENT>(ia, a, geo, nxt);
-        load_rows<TT>(pre, r0, a, geo, ci0, co0, cur);
+        if (DEPTH == 2 && nxt.k >= 0) load_idx<TT, IDENT>(r1, a, geo, nxt);
+        const Step& ahead = DEPTH == 2 ? nx2 : nxt;
+        if (ahead.k >= 0) load_idx<TT, IDENT>(ia, a, geo, ahead);
+        load_rows<TT>(ra, r0, a, geo, ci0, co0, cur);
+        if (DEPTH == 2 && nxt.k >= 0) load_rows<TT>(rb, r1, a, geo, ci0, co0, nxt);
     }
 
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int no = 0; no < 4; ++no) acc[mi][no] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // one step: cur's rows are in `pre`, which is then refilled with nxt's
-    // rows from indices `use`; the indices of the step after go to `fill`
-    auto step = [&](const int32_t (&use)[E], int32_t (&fill)[E]) {
-        const Step nx2 = nxt.k >= 0 ? step_at(sptr, nxt.e, nxt.k, s1) : Step{0, 0, -1};
+    // one step: cur's rows are in `mine`, which is then refilled with the
+    // rows of the step DEPTH ahead (indices in `use`); the indices of the
+    // step after that go to `fill`
+    auto step = [&](Item<TT>& mine, const int32_t (&use)[E], int32_t (&fill)[E]) {
+        const Step& ahead = DEPTH == 2 ? nx2 : nxt;
+        const Step after = ahead.k >= 0 ? step_at(sptr, ahead.e, ahead.k, s1) : Step{0, 0, -1};
         __syncthreads();  // the previous step's tiles are consumed
-        if (has_item) store_item<TT>(xt, gt, pre, my, xi_items);
+        if (has_item) store_item<TT>(xt, gt, mine, my, xi_items);
         for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32): not pipelined
             const ItemGeo g2(it, xi_items, E);
             int32_t r2[E];
@@ -234,26 +243,26 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
             store_item<TT>(xt, gt, tmp, it, xi_items);
         }
         __syncthreads();
-        if (nxt.k >= 0) {
-            load_rows<TT>(pre, use, a, geo, ci0, co0, nxt);
-            if (nx2.k >= 0) load_idx<TT, IDENT>(fill, a, geo, nx2);
+        if (ahead.k >= 0) {
+            load_rows<TT>(mine, use, a, geo, ci0, co0, ahead);
+            if (after.k >= 0) load_idx<TT, IDENT>(fill, a, geo, after);
         }
 #pragma unroll
         for (int ks = 0; ks < PS / (4 * E); ++ks) {
             const int poff = (ks * 4 + lg) * 16;
-            u32x4 gf[4], xf[4];
+            u32x4 gf[NOM], xf[MIM];
 #pragma unroll
-            for (int no = 0; no < 4; ++no)
+            for (int no = 0; no < NOM; ++no)
                 if (no < NO && (wo * NO + no) * 16 < TO)
                     gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MIM; ++mi)
                 if (mi < MI && (wi * MI + mi) * 16 < TI)
                     xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MIM; ++mi)
 #pragma unroll
-                for (int no = 0; no < 4; ++no)
+                for (int no = 0; no < NOM; ++no)
                     if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
                         acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
         }
@@ -262,9 +271,9 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
             // tile, this lane holds co = lg*4 .. +3 of ci = lr
             float* part = a.part + (int64_t(blockIdx.x) + cur.k) * a.cin * a.cout;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MIM; ++mi)
 #pragma unroll
-                for (int no = 0; no < 4; ++no) {
+                for (int no = 0; no < NOM; ++no) {
                     if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
                     const int ci = ci0 + (wi * MI + mi) * 16 + lr;
                     const int co = co0 + (wo * NO + no) * 16 + lg * 4;
@@ -273,12 +282,25 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
                 }
         }
         cur = nxt;
-        nxt = nx2;
+        if (DEPTH == 2) {
+            nxt = nx2;
+            nx2 = after;
+        } else {
+            nxt = after;
+        }
     };
-    while (cur.k >= 0) {
-        step(ia, ib);
-        if (cur.k < 0) break;
-        step(ib, ia);
+    if constexpr (DEPTH == 1) {
+        while (cur.k >= 0) {
+            step(ra, ia, ib);
+            if (cur.k < 0) break;
+            step(ra, ib, ia);
+        }
+    } else {
+        while (cur.k >= 0) {
+            step(ra, ia, ib);
+            if (cur.k < 0) break;
+            step(rb, ib, ia);
+        }
     }
 }
 
@@ -422,10 +444,27 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
     const unsigned tiles = unsigned(ceil_div(a.cin, TMAX) * ceil_div(a.cout, TMAX));
     DfArgs b = a;
     b.nseg = int32_t(std::max<int64_t>(64, MAX_WG / tiles));
-    if (a.ptr)
-        hipLaunchKernelGGL((k_dfilter<TT, false>), dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
+    // accumulator extent per wave: 2 or 4 blocks of 16 per dimension (a
+    // 128-channel tile needs 4); two steps of rows in flight fit the
+    // registers only next to the smaller accumulators
+    const int mim = std::min<int64_t>(a.cin, TMAX) > 64 ? 4 : 2, nom = std::min<int64_t>(a.cout, TMAX) > 64 ? 4 : 2;
+    const dim3 grid(unsigned(b.nseg), tiles);
+#define SPC_DFILTER(MIM_, NOM_, DEPTH_)                                                                     \
+    do {                                                                                                    \
+        if (a.ptr)                                                                                          \
+            hipLaunchKernelGGL((k_dfilter<TT, false, MIM_, NOM_, DEPTH_>), grid, dim3(DT), 0, stream, b);    \
+        else                                                                                                \
+            hipLaunchKernelGGL((k_dfilter<TT, true, MIM_, NOM_, DEPTH_>), grid, dim3(DT), 0, stream, b);     \
+    } while (0)
+    if (mim == 2 && nom == 2)
+        SPC_DFILTER(2, 2, 2);
+    else if (mim == 2)
+        SPC_DFILTER(2, 4, 2);
+    else if (nom == 2)
+        SPC_DFILTER(4, 2, 2);
     else
-        hipLaunchKernelGGL((k_dfilter<TT, true>), dim3(unsigned(b.nseg), tiles), dim3(DT), 0, stream, b);
+        SPC_DFILTER(4, 4, 1);
+#undef SPC_DFILTER
     SPC_LAUNCHED("k_dfilter");
     const int64_t L = int64_t(a.cin) * a.cout;
     hipLaunchKernelGGL(k_reduce_segs, dim3(unsigned(L / 256), unsigned(a.K)), dim3(256), 0, stream, b, dw);
