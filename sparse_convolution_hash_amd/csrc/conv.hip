@@ -185,13 +185,17 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     using S = typename TT::storage;
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB * 16;
+    // row stride of the LDS map tile: an odd stride spreads the writes of
+    // consecutive offsets of one row over consecutive banks
+    constexpr int BMP = BM + 1;
+    static_assert(KTILE % 4 == 0, "the tile keeps the following arrays 16-byte aligned");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // the two slab buffers are addressed arithmetically from the __shared__
     // base (a pointer table would hide the address space and turn the LDS
     // reads into flat loads that wait on the global prefetches)
     const int slab_bytes = a.kch * (BN * 16 + 16);
-    int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BM]
-    int32_t* flags = tile + KTILE * BM;                                // [KTILE]
+    int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BMP]
+    int32_t* flags = tile + KTILE * BMP;                               // [KTILE]
     int32_t* list = flags + KTILE;                                     // [KTILE + 4] (count at KTILE; keeps 16-B alignment)
     int32_t* rsrc = list + KTILE + 4;                                  // [BM] output row of tile row r, or -1
     float* sbias = reinterpret_cast<float*>(rsrc + BM);                // [BN] bias of this column block, or 0
@@ -207,18 +211,13 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // the bias (or zeros) into LDS now, so the epilogue reads no global memory
     if (threadIdx.x < BN) sbias[threadIdx.x] = a.bias ? a.bias[col0 + threadIdx.x] : 0.f;
 
-    // map staging: thread t owns tile row t % BM and the run of KPT offsets
-    // starting at (t / BM) * KPT
-    static_assert(CT % BM == 0, "whole rows per staging thread group");
-    constexpr int KQ = CT / BM, KPT = (KTILE + KQ - 1) / KQ;
-    const int sr = threadIdx.x % BM, sq = threadIdx.x / BM;
-    int32_t ssrc;  // source row of tile row sr (the processing order applied), or -1
-    {
-        const int row = row0 + sr;
+    // the processing order of this tile's rows into LDS: rsrc[r] is the
+    // source row of tile row r, or -1
+    if (threadIdx.x < BM) {
+        const int row = row0 + threadIdx.x;
         const int rc = row < a.n_rows ? row : a.n_rows - 1;
         const int32_t s0 = a.order ? a.order[rc] : rc;
-        ssrc = row < a.n_rows && (unsigned)s0 < (unsigned)a.n_rows ? s0 : -1;
-        if (sq == 0) rsrc[sr] = ssrc;
+        rsrc[threadIdx.x] = row < a.n_rows && (unsigned)s0 < (unsigned)a.n_rows ? s0 : -1;
     }
 
     f32x4_t acc[RB][NB];
@@ -236,25 +235,45 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
         if (threadIdx.x < KTILE) flags[threadIdx.x] = 0;
         __syncthreads();
         {
-            // all of this thread's map entries in flight at once: unguarded
-            // loads from one base (an invalid row reads row 0, entries past
-            // the chunk re-read its last one) whose results are then dropped
-            const int kb = sq * KPT, lim = kt - 1 - kb;  // lim < 0: no offset of this chunk here
-            const int l2 = lim >= 0 ? lim : 0;
-            const int32_t* p = a.map ? a.map + int64_t(ssrc < 0 ? 0 : ssrc) * a.K + kt0 + (lim >= 0 ? kb : 0)
-                                     : nullptr;
-            int32_t v[KPT];
+            // the chunk's BM x kt map entries, read row by row: entry e of the
+            // chunk is (row e / kt, offset e % kt) and thread t takes e = t,
+            // t + CT, ..., so a load instruction covers a few whole rows (a few
+            // cache lines) rather than one row per lane.  All loads are in
+            // flight at once: unguarded, from clamped addresses (an invalid row
+            // reads row 0, entries past the chunk re-read its last entry), with
+            // the results dropped when they are written to LDS.
+            constexpr int MPT = (BM * KTILE + CT - 1) / CT;
+            const int dq = CT / kt, dr = CT - dq * kt;
+            const int r0 = int(threadIdx.x) / kt, j0 = int(threadIdx.x) - r0 * kt;
+            int32_t v[MPT];
+            if (a.map) {
+                int r = r0, j = j0;
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) v[u] = p ? p[u <= l2 ? u : l2] : ssrc;
-#pragma unroll
-            for (int u = 0; u < KPT; ++u) {
-                if (u <= lim) {  // uniform over the wave (a wave's threads share sq)
-                    int32_t val = ssrc >= 0 ? v[u] : -1;
-                    if ((unsigned)val >= (unsigned)a.n_src) val = -1;
-                    tile[(kb + u) * BM + sr] = val;
-                    // one flag write per wave: lanes writing one LDS word serialise
-                    if (__any(val >= 0) && lane == 0) flags[kb + u] = 1;
+                for (int u = 0; u < MPT; ++u) {
+                    const bool in = r < BM;
+                    const int32_t src = rsrc[in ? r : BM - 1];
+                    v[u] = a.map[int64_t(src < 0 ? 0 : src) * a.K + kt0 + (in ? j : kt - 1)];
+                    r += dq;
+                    j += dr;
+                    if (j >= kt) j -= kt, ++r;
                 }
+            } else {  // identity map (K = 1): the entry is the row itself
+#pragma unroll
+                for (int u = 0; u < MPT; ++u) v[u] = 0;
+            }
+            int r = r0, j = j0;
+#pragma unroll
+            for (int u = 0; u < MPT; ++u) {
+                if (r < BM) {
+                    const int32_t src = rsrc[r];
+                    int32_t val = src < 0 ? -1 : a.map ? v[u] : src;
+                    if ((unsigned)val >= (unsigned)a.n_src) val = -1;
+                    tile[j * BMP + r] = val;
+                    if (val >= 0) flags[j] = 1;
+                }
+                r += dq;
+                j += dr;
+                if (j >= kt) j -= kt, ++r;
             }
         }
         __syncthreads();
@@ -270,7 +289,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
         auto slab_of = [&](int j) { const int kg = kt0 + list[j]; return a.w_rev ? a.K - 1 - kg : kg; };
         wst.load(a, slab_of(0));
-        bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, tile + list[0] * BM, wave, lr, lg);
+        bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, tile + list[0] * BMP, wave, lr, lg);
         wst.store(lds, a, slab_of(0), col0);
         // drain the prologue's gathers here, so that inside the loop the only
         // loads in flight are the next offset's prefetches and the MFMAs need
@@ -282,7 +301,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             bool any_next = false;
             if (has_next) {
                 wst.load(a, slab_of(j + 1));
-                any_next = gather_rows<TT, RB, KCMAX>(anext, a, tile + list[j + 1] * BM, wave, lr, lg);
+                any_next = gather_rows<TT, RB, KCMAX>(anext, a, tile + list[j + 1] * BMP, wave, lr, lg);
             }
             if (any_cur) {
                 const char* sl = lds + (j & 1) * slab_bytes;
@@ -334,8 +353,8 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BM = NW * RB_DEFAULT * 16;
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
     static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
-    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * BM * 4 + (2 * KTILE + 4) * 4 + BM * 4 +
-                       BN * 4;
+    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * (BM + 1) * 4 + (2 * KTILE + 4) * 4 +
+                       BM * 4 + BN * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));

@@ -159,3 +159,25 @@ def test_workload_train_shells_bf16():
     t = {"feats": w.feats, "weight": w.weight, "bias": None, "grad": w.grad}
     errs = run_subm_layer(w.coords, w.batch, w.shape, 3, t, w.dtype, what=w.name)
     print("errors", errs, flush=True)
+
+
+@pytest.mark.parametrize("dtype,cin,cout", [(torch.float16, 64, 48), (torch.float32, 32, 16)])
+def test_many_tiles_with_empty_tiles(dtype, cin, cout):
+    # more 128-row tiles than workgroups resident at once, whole tiles whose
+    # rows hit no offset, and a ragged tail: a grid that walks several tiles
+    # per workgroup must give every row its own sum and leave empty rows at
+    # the bias
+    r = W.rng(77)
+    n_src, M, K = 5000, 140_037, 27
+    nbr = np.where(r.random((K, M)) < 0.15, r.integers(0, n_src, (K, M)), -1).astype(np.int32)
+    tiles = (M + 127) // 128
+    for j in np.nonzero(r.random(tiles) < 0.3)[0]:
+        nbr[:, j * 128:(j + 1) * 128] = -1
+    t = W.small_layer(78, np.zeros((n_src, 4), np.int32), cin, cout, K, dtype)
+    print(f"synthetic map M={M} n_src={n_src} {dtype} {cin}->{cout}", flush=True)
+    x, w, b = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"])
+    nbr_mk = cuda(np.ascontiguousarray(nbr.T))
+    out = spc.sparse_conv_fwd(x, w, b, nbr_mk, M)
+    assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr), TOL[dtype], "fwd")
+    perm = cuda(r.permutation(M).astype(np.int32))
+    assert torch.equal(out, spc.sparse_conv_fwd(x, w, b, nbr_mk, M, perm))
