@@ -8,7 +8,9 @@ never calls it and has no CPU fallback.  It shares no code with the HIP path.
 * ``kmap``  -- kernel maps: the submanifold ``[K^3, N]`` neighbour map by sorted
   keys and binary search, and the strided output coordinates, maps and pair
   lists written out from their definition.
-* ``conv``  -- forward, dinput, dfilter and dbias as per-offset fp64 sums.
+* ``conv``  -- forward, dinput, dfilter and dbias as per-offset fp64 sums, and
+  the inverse (upsampling) convolution on a saved strided map with its
+  dinput and dfilter.
 
 Every function cites the passage it follows.  Pins that tie it to the pages
 and to mathematics live in ``tests/test_oracle_*.py``.

@@ -87,6 +87,57 @@ def conv_bwd_bias(dout) -> np.ndarray:
     return f64(dout).sum(axis=0)
 
 
+# ------------------------------------------------ inverse (upsampling) conv
+
+# SparseInverseConv3d (spconv USAGE.md, the layer table and "Using
+# SparseInverseConv for Inverse Sparse Operations"): an upsampling layer that
+# reuses the kernel map saved by an earlier strided SparseConv3d (same
+# indice_key) and writes its output on that layer's INPUT sites, so the result
+# has the sites the downsampling started from.  Every pair (i, o) of offset k of
+# the saved map (input row i = nbr[k][o] feeding output row o) carries the
+# coarse row o back to the fine row i through the inverse layer's own W[k].
+# ``nbr`` below is the saved strided map [K, M] as the forward conv used it.
+
+def inverse_conv_fwd(feats, weight, bias, nbr, n_fine: int) -> np.ndarray:
+    """``out[i] = bias + sum over (k, o) with nbr[k][o] = i of feats[o] @ W[k]``,
+    fp64 ``[n_fine, Cout]``; ``feats`` is ``[M, Cin]`` on the coarse sites."""
+    x, w = f64(feats), f64(weight)
+    nbr = np.asarray(nbr)
+    out = np.zeros((n_fine, w.shape[2]), dtype=np.float64)
+    if bias is not None:
+        out += f64(bias)[None, :]
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        i = nbr[k][o]
+        assert np.unique(i).size == i.size  # one offset pairs each fine row at most once
+        out[i] += x[o] @ w[k]
+    return out
+
+
+def inverse_conv_bwd_input(dout, weight, nbr, n_coarse: int) -> np.ndarray:
+    """Adjoint of ``inverse_conv_fwd`` in the coarse features:
+    ``din[o] = sum_k dout[nbr[k][o]] @ W[k]^T`` over present pairs, fp64."""
+    g, w = f64(dout), f64(weight)
+    nbr = np.asarray(nbr)
+    din = np.zeros((n_coarse, w.shape[1]), dtype=np.float64)
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        din[o] += g[nbr[k][o]] @ w[k].T
+    return din
+
+
+def inverse_conv_bwd_filter(feats, dout, nbr) -> np.ndarray:
+    """Weight derivative of ``inverse_conv_fwd``:
+    ``dW[k] = sum_o feats[o]^T dout[nbr[k][o]]`` over present pairs, fp64."""
+    x, g = f64(feats), f64(dout)
+    nbr = np.asarray(nbr)
+    dw = np.zeros((nbr.shape[0], x.shape[1], g.shape[1]), dtype=np.float64)
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        dw[k] = x[o].T @ g[nbr[k][o]]
+    return dw
+
+
 def max_rel_err(got, ref) -> float:
     """``max|got - ref| / max|ref|`` (0 when both are empty or ref is all zero)."""
     g, r = f64(got), f64(ref)

@@ -37,3 +37,16 @@ def dense_conv(coords, feats, weight, bias, batch, shape, ksize, stride=1, pad=N
     if pad is None:
         pad = ksize // 2
     return F.conv3d(x, torch_weight(weight, ksize), b, stride=stride, padding=pad, dilation=dil)
+
+
+def dense_conv_transpose(coarse_coords, coarse_feats, weight, bias, batch, coarse_shape, fine_shape, ksize,
+                         stride, pad, dil=1):
+    """torch's conv_transpose3d of the coarse voxels scattered into a dense grid,
+    with the output padding that makes its extent exactly ``fine_shape``."""
+    x = densify(coarse_coords, coarse_feats, batch, coarse_shape)
+    w = torch.as_tensor(np.asarray(weight), dtype=torch.float64)
+    K, cin, cout = w.shape
+    w = w.reshape(ksize, ksize, ksize, cin, cout).permute(3, 4, 0, 1, 2).contiguous()  # [Cin, Cout, kz, ky, kx]
+    b = None if bias is None else torch.as_tensor(np.asarray(bias), dtype=torch.float64)
+    op = tuple(f - ((c - 1) * stride - 2 * pad + dil * (ksize - 1) + 1) for f, c in zip(fine_shape, coarse_shape))
+    return F.conv_transpose3d(x, w, b, stride=stride, padding=pad, output_padding=op, dilation=dil)

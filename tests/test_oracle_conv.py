@@ -9,7 +9,7 @@ import torch
 import workloads as W
 from oracle import conv as C
 from oracle import kmap as O
-from tests.dense import dense_conv, densify, sample, torch_weight
+from tests.dense import dense_conv, dense_conv_transpose, densify, sample, torch_weight
 
 
 def _layer(seed, c, cin, cout, K, dtype=torch.float64, n_out=None):
@@ -163,3 +163,65 @@ def test_planted_dropped_offset_is_caught(monkeypatch):
         return nbr
     monkeypatch.setattr(O, "subm_kmap", dropped)
     assert not _dense_pin_holds()
+
+
+# ------------------------------------------------ inverse (upsampling) conv
+
+def _inverse_case(shape, k, s, p, d, seed, cin=3, cout=4):
+    c = W.tiny_grid(W.rng(seed), min(shape), 0.25, 2)
+    res = O.strided_kmap(c, 2, shape, k, s, p, d)
+    M = res["out_coords"].shape[0]
+    # the coarse layer's features, the inverse layer's weight [K, Cin, Cout], and a
+    # gradient on the fine sites
+    t = _layer(seed + 1, res["out_coords"], cin, cout, k ** 3, n_out=c.shape[0])
+    return c, res, M, t
+
+
+@pytest.mark.parametrize("shape,k,s,p,d", [
+    ((7, 8, 6), 3, 2, 1, 1), ((8, 8, 7), 2, 2, 0, 1), ((9, 7, 8), 3, 1, 0, 2), ((8, 9, 7), 3, 3, 2, 1),
+])
+def test_inverse_fwd_equals_dense_conv_transpose3d(shape, k, s, p, d):
+    c, res, M, t = _inverse_case(shape, k, s, p, d, 110 + k + s)
+    got = C.inverse_conv_fwd(t["feats"], t["weight"], t["bias"], res["nbr_out"], c.shape[0])
+    oshape = O.out_shape(shape, k, s, p, d)
+    dense = dense_conv_transpose(res["out_coords"], t["feats"], t["weight"], t["bias"], 2, oshape, shape, k, s, p, d)
+    np.testing.assert_allclose(got, sample(dense, c).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape,k,s,p,d", [((7, 8, 6), 3, 2, 1, 1), ((8, 8, 7), 2, 2, 0, 1)])
+def test_inverse_backward_equals_autograd(shape, k, s, p, d):
+    c, res, M, t = _inverse_case(shape, k, s, p, d, 120 + k)
+    oshape = O.out_shape(shape, k, s, p, d)
+    x = densify(res["out_coords"], t["feats"], 2, oshape).requires_grad_(True)
+    w = torch.as_tensor(t["weight"].numpy(), dtype=torch.float64).requires_grad_(True)
+    wt = w.reshape(k, k, k, w.shape[1], w.shape[2]).permute(3, 4, 0, 1, 2)
+    op = tuple(f - ((q - 1) * s - 2 * p + d * (k - 1) + 1) for f, q in zip(shape, oshape))
+    y = torch.nn.functional.conv_transpose3d(x, wt, None, stride=s, padding=p, output_padding=op, dilation=d)
+    g = torch.zeros_like(y)
+    cc = torch.as_tensor(c.astype(np.int64))
+    g[cc[:, 0], :, cc[:, 1], cc[:, 2], cc[:, 3]] = torch.as_tensor(t["grad"].numpy(), dtype=torch.float64)
+    (y * g).sum().backward()
+    np.testing.assert_allclose(C.inverse_conv_bwd_input(t["grad"], t["weight"], res["nbr_out"], M),
+                               sample(x.grad, res["out_coords"]).numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(C.inverse_conv_bwd_filter(t["feats"], t["grad"], res["nbr_out"]), w.grad.numpy(),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_inverse_is_adjoint_of_strided_conv():
+    # <inverse(x; W), z> = <x, strided conv(z; W^T)> on the same saved map
+    c, res, M, t = _inverse_case((9, 9, 9), 3, 2, 1, 1, 130, cin=5, cout=6)
+    x, w, z = t["feats"].numpy(), t["weight"].numpy(), t["grad"].numpy()
+    lhs = (C.inverse_conv_fwd(x, w, None, res["nbr_out"], c.shape[0]) * z).sum()
+    rhs = (x * C.conv_fwd(z, w.transpose(0, 2, 1), None, res["nbr_out"])).sum()
+    assert np.isclose(lhs, rhs, rtol=1e-12)
+
+
+def test_planted_inverse_offset_reversal_is_caught(monkeypatch):
+    # using W[K-1-k] (the transpose-conv flip that the inverse layer does not do)
+    c, res, M, t = _inverse_case((7, 8, 6), 3, 2, 1, 1, 140)
+    real = C.f64
+    monkeypatch.setattr(C, "f64", lambda a: real(a)[::-1].copy() if real(a).ndim == 3 else real(a))
+    got = C.inverse_conv_fwd(t["feats"], t["weight"], t["bias"], res["nbr_out"], c.shape[0])
+    dense = dense_conv_transpose(res["out_coords"], t["feats"], t["weight"], t["bias"], 2,
+                                 O.out_shape((7, 8, 6), 3, 2, 1, 1), (7, 8, 6), 3, 2, 1)
+    assert not np.allclose(got, sample(dense, c).numpy(), rtol=1e-10, atol=1e-10)
