@@ -28,6 +28,10 @@ between two HIP events (the step's stage timings include host gaps, e.g. after
 the strided kernel map's one synchronisation), and that average is its launch
 duration.  Its HBM traffic comes from the rocprofv3 counter runs recorded in
 profiles/traffic.json, and only while the kernel source is the one measured.
+
+``extras`` times the layers beyond the step the same way, one launch each on
+this step's maps: fwd_inverse is the upsampling layer back from the strided
+layer (its channels reversed).  They are not part of ``value``.
 """
 
 from __future__ import annotations
@@ -119,7 +123,7 @@ class Step:
     def kernel_ms(self, stage: str, reps: int = KERNEL_REPS) -> float:
         """Average duration of one single-kernel stage launched `reps` times back to
         back between two HIP events (the queue never drains, so no host gap counts)."""
-        spc, torch, inp = self.spc, self.torch, self.inp
+        spc, inp = self.spc, self.inp
         if self.km is None:
             self.km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         km, ks = self.km, self.ks
@@ -132,15 +136,7 @@ class Step:
             "dinput_strided": lambda: spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n,
                                                          ks["order_in"]),
         }[stage]
-        launch()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            launch()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return self.time_launch(launch, reps)
 
     def run(self, events=None):
         spc, inp = self.spc, self.inp
@@ -178,6 +174,37 @@ class Step:
         mark("dfilter_strided", 0)
         spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"])
         mark("dfilter_strided", 1)
+
+    def extras(self):
+        """The widened layers, each one launch timed like a single-kernel stage:
+        name -> (launch, effective FLOP, algorithmic HBM bytes).  They reuse this
+        step's maps and synthetic tensors of the right shapes (the strided
+        layer's upstream gradient serves as the coarse features)."""
+        spc, torch = self.spc, self.torch
+        ks = self.ks
+        n, m, Ps, K = self.n, self.m, self.Ps, 27
+        cin, cs = self.ws.shape[1], self.ws.shape[2]
+        s = self.x.element_size()
+        if not hasattr(self, "w_inv"):
+            self.w_inv = self.ws.transpose(1, 2).contiguous()  # [K, cs, cin]: upsampling back to cin channels
+        return {
+            "fwd_inverse": (lambda: spc.sparse_inverse_conv_fwd(self.gs, self.w_inv, None, ks["nbr_in"], n,
+                                                                ks["order_in"]),
+                            2 * Ps * cs * cin, m * cs * s + K * n * 4 + K * cs * cin * s + n * cin * s),
+        }
+
+    def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:
+        """Average duration of one launch repeated back to back between two events."""
+        torch = self.torch
+        launch()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
     # effective FLOP and algorithmic HBM bytes per stage (one launch / call)
     def work(self):
@@ -366,6 +393,16 @@ def main():
     roof["avg_launch_ms"] = round(kernel_ms[dom], 4)
     roof["kernel_ms"] = {k: round(v, 4) for k, v in kernel_ms.items()}
 
+    extras = {}
+    for name, (launch, fl, by) in step.extras().items():
+        ms = step.time_launch(launch)
+        t = ms * 1e-3
+        bound = "hbm" if fl / by < ridge else "mfma"
+        ach = by / t / 1e9 if bound == "hbm" else fl / t / 1e12
+        peak = HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dtype]
+        extras[name] = {"kernel_ms": round(ms, 4), "TFLOP/s": round(fl / t / 1e12, 2) if fl else None,
+                        "alg_GB/s": round(by / t / 1e9, 1), "bound": bound, "frac": round(ach / peak, 4)}
+
     kmap_vps = step.n / (stage_ms["kmap_subm"] * 1e-3)
     out = {
         "metric": "effective TFLOP/s of SubMConv3d fwd (occupied pairs) + kmap voxels/s, 1 MI355X",
@@ -387,6 +424,7 @@ def main():
         "kmap_voxels_per_s": round(kmap_vps, 1),
         "stages": stages,
         "roofline": roof,
+        "extras": extras,
     }
     if not args.no_cpu_baseline:
         def stage_flops(name, state):

@@ -150,6 +150,28 @@ spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_in,
                                hipStream_t stream);
 
 /*
+ * Inverse (upsampling) forward, SparseInverseConv3d (spconv USAGE.md, the
+ * layer table and "Using SparseInverseConv for Inverse Sparse Operations"):
+ * the output rows are the INPUT sites of the strided layer whose kernel map
+ * is reused, and
+ *   out[i] = bias + sum_k feats[nbr_in[i*K + k]] @ W[k]   over entries >= 0.
+ * feats [n_coarse, cin] lives on that layer's output sites; weight
+ * [K, cin, cout] is the inverse layer's own; nbr_in [n_fine, K] and order_in
+ * (NULL ok) come from the strided spc_build_kmap; out [n_fine, cout] is
+ * overwritten.  Errors as spc_sparse_conv_fwd.
+ * The backward needs no further entry point; with the same strided map:
+ *   dinput  = spc_conv_bwd_input(dout [n_fine, cout], weight, map = that map's
+ *             nbr [n_coarse, K], map_is_subm = 0, order = its order,
+ *             n_in = n_coarse), i.e. din[o] = sum_k dout[nbr[o*K + k]] @ W[k]^T;
+ *   dfilter = spc_conv_bwd_filter(feats = the coarse features, dout = the fine
+ *             gradient, pair_in and pair_out of that map exchanged).
+ */
+spc_status spc_sparse_inverse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_coarse, int32_t cin,
+                                       const void* weight, int32_t K, int32_t cout, const float* bias,
+                                       const int32_t* nbr_in, const int32_t* order_in, int64_t n_fine,
+                                       void* out, hipStream_t stream);
+
+/*
  * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput
  * and dfilter): din[i] = sum over (k, o) with map_fwd[k][o] = i of
  * dout[o] @ W[k]^T, computed output-stationary over the input rows:

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     make_geom,
     out_shape,
     sparse_conv_fwd,
+    sparse_inverse_conv_fwd,
     subm_conv_fwd,
     version,
 )

@@ -25,7 +25,8 @@ _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4:
            5: "SPC_ERR_WORKSPACE", 6: "SPC_ERR_HIP"}
 
 EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
-           "spc_sparse_conv_fwd", "spc_conv_bwd_input", "spc_conv_bwd_filter_workspace",
+           "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_bwd_input",
+           "spc_conv_bwd_filter_workspace",
            "spc_conv_bwd_filter", "spc_last_error", "spc_version")
 
 
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
                            _SZ, _P],
         "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P],
         "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
+        "spc_sparse_inverse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -243,6 +245,26 @@ def sparse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[to
     st = lib().spc_sparse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,
                                    _ptr(bias), _ptr(nbr_out), _ptr(order), int(n_out), _ptr(out), _stream(dev))
     _check(st, "spc_sparse_conv_fwd")
+    return out
+
+
+def sparse_inverse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                            nbr_in: torch.Tensor, n_fine: int, order_in: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Inverse (upsampling) forward onto the input sites of a strided kernel map
+    (spc_sparse_inverse_conv_fwd): feats [n_coarse, cin] -> [n_fine, cout]."""
+    dev = feats.device
+    _conv_checks(feats, weight, bias, dev)
+    _need(nbr_in, "nbr_in", torch.int32, dev)
+    if order_in is not None:
+        _need(order_in, "order_in", torch.int32, dev)
+    K, cin, cout = weight.shape
+    if out is None:
+        out = torch.empty((n_fine, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_sparse_inverse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K,
+                                           cout, _ptr(bias), _ptr(nbr_in), _ptr(order_in), int(n_fine), _ptr(out),
+                                           _stream(dev))
+    _check(st, "spc_sparse_inverse_conv_fwd")
     return out
 
 

@@ -443,6 +443,21 @@ extern "C" spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, in
     return run_conv(dtype, a, true, stream);
 }
 
+extern "C" spc_status spc_sparse_inverse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_coarse,
+                                                  int32_t cin, const void* weight, int32_t K, int32_t cout,
+                                                  const float* bias, const int32_t* nbr_in, const int32_t* order_in,
+                                                  int64_t n_fine, void* out, hipStream_t stream) {
+    clear_error();
+    spc_status st = check_common(dtype, n_fine, n_coarse, cin, cout, K, feats, weight, bias, out, nbr_in, order_in,
+                                 true);
+    if (st != SPC_OK) return st;
+    // the fine rows gather the coarse rows through the transposed map: the
+    // same output-stationary kernel as the strided forward
+    ConvArgs a{feats, weight, bias, nbr_in, order_in, out, int32_t(n_fine), int32_t(n_coarse), K, cin, cout, cin,
+               cout, 0, 0};
+    return run_conv(dtype, a, true, stream);
+}
+
 extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int64_t n_out, int32_t cout,
                                          const void* weight, int32_t K, int32_t cin, const int32_t* map,
                                          int32_t map_is_subm, const int32_t* order, int64_t n_in, void* din,

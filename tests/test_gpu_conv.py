@@ -181,3 +181,43 @@ def test_many_tiles_with_empty_tiles(dtype, cin, cout):
     assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr), TOL[dtype], "fwd")
     perm = cuda(r.permutation(M).astype(np.int32))
     assert torch.equal(out, spc.sparse_conv_fwd(x, w, b, nbr_mk, M, perm))
+
+
+# ------------------------------------------------ inverse (upsampling) conv
+
+def run_inverse(c, batch, shape, k, s, p, d, t, dtype, ref, what=""):
+    """Inverse forward on a strided map, and its dinput / dfilter / dbias through
+    the existing backward calls (map and pair lists exchanged), vs the oracle."""
+    km = spc.build_kmap(cuda(c), batch, shape, k, s, p, d, subm=False, orders=True)
+    M, N = km["n_out"], c.shape[0]
+    print(f"inverse conv {what} N={N} M={M} k={k} s={s} {tuple(t['weight'].shape)} {dtype}", flush=True)
+    x, w, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["grad"])
+    b = cuda(t["bias"]) if t.get("bias") is not None else None
+    out = spc.sparse_inverse_conv_fwd(x, w, b, km["nbr_in"], N, km["order_in"])
+    assert_close(out, OC.inverse_conv_fwd(t["feats"], t["weight"], t["bias"], ref["nbr_out"], N), TOL[dtype], "fwd")
+    assert torch.equal(out, spc.sparse_inverse_conv_fwd(x, w, b, km["nbr_in"], N))  # order never changes a result
+    din = spc.conv_bwd_input(g, w, km["nbr"], False, M, km["order"])
+    assert_close(din, OC.inverse_conv_bwd_input(t["grad"], t["weight"], ref["nbr_out"], M), TOL[dtype], "din")
+    dw, db = spc.conv_bwd_filter(x, g, k ** 3, km["pair_ptr"], km["pair_out"], km["pair_in"], want_dbias=True)
+    assert_close(dw, OC.inverse_conv_bwd_filter(t["feats"], t["grad"], ref["nbr_out"]), TOL_DW, "dw")
+    assert_close(db, OC.conv_bwd_bias(t["grad"]), TOL_DW, "dbias")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,k,s,p,d,cin,cout", [
+    ((12, 14, 10), 3, 2, 1, 1, 32, 16), ((15, 13, 11), 2, 2, 0, 1, 16, 48), ((11, 11, 11), 3, 1, 0, 2, 64, 32),
+])
+def test_inverse_small(dtype, shape, k, s, p, d, cin, cout):
+    c = W.tiny_grid(W.rng(45 + k + s), min(shape), 0.25, 2)
+    ref = O.strided_kmap(c, 2, shape, k, s, p, d)
+    # coarse features [M, cin], the inverse layer's weight [K, cin, cout], a fine gradient [N, cout]
+    t = W.small_layer(56, ref["out_coords"], cin, cout, k ** 3, dtype, n_out=c.shape[0])
+    run_inverse(c, 2, shape, k, s, p, d, t, dtype, ref)
+
+
+def test_workload_inverse_lidar_fp16():
+    # the upsampling back from the strided lidar layer: 128 coarse channels -> 64
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    ref = O.strided_kmap(w.coords, w.batch, w.shape, 3, 2, 1, 1)
+    t = W.small_layer(57, ref["out_coords"], 128, 64, 27, w.dtype, bias=False, n_out=w.n)
+    run_inverse(w.coords, w.batch, w.shape, 3, 2, 1, 1, t, w.dtype, ref, what=w.name)
