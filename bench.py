@@ -24,14 +24,18 @@ pairs), divided by the step time.  The kernel-map rate is reported as voxels/s
 (N over the kmap_subm time).  Every stage is timed with HIP events on the
 stream the library launches on.  The roofline is given for the single-kernel
 stage with the longest kernel: each such kernel is also launched back to back
-between two HIP events (the step's stage timings include host gaps, e.g. after
+between two HIP events, behind a few ms of queued fills so that no host time
+between launches counts (the step's stage timings include host gaps, e.g. after
 the strided kernel map's one synchronisation), and that average is its launch
 duration.  Its HBM traffic comes from the rocprofv3 counter runs recorded in
 profiles/traffic.json, and only while the kernel source is the one measured.
 
 ``extras`` times the layers beyond the step the same way, one launch each on
 this step's maps: fwd_inverse is the upsampling layer back from the strided
-layer (its channels reversed).  They are not part of ``value``.
+layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
+residual block relu(conv(x) + x) in one kernel, and ..._unfused the same
+through the plain forward plus torch's add and relu (three launches, timed
+together).  They are not part of ``value``.
 """
 
 from __future__ import annotations
@@ -51,6 +55,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "dinput_strided")
 KERNEL_REPS = 20         # back-to-back launches per single-kernel stage for its duration
+BUSY_FILLS = 12          # 1 GiB fills queued ahead of them (~2-3 ms of GPU time)
 CPU_MIN_S = 10.0         # the oracle repeats whole steps for at least this long (within --cpu-budget)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -187,17 +192,37 @@ class Step:
         s = self.x.element_size()
         if not hasattr(self, "w_inv"):
             self.w_inv = self.ws.transpose(1, 2).contiguous()  # [K, cs, cin]: upsampling back to cin channels
+        if self.km is None:
+            self.km = spc.build_kmap(self.coords, self.inp["batch"], self.inp["shape"], 3, orders=True)
+        km, P, c1 = self.km, self.P, self.w3.shape[2]
+
+        def unfused():  # the same layer as three launches: conv, then torch's add and relu
+            y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
+            y.add_(self.x).relu_()
+
+        sub_bytes = n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s
         return {
             "fwd_inverse": (lambda: spc.sparse_inverse_conv_fwd(self.gs, self.w_inv, None, ks["nbr_in"], n,
                                                                 ks["order_in"]),
                             2 * Ps * cs * cin, m * cs * s + K * n * 4 + K * cs * cin * s + n * cin * s),
+            # relu(conv(x) + x): the residual read is one more [n, c1] pass
+            "fwd_subm_add_relu_fused": (lambda: spc.conv_fwd_fused(self.x, self.w3, None, km["nbr"], n, km["order"],
+                                                                   residual=self.x, relu=True),
+                                        2 * P * cin * c1, sub_bytes + n * c1 * s),
+            "fwd_subm_add_relu_unfused": (unfused, 2 * P * cin * c1, sub_bytes + n * c1 * s),
         }
 
     def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:
-        """Average duration of one launch repeated back to back between two events."""
+        """Average duration of one launch repeated back to back between two events.
+        A few ms of fills are queued first, so the host has enqueued every launch
+        before the first one starts and the host's per-call cost is not timed."""
         torch = self.torch
         launch()
         torch.cuda.synchronize()
+        if not hasattr(self, "busy"):
+            self.busy = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        for _ in range(BUSY_FILLS):
+            self.busy.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):

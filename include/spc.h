@@ -172,6 +172,26 @@ spc_status spc_sparse_inverse_conv_fwd(spc_dtype dtype, const void* feats, int64
                                        void* out, hipStream_t stream);
 
 /*
+ * Fused forward (the implicit-GEMM call on spconv TENSORRT_INT8_GUIDE.md, "Call
+ * Spconv Implicit GEMM with Calculated Scales and Bias": a bias, an added
+ * output and a ReLU activation fused into the convolution for a
+ * conv-add-relu layer).  Any of the forwards above, with
+ *   out[r] = act(bias + residual[r] + sum_k feats[map[r*K + k]] @ W[k])
+ * all in fp32 with one rounding to the storage dtype; act is ReLU when
+ * relu != 0 (NaN passes through), else the identity.
+ * map [n_rows, K] is the submanifold nbr (n_src == n_rows), the strided nbr
+ * (n_src = input rows) or the strided nbr_in for the inverse layer (n_src =
+ * coarse rows); NULL with K == 1 is the identity (n_src == n_rows).  order as
+ * for that map (NULL ok).  residual [n_rows, cout] in the features' dtype,
+ * NULL for none; it may be the same buffer as out (in-place add).  Other
+ * arguments and errors as spc_subm_conv_fwd.
+ */
+spc_status spc_conv_fwd_fused(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                              const void* weight, int32_t K, int32_t cout, const float* bias,
+                              const int32_t* map, const int32_t* order, int64_t n_rows,
+                              const void* residual, int32_t relu, void* out, hipStream_t stream);
+
+/*
  * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput
  * and dfilter): din[i] = sum over (k, o) with map_fwd[k][o] = i of
  * dout[o] @ W[k]^T, computed output-stationary over the input rows:

@@ -87,6 +87,24 @@ def conv_bwd_bias(dout) -> np.ndarray:
     return f64(dout).sum(axis=0)
 
 
+def conv_fwd_fused(feats, weight, bias, nbr, residual=None, relu=False) -> np.ndarray:
+    """The fused conv-add-relu layer of the implicit-GEMM call on spconv
+    TENSORRT_INT8_GUIDE.md ("Call Spconv Implicit GEMM with Calculated Scales
+    and Bias"): ``act(bias + residual + sum_k feats[nbr[k][o]] @ W[k])`` with
+    act = ReLU (``max(v, 0)``) or the identity, fp64."""
+    x, w = f64(feats), f64(weight)
+    nbr = np.asarray(nbr)
+    out = np.zeros((nbr.shape[1], w.shape[2]), dtype=np.float64)
+    if bias is not None:
+        out += f64(bias)[None, :]
+    if residual is not None:
+        out += f64(residual)
+    for k in range(nbr.shape[0]):
+        o = np.nonzero(nbr[k] >= 0)[0]
+        out[o] += x[nbr[k][o]] @ w[k]
+    return np.maximum(out, 0.0) if relu else out
+
+
 # ------------------------------------------------ inverse (upsampling) conv
 
 # SparseInverseConv3d (spconv USAGE.md, the layer table and "Using

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     build_kmap,
     conv_bwd_filter,
     conv_bwd_input,
+    conv_fwd_fused,
     lib,
     make_geom,
     out_shape,

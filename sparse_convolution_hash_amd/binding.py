@@ -25,7 +25,7 @@ _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4:
            5: "SPC_ERR_WORKSPACE", 6: "SPC_ERR_HIP"}
 
 EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
-           "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_bwd_input",
+           "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
            "spc_conv_bwd_filter", "spc_last_error", "spc_version")
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P],
         "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_sparse_inverse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
+        "spc_conv_fwd_fused": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P],
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -265,6 +266,31 @@ def sparse_inverse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Opt
                                            cout, _ptr(bias), _ptr(nbr_in), _ptr(order_in), int(n_fine), _ptr(out),
                                            _stream(dev))
     _check(st, "spc_sparse_inverse_conv_fwd")
+    return out
+
+
+def conv_fwd_fused(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                   map_: Optional[torch.Tensor], n_rows: int, order: Optional[torch.Tensor] = None,
+                   residual: Optional[torch.Tensor] = None, relu: bool = False,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward over any map with the fused bias + residual + ReLU epilogue
+    (spc_conv_fwd_fused); ``out`` may be ``residual`` itself."""
+    dev = feats.device
+    _conv_checks(feats, weight, bias, dev)
+    for t, nm in ((map_, "map"), (order, "order")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
+    K, cin, cout = weight.shape
+    if residual is not None:
+        _need(residual, "residual", feats.dtype, dev)
+        if tuple(residual.shape) != (n_rows, cout):
+            raise ValueError(f"residual must be [{n_rows}, {cout}], got {tuple(residual.shape)}")
+    if out is None:
+        out = torch.empty((n_rows, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_conv_fwd_fused(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,
+                                  _ptr(bias), _ptr(map_), _ptr(order), int(n_rows), _ptr(residual),
+                                  1 if relu else 0, _ptr(out), _stream(dev))
+    _check(st, "spc_conv_fwd_fused")
     return out
 
 

@@ -148,6 +148,29 @@ __device__ __forceinline__ void store4<F16>(void* p, f32x4_t v) {
     *reinterpret_cast<uint2*>(p) = w;
 }
 
+// Loads four consecutive elements of the element type as fp32 (exact).
+template <typename TT>
+__device__ __forceinline__ f32x4_t load4(const void* p);
+
+template <>
+__device__ __forceinline__ f32x4_t load4<F32>(const void* p) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+}
+
+template <>
+__device__ __forceinline__ f32x4_t load4<BF16>(const void* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                   __uint_as_float(w.y & 0xffff0000u)};
+}
+
+template <>
+__device__ __forceinline__ f32x4_t load4<F16>(const void* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    auto h = [](uint32_t b) { return float(__builtin_bit_cast(_Float16, uint16_t(b))); };
+    return f32x4_t{h(w.x & 0xffffu), h(w.x >> 16), h(w.y & 0xffffu), h(w.y >> 16)};
+}
+
 inline int dtype_size(spc_dtype d) { return d == SPC_F32 ? 4 : 2; }
 
 }  // namespace spc

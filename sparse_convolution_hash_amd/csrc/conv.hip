@@ -45,6 +45,8 @@ struct ConvArgs {
     int32_t cin, cout;   // weight dims
     int32_t w_rev;       // slab of offset k is W[K-1-k]
     int32_t kch;         // 16-byte chunks along CK, padded to a multiple of 4
+    const void* res;     // residual [n_rows, CN] added before the activation, or NULL (may alias y)
+    int32_t relu;        // ReLU on the final fp32 value
 };
 
 // LDS slab layout: chunk row kb (16 bytes of CK per output channel) has BN
@@ -329,7 +331,11 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
     // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
     // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels
+    // (bias, then the residual and the ReLU of a fused layer, all on the fp32
+    // value before its one rounding; a residual aliasing y is read by the lane
+    // that then overwrites it)
     S* y = static_cast<S*>(a.y);
+    const S* res = static_cast<const S*>(a.res);
     f32x4_t bv[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(sbias + nb * 16 + lg * 4);
@@ -337,11 +343,21 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
         const int row = rsrc[(wave * RB + rb) * 16 + lr];
         if (row < 0) continue;
+        f32x4_t v[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int ch = col0 + nb * 16 + lg * 4;
-            store4<TT>(y + int64_t(row) * a.CN + ch, acc[rb][nb] + bv[nb]);
+        for (int nb = 0; nb < NB; ++nb) v[nb] = acc[rb][nb] + bv[nb];
+        if (res) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) v[nb] += load4<TT>(res + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4);
         }
+        if (a.relu) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[nb][e] = v[nb][e] < 0.f ? 0.f : v[nb][e];  // NaN stays NaN
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) store4<TT>(y + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4, v[nb]);
     }
 }
 
@@ -455,6 +471,23 @@ extern "C" spc_status spc_sparse_inverse_conv_fwd(spc_dtype dtype, const void* f
     // same output-stationary kernel as the strided forward
     ConvArgs a{feats, weight, bias, nbr_in, order_in, out, int32_t(n_fine), int32_t(n_coarse), K, cin, cout, cin,
                cout, 0, 0};
+    return run_conv(dtype, a, true, stream);
+}
+
+extern "C" spc_status spc_conv_fwd_fused(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                                         const void* weight, int32_t K, int32_t cout, const float* bias,
+                                         const int32_t* map, const int32_t* order, int64_t n_rows,
+                                         const void* residual, int32_t relu, void* out, hipStream_t stream) {
+    clear_error();
+    const bool identity = K == 1 && map == nullptr;
+    if (identity && n_src != n_rows)
+        return fail(SPC_ERR_ARG, "an identity map needs n_src == n_rows (%lld vs %lld)", (long long)n_src,
+                    (long long)n_rows);
+    spc_status st = check_common(dtype, n_rows, n_src, cin, cout, K, feats, weight, bias, out, map, order, !identity);
+    if (st != SPC_OK) return st;
+    if (residual && !aligned16(residual)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
+    ConvArgs a{feats, weight, bias, identity ? nullptr : map, identity ? nullptr : order, out, int32_t(n_rows),
+               int32_t(n_src), K, cin, cout, cin, cout, 0, 0, residual, relu ? 1 : 0};
     return run_conv(dtype, a, true, stream);
 }
 

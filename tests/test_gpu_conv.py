@@ -221,3 +221,61 @@ def test_workload_inverse_lidar_fp16():
     ref = O.strided_kmap(w.coords, w.batch, w.shape, 3, 2, 1, 1)
     t = W.small_layer(57, ref["out_coords"], 128, 64, 27, w.dtype, bias=False, n_out=w.n)
     run_inverse(w.coords, w.batch, w.shape, 3, 2, 1, 1, t, w.dtype, ref, what=w.name)
+
+
+# ------------------------------------------------ fused conv-add-relu epilogue
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind", ["subm", "strided", "inverse", "k1"])
+def test_fused_epilogue(dtype, kind):
+    shape = (12, 14, 10)
+    c = W.tiny_grid(W.rng(160), min(shape), 0.3, 2)
+    cin, cout = 32, 48
+    if kind in ("subm", "k1"):
+        k = 3 if kind == "subm" else 1
+        km = spc.build_kmap(cuda(c), 2, shape, k, orders=True) if k > 1 else None
+        nbr = O.subm_kmap(c, shape, k) if k > 1 else np.arange(c.shape[0])[None]
+        src_n, rows = c.shape[0], c.shape[0]
+        m, order = (km["nbr"], km["order"]) if k > 1 else (None, None)
+    else:
+        k = 3
+        km = spc.build_kmap(cuda(c), 2, shape, 3, 2, 1, 1, subm=False, orders=True)
+        ref = O.strided_kmap(c, 2, shape, 3, 2, 1, 1)
+        M = ref["out_coords"].shape[0]
+        if kind == "strided":
+            nbr, src_n, rows, m, order = ref["nbr_out"], c.shape[0], M, km["nbr"], km["order"]
+        else:
+            nbr, src_n, rows, m, order = ref["nbr_in"], M, c.shape[0], km["nbr_in"], km["order_in"]
+    t = W.small_layer(161, np.zeros((src_n, 4), np.int32), cin, cout, k ** 3, dtype)
+    res = W.small_layer(162, np.zeros((rows, 4), np.int32), cout, cout, 1, dtype)["feats"]
+    x, w, b, r = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"]), cuda(res)
+    print(f"fused {kind} rows={rows} src={src_n} {dtype}", flush=True)
+    for relu in (False, True):
+        out = spc.conv_fwd_fused(x, w, b, m, rows, order, residual=r, relu=relu)
+        assert_close(out, OC.conv_fwd_fused(t["feats"], t["weight"], t["bias"], nbr, res, relu), TOL[dtype],
+                     f"fused relu={relu}")
+        if relu:
+            assert (out.float() >= 0).all()
+    # without residual and activation it is the plain forward, bit for bit
+    plain = spc.conv_fwd_fused(x, w, b, m, rows, order)
+    if kind in ("subm", "k1"):
+        assert torch.equal(plain, spc.subm_conv_fwd(x, w, b, m, order))
+    elif kind == "strided":
+        assert torch.equal(plain, spc.sparse_conv_fwd(x, w, b, m, rows, order))
+    else:
+        assert torch.equal(plain, spc.sparse_inverse_conv_fwd(x, w, b, m, rows, order))
+    # in place: the residual buffer is also the output
+    buf = r.clone()
+    spc.conv_fwd_fused(x, w, b, m, rows, order, residual=buf, relu=True, out=buf)
+    assert torch.equal(buf, spc.conv_fwd_fused(x, w, b, m, rows, order, residual=r, relu=True))
+
+
+def test_workload_fused_lidar_fp16():
+    # the submanifold lidar layer as a residual block: relu(conv(x) + x)
+    w = W.workload("subm_k3_f16_lidar120k")
+    km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, orders=True)
+    nbr_ref = O.subm_kmap(w.coords, w.shape, 3)
+    x, wt = cuda(w.feats), cuda(w.weight)
+    print(f"{w.name} fused n={w.n}", flush=True)
+    out = spc.conv_fwd_fused(x, wt, None, km["nbr"], w.n, km["order"], residual=x, relu=True)
+    assert_close(out, OC.conv_fwd_fused(w.feats, w.weight, None, nbr_ref, w.feats, True), TOL[w.dtype], "fused")

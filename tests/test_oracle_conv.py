@@ -225,3 +225,31 @@ def test_planted_inverse_offset_reversal_is_caught(monkeypatch):
     dense = dense_conv_transpose(res["out_coords"], t["feats"], t["weight"], t["bias"], 2,
                                  O.out_shape((7, 8, 6), 3, 2, 1, 1), (7, 8, 6), 3, 2, 1)
     assert not np.allclose(got, sample(dense, c).numpy(), rtol=1e-10, atol=1e-10)
+
+
+# ------------------------------------------------ fused conv-add-relu epilogue
+
+def test_fused_single_voxel_by_hand():
+    # one voxel: only the centre tap W[13] acts.  x @ W[13] = [-3, -2, -1];
+    # + bias = [-2.5, -6, 0]; + residual = [1.5, -5, 5]; ReLU -> [1.5, 0, 5]
+    # (ReLU before the add would give [4, 1, 5])
+    c = np.array([[0, 1, 1, 1]], np.int32)
+    nbr = O.subm_kmap(c, (3, 3, 3), 3)
+    w = np.zeros((27, 2, 3))
+    w[13] = [[1, 0, -1], [2, 1, 0]]
+    x = np.array([[1.0, -2.0]])
+    got = C.conv_fwd_fused(x, w, np.array([0.5, -4.0, 1.0]), nbr, np.array([[4.0, 1.0, 5.0]]), relu=True)
+    np.testing.assert_array_equal(got, [[1.5, 0.0, 5.0]])
+    got = C.conv_fwd_fused(x, w, np.array([0.5, -4.0, 1.0]), nbr, np.array([[4.0, 1.0, 5.0]]), relu=False)
+    np.testing.assert_array_equal(got, [[1.5, -5.0, 5.0]])
+
+
+def test_fused_equals_dense_conv3d_add_relu():
+    c = W.tiny_grid(W.rng(150), 7, 0.3, 1)
+    t = _layer(150, c, 4, 5, 27)
+    r = _layer(151, c, 5, 5, 27)["feats"]  # a residual [N, 5]
+    nbr = O.subm_kmap(c, (7, 7, 7), 3)
+    dense = dense_conv(c, t["feats"], t["weight"], t["bias"], 1, (7, 7, 7), 3)
+    ref = torch.relu(sample(dense, c) + torch.as_tensor(r.numpy(), dtype=torch.float64)).numpy()
+    got = C.conv_fwd_fused(t["feats"], t["weight"], t["bias"], nbr, r, relu=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
