@@ -11,9 +11,11 @@ never calls it and has no CPU fallback.  It shares no code with the HIP path.
 * ``conv``  -- forward, dinput, dfilter and dbias as per-offset fp64 sums, and
   the inverse (upsampling) convolution on a saved strided map with its
   dinput and dfilter.
+* ``pool``  -- sparse max pooling over a strided map, forward (max and winning
+  offset) and backward.
 
 Every function cites the passage it follows.  Pins that tie it to the pages
 and to mathematics live in ``tests/test_oracle_*.py``.
 """
 
-from . import conv, kmap  # noqa: F401
+from . import conv, kmap, pool  # noqa: F401

@@ -7,11 +7,11 @@ import torch
 import torch.nn.functional as F
 
 
-def densify(coords, values, batch, shape):
-    """[N, C] values at (b, z, y, x) rows -> float64 [B, C, Z, Y, X]."""
+def densify(coords, values, batch, shape, fill=0.0):
+    """[N, C] values at (b, z, y, x) rows -> float64 [B, C, Z, Y, X], ``fill`` elsewhere."""
     v = torch.as_tensor(np.asarray(values), dtype=torch.float64)
     C = v.shape[1]
-    d = torch.zeros((batch, C) + tuple(shape), dtype=torch.float64)
+    d = torch.full((batch, C) + tuple(shape), fill, dtype=torch.float64)
     c = torch.as_tensor(np.asarray(coords, dtype=np.int64))
     if c.shape[0]:
         d[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]] = v
