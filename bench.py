@@ -35,7 +35,8 @@ this step's maps: fwd_inverse is the upsampling layer back from the strided
 layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
 residual block relu(conv(x) + x) in one kernel, and ..._unfused the same
 through the plain forward plus torch's add and relu (three launches, timed
-together).  They are not part of ``value``.
+together); maxpool_fwd / maxpool_bwd pool x over the strided layer's map
+(3^3, stride 2).  They are not part of ``value``.
 """
 
 from __future__ import annotations
@@ -192,6 +193,8 @@ class Step:
         s = self.x.element_size()
         if not hasattr(self, "w_inv"):
             self.w_inv = self.ws.transpose(1, 2).contiguous()  # [K, cs, cin]: upsampling back to cin channels
+            self.pool_y, self.pool_a = spc.sparse_maxpool_fwd(self.x, ks["nbr"], m)
+            self.pool_g = self.gs[:, :cin].contiguous()  # an upstream gradient of the pooled shape
         if self.km is None:
             self.km = spc.build_kmap(self.coords, self.inp["batch"], self.inp["shape"], 3, orders=True)
         km, P, c1 = self.km, self.P, self.w3.shape[2]
@@ -210,6 +213,12 @@ class Step:
                                                                    residual=self.x, relu=True),
                                         2 * P * cin * c1, sub_bytes + n * c1 * s),
             "fwd_subm_add_relu_unfused": (unfused, 2 * P * cin * c1, sub_bytes + n * c1 * s),
+            # 3^3 stride-2 max pooling of x on the strided layer's map; the bytes
+            # count the map, each input and output row once, and the winner bytes
+            "maxpool_fwd": (lambda: spc.sparse_maxpool_fwd(self.x, ks["nbr"], m, out=self.pool_y, argk=self.pool_a),
+                            0, m * K * 4 + n * cin * s + m * cin * s + m * cin),
+            "maxpool_bwd": (lambda: spc.sparse_maxpool_bwd(self.pool_g, self.pool_a, ks["nbr_in"], n),
+                            0, n * K * 4 + m * cin * s + m * cin + n * cin * s),
         }
 
     def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:

@@ -226,6 +226,35 @@ spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in,
                                const int32_t* pair_out, float* dw, float* dbias,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Sparse max pooling, forward (SparseMaxPool3d, spconv USAGE.md layer table:
+ * downsampling whose dense version is nn.MaxPool3d, on the kernel map of a
+ * strided layer with the pool's kernel size, stride and padding):
+ *   out[o][c]  = max over k with nbr_out[o*K + k] >= 0 of feats[nbr_out[o*K + k]][c]
+ *   argk[o][c] = the smallest such k reaching that maximum (ties go to the
+ *                first offset), 255 when row o has no input (out is then 0).
+ * feats [n_in, C], nbr_out [n_out, K] (a strided spc_build_kmap's nbr), out
+ * [n_out, C] in the features' dtype (exact: a copy of the winning value),
+ * argk uint8 [n_out, C] (NULL ok; the backward needs it).  C a positive
+ * multiple of 16, 1 <= K <= 254.  NaN inputs are outside the contract.
+ * SPC_ERR_UNSUPPORTED / SPC_ERR_ARG as the convolutions.
+ */
+spc_status spc_sparse_maxpool_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t C,
+                                  const int32_t* nbr_out, int32_t K, int64_t n_out, void* out,
+                                  uint8_t* argk, hipStream_t stream);
+
+/*
+ * Sparse max pooling, backward: each output's gradient goes, per channel, to
+ * the input that won the maximum,
+ *   din[i][c] = sum over k with o = nbr_in[i*K + k] >= 0 and argk[o][c] == k of dout[o][c],
+ * summed in fp32 in offset order and rounded once (input-stationary over the
+ * same kernel map's nbr_in [n_in, K]; no atomics, run-to-run identical).
+ * dout [n_out, C], argk from spc_sparse_maxpool_fwd, din [n_in, C] overwritten.
+ */
+spc_status spc_sparse_maxpool_bwd(spc_dtype dtype, const void* dout, int64_t n_out, int32_t C,
+                                  const uint8_t* argk, const int32_t* nbr_in, int32_t K, int64_t n_in,
+                                  void* din, hipStream_t stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* spc_last_error(void);
 

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     out_shape,
     sparse_conv_fwd,
     sparse_inverse_conv_fwd,
+    sparse_maxpool_bwd,
+    sparse_maxpool_fwd,
     subm_conv_fwd,
     version,
 )

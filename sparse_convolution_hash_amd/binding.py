@@ -27,7 +27,8 @@ _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4:
 EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
            "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
-           "spc_conv_bwd_filter", "spc_last_error", "spc_version")
+           "spc_conv_bwd_filter", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd", "spc_last_error",
+           "spc_version")
 
 
 class SpcError(RuntimeError):
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "spc_sparse_maxpool_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I64, _P, _P, _P],
+        "spc_sparse_maxpool_bwd": [_I32, _P, _I64, _I32, _P, _P, _I32, _I64, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -345,3 +348,39 @@ def conv_bwd_filter(feats: torch.Tensor, dout: torch.Tensor, K: int, pair_ptr: O
                                    _ptr(dw), _ptr(db), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "spc_conv_bwd_filter")
     return dw, db
+
+
+def sparse_maxpool_fwd(feats: torch.Tensor, nbr_out: torch.Tensor, n_out: int, want_argk: bool = True,
+                       out: Optional[torch.Tensor] = None, argk: Optional[torch.Tensor] = None):
+    """Channel-wise max over each output's map row (spc_sparse_maxpool_fwd):
+    returns ``(out [n_out, C], argk uint8 [n_out, C] or None)``."""
+    dev = feats.device
+    _need(feats, "feats", feats.dtype, dev)
+    _need(nbr_out, "nbr_out", torch.int32, dev)
+    C = feats.shape[1]
+    K = nbr_out.shape[1] if nbr_out.dim() == 2 else 0
+    if out is None:
+        out = torch.empty((n_out, C), dtype=feats.dtype, device=dev)
+    if want_argk and argk is None:
+        argk = torch.empty((n_out, C), dtype=torch.uint8, device=dev)
+    st = lib().spc_sparse_maxpool_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], C, _ptr(nbr_out), K,
+                                      int(n_out), _ptr(out), _ptr(argk if want_argk else None), _stream(dev))
+    _check(st, "spc_sparse_maxpool_fwd")
+    return out, (argk if want_argk else None)
+
+
+def sparse_maxpool_bwd(dout: torch.Tensor, argk: torch.Tensor, nbr_in: torch.Tensor, n_in: int,
+                       din: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the pooled features routed to the winning inputs (spc_sparse_maxpool_bwd)."""
+    dev = dout.device
+    _need(dout, "dout", dout.dtype, dev)
+    _need(argk, "argk", torch.uint8, dev)
+    _need(nbr_in, "nbr_in", torch.int32, dev)
+    C = dout.shape[1]
+    K = nbr_in.shape[1] if nbr_in.dim() == 2 else 0
+    if din is None:
+        din = torch.empty((n_in, C), dtype=dout.dtype, device=dev)
+    st = lib().spc_sparse_maxpool_bwd(_DTYPES[dout.dtype], _ptr(dout), dout.shape[0], C, _ptr(argk), _ptr(nbr_in),
+                                      K, int(n_in), _ptr(din), _stream(dev))
+    _check(st, "spc_sparse_maxpool_bwd")
+    return din
