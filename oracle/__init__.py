@@ -13,9 +13,11 @@ never calls it and has no CPU fallback.  It shares no code with the HIP path.
   dinput and dfilter.
 * ``pool``  -- sparse max pooling over a strided map, forward (max and winning
   offset) and backward.
+* ``voxel`` -- point-cloud voxelisation (points to voxels, coordinates, counts
+  and per-point voxel ids) by one sequential pass over the points.
 
 Every function cites the passage it follows.  Pins that tie it to the pages
 and to mathematics live in ``tests/test_oracle_*.py``.
 """
 
-from . import conv, kmap, pool  # noqa: F401
+from . import conv, kmap, pool, voxel  # noqa: F401
