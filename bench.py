@@ -36,7 +36,8 @@ layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
 residual block relu(conv(x) + x) in one kernel, and ..._unfused the same
 through the plain forward plus torch's add and relu (three launches, timed
 together); maxpool_fwd / maxpool_bwd pool x over the strided layer's map
-(3^3, stride 2).  They are not part of ``value``.
+(3^3, stride 2); point_to_voxel voxelises a 200k-point synthetic sweep (one
+call, its host synchronisation included).  They are not part of ``value``.
 """
 
 from __future__ import annotations
@@ -186,6 +187,7 @@ class Step:
         name -> (launch, effective FLOP, algorithmic HBM bytes).  They reuse this
         step's maps and synthetic tensors of the right shapes (the strided
         layer's upstream gradient serves as the coarse features)."""
+        import workloads as W
         spc, torch = self.spc, self.torch
         ks = self.ks
         n, m, Ps, K = self.n, self.m, self.Ps, 27
@@ -195,6 +197,8 @@ class Step:
             self.w_inv = self.ws.transpose(1, 2).contiguous()  # [K, cs, cin]: upsampling back to cin channels
             self.pool_y, self.pool_a = spc.sparse_maxpool_fwd(self.x, ks["nbr"], m)
             self.pool_g = self.gs[:, :cin].contiguous()  # an upstream gradient of the pooled shape
+            self.pts = torch.from_numpy(W.lidar_points(W.rng(236))).to(self.dev)
+        vc = W.LIDAR_VOXEL
         if self.km is None:
             self.km = spc.build_kmap(self.coords, self.inp["batch"], self.inp["shape"], 3, orders=True)
         km, P, c1 = self.km, self.P, self.w3.shape[2]
@@ -219,6 +223,13 @@ class Step:
                             0, m * K * 4 + n * cin * s + m * cin * s + m * cin),
             "maxpool_bwd": (lambda: spc.sparse_maxpool_bwd(self.pool_g, self.pool_a, ks["nbr_in"], n),
                             0, n * K * 4 + m * cin * s + m * cin + n * cin * s),
+            # a 200k-point synthetic sweep into 0.1 x 0.1 x 0.2 m voxels (one call,
+            # including its one host synchronisation); bytes: the points read, the
+            # voxel block, coordinates, counts and point ids written
+            "point_to_voxel": (lambda: spc.point_to_voxel(self.pts, vc["vsize_xyz"], vc["range_xyz"],
+                                                          vc["max_voxels"], vc["max_points"], True, with_id=True),
+                               0, self.pts.numel() * 4 + vc["max_voxels"] * (vc["max_points"] * self.pts.shape[1] * 4
+                                                                            + 16) + self.pts.shape[0] * 4),
         }
 
     def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:

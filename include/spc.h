@@ -255,6 +255,48 @@ spc_status spc_sparse_maxpool_bwd(spc_dtype dtype, const void* dout, int64_t n_o
                                   const uint8_t* argk, const int32_t* nbr_in, int32_t K, int64_t n_in,
                                   void* din, hipStream_t stream);
 
+/* Host only.  Workspace bytes spc_point_to_voxel needs. */
+spc_status spc_point_to_voxel_workspace(int64_t n_points, int32_t n_features, int64_t max_voxels,
+                                        int32_t max_points, size_t* bytes);
+
+/*
+ * Point cloud to voxels (spconv.pytorch.utils.PointToVoxel, spconv USAGE.md:
+ * "spconv.pytorch.utils API Reference" and the PointToVoxel example).
+ * points [n_points, n_features] fp32 with x, y, z first (3 <= n_features <= 64);
+ * vsize_xyz[3] and range_xyz[6] = {x_min, y_min, z_min, x_max, y_max, z_max}
+ * are HOST arrays.  The grid has round((max - min) / vsize) voxels per axis
+ * (at most 2^32 - 1 cells); a point's voxel is floor((p - min) / vsize) in
+ * fp32, and it is inside iff that is within the grid on every axis.
+ * Voxels are numbered in order of their first point; each keeps its first
+ * max_points points in point order; once max_voxels voxels exist, points of
+ * further voxels are dropped.  Outputs, first *n_voxels rows valid:
+ *   voxels      fp32 [max_voxels, max_points, n_features]: the stored points,
+ *               then (empty_mean != 0) the mean of the voxel's stored points
+ *               in every unused slot, else zeros;
+ *   coords      int32 [max_voxels, 3], (z, y, x) voxel coordinates, no batch;
+ *   num_points  int32 [max_voxels], points stored in each voxel;
+ *   pc_voxel_id int32 [n_points] (NULL ok): the voxel holding each point, -1
+ *               when it lies outside or found no room;
+ *   *n_voxels   (host) the number of voxels.
+ * ws: spc_point_to_voxel_workspace bytes, 16-byte aligned.  Synchronises the
+ * stream once, to return *n_voxels; every result is run-to-run identical.
+ */
+spc_status spc_point_to_voxel(const float* points, int64_t n_points, int32_t n_features,
+                              const float* vsize_xyz, const float* range_xyz, int64_t max_voxels,
+                              int32_t max_points, int32_t empty_mean, float* voxels, int32_t* coords,
+                              int32_t* num_points, int32_t* pc_voxel_id, int64_t* n_voxels,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-point features from per-voxel ones (spconv.pytorch.utils
+ * gather_features_by_pc_voxel_id, same page): out[i] = seg_features[id[i]],
+ * zeros where pc_voxel_id[i] is outside [0, n_voxels).  seg_features
+ * [n_voxels, C], out [n_points, C], C a positive multiple of 16.
+ */
+spc_status spc_gather_by_voxel_id(spc_dtype dtype, const void* seg_features, int64_t n_voxels, int32_t C,
+                                  const int32_t* pc_voxel_id, int64_t n_points, void* out,
+                                  hipStream_t stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* spc_last_error(void);
 

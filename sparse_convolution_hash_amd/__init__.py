@@ -11,9 +11,11 @@ from .binding import (  # noqa: F401
     conv_bwd_filter,
     conv_bwd_input,
     conv_fwd_fused,
+    gather_by_voxel_id,
     lib,
     make_geom,
     out_shape,
+    point_to_voxel,
     sparse_conv_fwd,
     sparse_inverse_conv_fwd,
     sparse_maxpool_bwd,

@@ -27,7 +27,8 @@ _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4:
 EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
            "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
-           "spc_conv_bwd_filter", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd", "spc_last_error",
+           "spc_conv_bwd_filter", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
+           "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_last_error",
            "spc_version")
 
 
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
         "spc_sparse_maxpool_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I64, _P, _P, _P],
         "spc_sparse_maxpool_bwd": [_I32, _P, _I64, _I32, _P, _P, _I32, _I64, _P, _P],
+        "spc_point_to_voxel_workspace": [_I64, _I32, _I64, _I32, ctypes.POINTER(_SZ)],
+        "spc_point_to_voxel": [_P, _I64, _I32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P,
+                               ctypes.POINTER(ctypes.c_int64), _P, _SZ, _P],
+        "spc_gather_by_voxel_id": [_I32, _P, _I64, _I32, _P, _I64, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -384,3 +389,48 @@ def sparse_maxpool_bwd(dout: torch.Tensor, argk: torch.Tensor, nbr_in: torch.Ten
                                       K, int(n_in), _ptr(din), _stream(dev))
     _check(st, "spc_sparse_maxpool_bwd")
     return din
+
+
+def point_to_voxel(points: torch.Tensor, vsize_xyz, coors_range_xyz, max_num_voxels: int,
+                   max_num_points_per_voxel: int, empty_mean: bool = True, with_id: bool = False):
+    """Voxelise a point cloud [N, F] fp32 (spc_point_to_voxel), like spconv's
+    PointToVoxel: returns (voxels [V, P, F], coords [V, 3] ZYX, num_points [V])
+    and, with ``with_id``, the per-point voxel ids [N] as a fourth item."""
+    dev = points.device
+    _need(points, "points", torch.float32, dev)
+    if points.dim() != 2:
+        raise ValueError("points must be [N, F]")
+    n, F = points.shape
+    vs = (ctypes.c_float * 3)(*[float(v) for v in vsize_xyz])
+    rg = (ctypes.c_float * 6)(*[float(v) for v in coors_range_xyz])
+    b = ctypes.c_size_t()
+    _check(lib().spc_point_to_voxel_workspace(n, F, int(max_num_voxels), int(max_num_points_per_voxel),
+                                              ctypes.byref(b)), "spc_point_to_voxel_workspace")
+    ws = torch.empty(max(int(b.value), 16), dtype=torch.uint8, device=dev)
+    voxels = torch.empty((max_num_voxels, max_num_points_per_voxel, F), dtype=torch.float32, device=dev)
+    coords = torch.empty((max_num_voxels, 3), dtype=torch.int32, device=dev)
+    num = torch.empty((max_num_voxels,), dtype=torch.int32, device=dev)
+    pcid = torch.empty((n,), dtype=torch.int32, device=dev) if with_id else None
+    nv = ctypes.c_int64()
+    st = lib().spc_point_to_voxel(_ptr(points), n, F, vs, rg, int(max_num_voxels), int(max_num_points_per_voxel),
+                                  1 if empty_mean else 0, _ptr(voxels), _ptr(coords), _ptr(num), _ptr(pcid),
+                                  ctypes.byref(nv), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "spc_point_to_voxel")
+    V = nv.value
+    res = (voxels[:V], coords[:V], num[:V])
+    return res + (pcid,) if with_id else res
+
+
+def gather_by_voxel_id(seg_features: torch.Tensor, pc_voxel_id: torch.Tensor,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-point features from per-voxel ones, zeros for id -1 (spc_gather_by_voxel_id)."""
+    dev = seg_features.device
+    _need(seg_features, "seg_features", seg_features.dtype, dev)
+    _need(pc_voxel_id, "pc_voxel_id", torch.int32, dev)
+    C = seg_features.shape[1]
+    if out is None:
+        out = torch.empty((pc_voxel_id.shape[0], C), dtype=seg_features.dtype, device=dev)
+    st = lib().spc_gather_by_voxel_id(_DTYPES[seg_features.dtype], _ptr(seg_features), seg_features.shape[0], C,
+                                      _ptr(pc_voxel_id), pc_voxel_id.shape[0], _ptr(out), _stream(dev))
+    _check(st, "spc_gather_by_voxel_id")
+    return out

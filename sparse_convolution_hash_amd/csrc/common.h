@@ -41,6 +41,35 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int WAVE = 64;
 
+// Load of a[min(i, n - 1)] (n >= 1): an unconditional load, so a batch of
+// them issues back to back; the caller discards the value when i >= n.
+template <typename T>
+__device__ __forceinline__ T ld_clamped(const T* __restrict__ a, int64_t i, int64_t n) {
+    return a[i < n ? i : n - 1];
+}
+
+// Block-wide exclusive scan of one int per thread; returns the block total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    int incl = v;
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    if (lane == WAVE - 1) lds_waves[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < NT / WAVE; ++w) {
+        const int s = lds_waves[w];
+        if (w < wave) before += s;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return before + incl - v;
+}
+
 // 16 bytes moved as one unit (one dwordx4 load/store).
 struct alignas(16) u32x4 {
     uint32_t x, y, z, w;

@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "radix.h"
 
 namespace spc {
 namespace {
@@ -36,13 +37,6 @@ constexpr int KB = 256;          // threads per block of the per-row / per-entry
 constexpr int WORDS_PER_THREAD = 8;
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER_THREAD = 16;
-constexpr int RS_THREADS = 512;              // threads per radix block (one per digit in the spine)
-constexpr int RS_ITEMS = 4;                  // keys per thread in the radix passes
-constexpr int RS_TILE = RS_THREADS * RS_ITEMS;  // keys per radix block
-constexpr int RS_GROUP = 16;                 // radix blocks per group of the two-level offset sums
-constexpr int RS_MAX_PASSES = 4;             // K <= 32 bits of mask, 9 bits per pass
-constexpr int RS_BITS = 9;                   // digit width of the radix passes
-constexpr int RS_BINS = 1 << RS_BITS;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
 
@@ -134,40 +128,11 @@ __device__ __forceinline__ int32_t table_find(const uint64_t* __restrict__ table
     return -1;
 }
 
-// Load of a[min(i, n - 1)] (n >= 1): an unconditional load, so a batch of
-// them issues back to back; the caller discards the value when i >= n.
-template <typename T>
-__device__ __forceinline__ T ld_clamped(const T* __restrict__ a, int64_t i, int64_t n) {
-    return a[i < n ? i : n - 1];
-}
-
 // Output-row count M as the later kernels see it: 0 when it exceeds the
 // caller's capacity (the host then reports SPC_ERR_CAPACITY).
 __device__ __forceinline__ int32_t rows_within(const uint32_t* hdr, int64_t cap) {
     const uint32_t m = hdr[H_NOUT];
     return int64_t(m) <= cap ? int32_t(m) : 0;
-}
-
-// Block-wide exclusive scan of one int per thread; returns the block total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
-    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-    int incl = v;
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const int u = __shfl_up(incl, off);
-        if (lane >= off) incl += u;
-    }
-    if (lane == WAVE - 1) lds_waves[wave] = incl;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < NT / WAVE; ++w) {
-        const int s = lds_waves[w];
-        if (w < wave) before += s;
-        tot += s;
-    }
-    __syncthreads();
-    total = tot;
-    return before + incl - v;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -537,143 +502,6 @@ __global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict_
     }
 }
 
-// Lanes of this wave whose (valid) digit equals this lane's, from RS_BITS ballots.
-__device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d) {
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < RS_BITS; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __ballot(valid && bit);
-        peers &= bit ? bb : ~bb;
-    }
-    return peers;
-}
-
-// Radix sort.  A block owns RS_TILE consecutive keys; wave w of the block
-// owns the contiguous run [w * RS_TILE / NW, (w + 1) * RS_TILE / NW), taken
-// 64 at a time, so the block's keys are visited in index order per wave.
-constexpr int RS_WAVES = RS_THREADS / WAVE;
-constexpr int RS_PER_WAVE = RS_TILE / RS_WAVES;
-static_assert(RS_THREADS == RS_BINS, "one thread per digit");
-
-// Pass histogram.  Every block counts the digits (key >> shift) &
-// (RS_BINS-1) of its tile into hist[d*nb + block] and adds them to the sums
-// of its group of RS_GROUP blocks, gsum[d*ng + block/RS_GROUP] (zeroed
-// beforehand).  rows < 0: M from the header.
-__global__ __launch_bounds__(RS_THREADS) void k_rs_hist(const uint32_t* __restrict__ keys, int32_t rows, int64_t cap,
-                                                        const uint32_t* hdr, int shift, int32_t* __restrict__ hist,
-                                                        int32_t* __restrict__ gsum, int ng) {
-    __shared__ int32_t h[RS_BINS];
-    if (rows < 0) rows = rows_within(hdr, cap);
-    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
-    if (tile0 >= rows) return;  // uniform per block; later blocks are never read
-    const int t = threadIdx.x;
-    uint32_t k[RS_ITEMS];
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) k[r] = ld_clamped(keys, tile0 + r * RS_THREADS + t, rows);
-    h[t] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r)
-        if (tile0 + r * RS_THREADS + t < rows) atomicAdd(h + ((k[r] >> shift) & (RS_BINS - 1)), 1);
-    __syncthreads();
-    const int c = h[t];
-    hist[int64_t(t) * gridDim.x + blockIdx.x] = c;
-    if (c) atomicAdd(gsum + int64_t(t) * ng + blockIdx.x / RS_GROUP, c);
-}
-
-// Pass scatter, stable.  Slot base of digit d for this block: keys of
-// smaller digits, plus digit-d keys of earlier groups (group sums) and of
-// earlier blocks of this group (histogram columns); each wave adds the
-// counts of earlier waves of the block, then ranks its keys among equal
-// digits with RS_BITS ballots (computed once, for counting and writing) and
-// writes them in order.  vals_in == NULL means the identity (row index).
-__global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(const uint32_t* __restrict__ keys_in,
-                                                           const int32_t* __restrict__ vals_in, int32_t rows,
-                                                           int64_t cap, const uint32_t* hdr, int shift,
-                                                           const int32_t* __restrict__ hist,
-                                                           const int32_t* __restrict__ gsum, int ng,
-                                                           uint32_t* __restrict__ keys_out,
-                                                           int32_t* __restrict__ vals_out) {
-    __shared__ int32_t base[RS_WAVES][RS_BINS];
-    __shared__ uint32_t skey[RS_TILE];
-    __shared__ int32_t sval[RS_TILE];
-    if (rows < 0) rows = rows_within(hdr, cap);
-    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
-    if (tile0 >= rows) return;  // uniform per block
-    const int t = threadIdx.x, lane = t & (WAVE - 1), wave = t / WAVE;
-    // 0. the block's keys and values, in index order, into LDS (coalesced,
-    //    unconditional loads so that they are all in flight together)
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = r * RS_THREADS + t;
-        skey[j] = ld_clamped(keys_in, tile0 + j, rows);
-        sval[j] = vals_in ? ld_clamped(vals_in, tile0 + j, rows) : tile0 + j;
-    }
-    // digit t: totals over the groups and the part before this block
-    const int me = int(blockIdx.x), g_me = me / RS_GROUP, b0 = g_me * RS_GROUP;
-    int tot = 0, before = 0;
-    {
-        const int32_t* gs = gsum + int64_t(t) * ng;
-        const int32_t* hc = hist + int64_t(t) * gridDim.x;
-        int hv[RS_GROUP];
-#pragma unroll
-        for (int u = 0; u < RS_GROUP; ++u) hv[u] = ld_clamped(hc, b0 + u, int64_t(me) + 1);
-        for (int q0 = 0; q0 < ng; q0 += RS_GROUP) {
-            int v[RS_GROUP];
-#pragma unroll
-            for (int u = 0; u < RS_GROUP; ++u) v[u] = ld_clamped(gs, q0 + u, ng);
-#pragma unroll
-            for (int u = 0; u < RS_GROUP; ++u) {
-                tot += q0 + u < ng ? v[u] : 0;
-                before += q0 + u < g_me ? v[u] : 0;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < RS_GROUP; ++u) before += b0 + u < me ? hv[u] : 0;
-    }
-#pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w) base[w][t] = 0;
-    __shared__ int waves[RS_WAVES];
-    int total;
-    const int32_t my_off = block_exclusive_scan<RS_THREADS>(tot, waves, total) + before;
-    // (the scan's barriers also publish the LDS keys and the cleared bases)
-    // 1. per-wave digit counts; wave w owns keys [w*RS_PER_WAVE, (w+1)*RS_PER_WAVE) of the block
-    const uint64_t lt = (1ull << lane) - 1ull;
-    uint64_t peers[RS_ITEMS];
-    uint32_t dig[RS_ITEMS];
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = wave * RS_PER_WAVE + r * WAVE + lane;
-        const bool valid = tile0 + j < rows;
-        dig[r] = (skey[j] >> shift) & (RS_BINS - 1);
-        peers[r] = digit_peers(valid, dig[r]);
-        if (valid && (peers[r] & lt) == 0) base[wave][dig[r]] += int(__popcll(peers[r]));  // one leader per digit
-    }
-    __syncthreads();
-    // 2. wave bases: block base + earlier waves of this block
-    int run = my_off;
-#pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w) {
-        const int c = base[w][t];
-        base[w][t] = run;
-        run += c;
-    }
-    __syncthreads();
-    // 3. each wave writes its keys in order
-#pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = wave * RS_PER_WAVE + r * WAVE + lane;
-        if (tile0 + j < rows) {
-            const int rank = __popcll(peers[r] & lt);
-            const int pos = base[wave][dig[r]] + rank;
-            keys_out[pos] = skey[j];
-            vals_out[pos] = sval[j];
-            if (rank == 0) base[wave][dig[r]] += __popcll(peers[r]);
-        }
-    }
-}
-
 // Identity order (used when K > 32 leaves no mask to sort by).
 __global__ void k_iota(int32_t* __restrict__ out, int32_t rows, int64_t cap, const uint32_t* hdr) {
     if (rows < 0) rows = rows_within(hdr, cap);
@@ -840,13 +668,14 @@ spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = RS_BITS * pass;
         int32_t* gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
-        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, kin, rows_dev, cap, s.hdr, shift,
+        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, kin, rows_dev, cap, s.hdr + H_NOUT, shift,
                            sb.hist, gsum, ng);
         SPC_LAUNCHED("k_rs_hist");
         const bool last = pass + 1 == passes;
         uint32_t* kout = sb.keys[pass & 1];
         int32_t* vout = last ? order : sb.vals[pass & 1];
-        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, kin, vin, rows_dev, cap, s.hdr, shift,
+        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, kin, vin, rows_dev, cap,
+                           s.hdr + H_NOUT, shift,
                            sb.hist, gsum, ng, kout, vout);
         SPC_LAUNCHED("k_rs_scatter");
         kin = kout;

@@ -9,7 +9,9 @@ without sharing any of the method.
 from .generators import (  # noqa: F401
     WORKLOAD_NAMES,
     Workload,
+    LIDAR_VOXEL,
     grad_for,
+    lidar_points,
     lidar_scene,
     mesh_shells,
     random_block,

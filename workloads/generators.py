@@ -138,6 +138,32 @@ def mesh_shells(rng: np.random.Generator, batch: int = 4, side: int = 128, shell
     return _shuffle_rows(rng, np.concatenate(rows, axis=0))
 
 
+# Point-cloud voxelisation on a LiDAR-like sweep: 0.1 x 0.1 x 0.2 m voxels
+# over +-51.2 m (x, y) and [-5, 3) m (z), at most 10 points per voxel and
+# 160k voxels (a common detection-network setting; no dataset is read).
+LIDAR_VOXEL = dict(vsize_xyz=[0.1, 0.1, 0.2], range_xyz=[-51.2, -51.2, -5.0, 51.2, 51.2, 3.0],
+                   max_voxels=160_000, max_points=10)
+
+
+def lidar_points(rng: np.random.Generator, n: int = 200_000, features: int = 4) -> np.ndarray:
+    """A synthetic sweep ``[n, features]`` fp32 (x, y, z, intensity, ...): 65%
+    ground returns around the sensor (range uniform in [1, 60] m, so the
+    density falls as 1/range and the far ones leave the box; azimuth uniform;
+    z = -1.7 m with 3 cm noise), 35% object returns in 150 Gaussian blobs
+    (centres uniform over +-45 m, z in [-1.5, 0.5] m, spread 0.6 / 0.6 / 0.4 m);
+    further features uniform in [0, 1); rows in a seeded random order."""
+    ng = int(n * 0.65)
+    no = n - ng
+    rad, az = rng.uniform(1, 60, ng), rng.uniform(0, 2 * np.pi, ng)
+    ground = np.stack([rad * np.cos(az), rad * np.sin(az), -1.7 + 0.03 * rng.standard_normal(ng)], 1)
+    centres = np.stack([rng.uniform(-45, 45, 150), rng.uniform(-45, 45, 150), rng.uniform(-1.5, 0.5, 150)], 1)
+    which = rng.integers(0, 150, no)
+    objects = centres[which] + rng.standard_normal((no, 3)) * np.array([0.6, 0.6, 0.4])
+    xyz = np.concatenate([ground, objects])[rng.permutation(n)]
+    extra = rng.uniform(0, 1, (n, features - 3))
+    return np.concatenate([xyz, extra], 1).astype(np.float32)
+
+
 def tiny_grid(rng: np.random.Generator, side: int, fill: float, batch: int = 1) -> np.ndarray:
     """Each site of a side^3 grid per sample kept independently with probability ``fill``."""
     rows = []
