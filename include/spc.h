@@ -17,14 +17,18 @@
  * - feats / weight / out / dout / din share one dtype (spc_dtype); bias, dW and
  *   dbias are fp32.  Accumulation is fp32, and a 16-bit output is rounded once,
  *   round-to-nearest-even, from the fp32 accumulator with the bias added.
- * - Every pointer except n_out / out_shape / bytes is a DEVICE pointer owned by
- *   the caller; the library allocates nothing and keeps no state between calls
- *   (apart from a thread-local error string).  Device pointers must be 16-byte
+ * - Every pointer except n_out / out_shape / bytes (and the host arrays of
+ *   spc_point_to_voxel) is a DEVICE pointer owned by the caller; the library
+ *   allocates no device memory.  Its only state between calls is per host
+ *   thread: an error string and, per device, created on first use, two side
+ *   streams with their events and 64 bytes of pinned host memory with an
+ *   event (for the strided kernel map).  Device pointers must be 16-byte
  *   aligned.  Every launch is ordered on `stream` (NULL = the default stream).
  * - Errors: a call returns before any launch when its host-side checks fail,
  *   leaving outputs untouched; spc_last_error() then describes the failure.
- *   Only the strided spc_build_kmap synchronises the stream (once, to learn the
- *   output count); every other call is asynchronous.
+ *   Only the strided spc_build_kmap (for the output count) and
+ *   spc_point_to_voxel (for the voxel count) wait for the GPU, once each;
+ *   every other call is asynchronous.
  * - Sizes: row counts below 2^31; channel counts multiples of 16.
  */
 #ifndef SPC_H
@@ -97,7 +101,9 @@ spc_status spc_kmap_workspace(const spc_geom* g, int64_t n_in, size_t* bytes);
  *             output o through offset k, else -1.
  *   nbr_in    [n_in, K] int32 (NULL ok): output row fed by input i through
  *             offset k, else -1.
- *   *n_out    receives M.  The call synchronises `stream` once, at its end.
+ *   *n_out    receives M.  The call waits once, for the count only: the maps,
+ *             pair lists and orders are still being built in stream order
+ *             when it returns.
  *   If out_coords is NULL the call only counts: *n_out = M, nothing else is
  *   written.  If M > out_cap it returns SPC_ERR_CAPACITY with *n_out = M.
  *   An empty output (M = 0) is valid.

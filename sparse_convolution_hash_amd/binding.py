@@ -11,6 +11,7 @@ the library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence
 
@@ -143,6 +144,11 @@ def kmap_workspace(g: Geom, n_in: int) -> int:
     return b.value
 
 
+@functools.lru_cache(maxsize=64)
+def _kmap_workspace_cached(batch, shape, ksize, stride, pad, dil, subm, n_in) -> int:
+    return kmap_workspace(make_geom(batch, shape, ksize, stride, pad, dil, subm), n_in)
+
+
 def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
                subm: bool = True, pairs: bool = True, with_nbr_in: bool = True, orders: bool = False,
                out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> dict:
@@ -164,31 +170,50 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     n = coords.shape[0]
     g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
     K = int(g.ksize[0] * g.ksize[1] * g.ksize[2])
-    ws_bytes = kmap_workspace(g, n)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = _kmap_workspace_cached(batch, tuple(_t3(shape)), tuple(_t3(ksize)), tuple(_t3(stride)),
+                                      tuple(_t3(pad)), tuple(_t3(dil)), bool(subm), n)
     stream = _stream(dev)
     n_out = ctypes.c_int64(0)
-    err = torch.zeros(4, dtype=torch.int32, device=dev)
-    i32 = dict(dtype=torch.int32, device=dev)
     if not subm and out_cap is None:
+        ws = workspace if workspace is not None and workspace.numel() >= ws_bytes else \
+            torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, None, 0, ctypes.byref(n_out), None, None,
-                                  None, None, None, 0, None, None, _ptr(err), _ptr(workspace), workspace.numel(),
-                                  stream)
+                                  None, None, None, 0, None, None, None, _ptr(ws), ws.numel(), stream)
         _check(st, "spc_build_kmap")
         out_cap = n_out.value
+        workspace = ws
     cap = n if subm else int(out_cap)
+    # every int32 output in one allocation (views start 256-byte aligned) and the
+    # workspace in a second one, which the results do not keep alive
+    sizes = {"err": 4, "nbr": max(K * cap, 4)}
+    if not subm:
+        sizes["out_coords"] = max(cap, 1) * 4
+    if not subm and (with_nbr_in or orders):
+        sizes["nbr_in"] = max(n * K, 4)
+    if orders:
+        sizes["order"] = max(cap, 4)
+        if not subm:
+            sizes["order_in"] = max(n, 4)
+    if pairs:
+        sizes.update(pp=K + 1, pi=max(K * n, 4), po=max(K * n, 4))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    offs, total = {}, 0
+    for k, v in sizes.items():
+        offs[k] = total
+        total += (v + 63) // 64 * 64
+    buf = torch.empty(total, dtype=torch.int32, device=dev)
+    view = lambda k: buf[offs[k]:offs[k] + sizes[k]]
+    err = view("err")
     res = {"coord_err": err[:1]}
-    out_coords = None if subm else torch.empty((max(cap, 1), 4), **i32)
-    nbr = torch.empty(max(K * cap, 4), **i32)
-    nbr_in = torch.empty((n, K), **i32) if (not subm and (with_nbr_in or orders)) else None
-    order = torch.empty(max(cap, 4), **i32) if orders else None
-    order_in = torch.empty(max(n, 4), **i32) if (orders and not subm) else None
+    out_coords = None if subm else view("out_coords").view(-1, 4)
+    nbr = view("nbr")
+    nbr_in = view("nbr_in")[:n * K].view(n, K) if "nbr_in" in sizes else None
+    order = view("order") if orders else None
+    order_in = view("order_in") if "order_in" in sizes else None
     pp = pi = po = None
     if pairs:
-        pp = torch.empty(K + 1, **i32)
-        pi = torch.empty(max(K * n, 4), **i32)
-        po = torch.empty(max(K * n, 4), **i32)
+        pp, pi, po = view("pp"), view("pi"), view("po")
     st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, _ptr(out_coords), cap, ctypes.byref(n_out),
                               _ptr(nbr), _ptr(nbr_in), _ptr(pp), _ptr(pi), _ptr(po), max(K * n, 0) if pairs else 0,
                               _ptr(order), _ptr(order_in), _ptr(err), _ptr(workspace), workspace.numel(), stream)

@@ -684,25 +684,49 @@ spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_
     return SPC_OK;
 }
 
-// Concurrent work of one call: a side stream (per host thread and device,
-// default priority) forked from and joined back into the caller's stream.
+// Concurrent work of one call: side streams (per host thread, device and
+// index, default priority) forked from and joined back into the caller's
+// stream.
 struct Side {
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
 };
+constexpr int N_SIDES = 2;
 
-spc_status side_for_device(Side** out) {
-    static thread_local Side sides[64];
+spc_status side_for_device(Side** out, int which) {
+    static thread_local Side sides[64][N_SIDES];
     int dev = 0;
     SPC_HIP(hipGetDevice(&dev));
     if (dev < 0 || dev >= 64) return fail(SPC_ERR_UNSUPPORTED, "device %d", dev);
-    Side& sd = sides[dev];
+    Side& sd = sides[dev][which];
     if (!sd.stream) {
         SPC_HIP(hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking));
         SPC_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
         SPC_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
     }
     *out = &sd;
+    return SPC_OK;
+}
+
+// Pinned host words and an event per host thread and device: a strided call
+// copies M and the coordinate flags there as soon as they are known and waits
+// for that copy only, so the host returns while the rest of the map is built.
+struct HostCount {
+    hipEvent_t ev = nullptr;
+    uint32_t* words = nullptr;
+};
+
+spc_status host_count_for_device(HostCount** out) {
+    static thread_local HostCount hcs[64];
+    int dev = 0;
+    SPC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(SPC_ERR_UNSUPPORTED, "device %d", dev);
+    HostCount& h = hcs[dev];
+    if (!h.ev) {
+        SPC_HIP(hipHostMalloc(reinterpret_cast<void**>(&h.words), 64, hipHostMallocDefault));
+        SPC_HIP(hipEventCreateWithFlags(&h.ev, hipEventDisableTiming));
+    }
+    *out = &h;
     return SPC_OK;
 }
 
@@ -863,10 +887,16 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, bsums, p.bm_blocks, (int32_t*)nullptr, 0,
                        int64_t(0), s.hdr + H_NOUT);
     SPC_LAUNCHED("k_scan");
-    uint32_t host_hdr[2] = {0, 0};
+    // M and the flags are final here: their copy goes first, and the host waits
+    // for it alone once everything else is enqueued
+    HostCount* hc = nullptr;
+    if ((st = host_count_for_device(&hc)) != SPC_OK) return st;
+    SPC_HIP(hipMemcpyAsync(hc->words, s.hdr, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
+    SPC_HIP(hipEventRecord(hc->ev, stream));
     if (!strided_count_only) {
         // Everything after the count is sized by the caller's capacity and reads
-        // M on the device, so the stream is synchronised only once, at the end.
+        // M on the device (a count above the capacity reads as 0), so nothing
+        // after this point waits for the host.
         const int64_t cap = std::min<int64_t>(out_cap, p.m_max);
         if (p.bm_blocks > 0) {
             hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords,
@@ -882,7 +912,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         // the input-side order (its own row pass and sort) runs beside the rest
         Side* sd = nullptr;
         if (order_in) {
-            if ((st = side_for_device(&sd)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
+            if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
             st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, sd->stream);
             if (st != SPC_OK) return st;
         }
@@ -890,18 +920,28 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             st = row_pass(p, nbr, -1, cap, int64_t(out_cap), s, s.mask[0], pairs ? s.counts : nullptr, stream);
             if (st != SPC_OK) return st;
         }
+        // the output-side sort needs only the row pass's masks, so it runs beside
+        // the pair compaction (which reads the masks too, and writes neither the
+        // masks nor the sort's buffers)
+        Side* so = nullptr;
+        if (order) {
+            hipStream_t os = stream;
+            if (pairs) {
+                if ((st = side_for_device(&so, 1)) != SPC_OK || (st = fork_to(so, stream)) != SPC_OK) return st;
+                os = so->stream;
+            }
+            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, os);
+            if (st != SPC_OK) return st;
+        }
         if (pairs) {
             st = map_pairs(p, nbr, -1, cap, int64_t(out_cap), s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
         }
-        if (order) {
-            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, stream);
-            if (st != SPC_OK) return st;
-        }
+        if (so && (st = join_from(so, stream)) != SPC_OK) return st;
         if (sd && (st = join_from(sd, stream)) != SPC_OK) return st;
     }
-    SPC_HIP(hipMemcpyAsync(host_hdr, s.hdr, sizeof(host_hdr), hipMemcpyDeviceToHost, stream));
-    SPC_HIP(hipStreamSynchronize(stream));
+    SPC_HIP(hipEventSynchronize(hc->ev));
+    const uint32_t host_hdr[2] = {hc->words[H_FLAGS], hc->words[H_NOUT]};
     const int64_t M = host_hdr[H_NOUT];
     *n_out = M;
     if (host_hdr[H_FLAGS] & (SPC_COORD_OUT_OF_RANGE | SPC_COORD_DUPLICATE))
