@@ -57,7 +57,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "dinput_strided")
 KERNEL_REPS = 20         # back-to-back launches per single-kernel stage for its duration
-BUSY_FILLS = 12          # 1 GiB fills queued ahead of them (~2-3 ms of GPU time)
+BUSY_FILLS = 3           # 1 GiB fills queued ahead of them (~0.5 ms of GPU time)
 CPU_MIN_S = 10.0         # the oracle repeats whole steps for at least this long (within --cpu-budget)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -234,8 +234,9 @@ class Step:
 
     def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:
         """Average duration of one launch repeated back to back between two events.
-        A few ms of fills are queued first, so the host has enqueued every launch
-        before the first one starts and the host's per-call cost is not timed."""
+        Some GPU work is queued first (fills, then one untimed launch that brings
+        the caches back), so the host has enqueued every timed launch before the
+        first one starts and the host's per-call cost is not timed."""
         torch = self.torch
         launch()
         torch.cuda.synchronize()
@@ -243,6 +244,7 @@ class Step:
             self.busy = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
         for _ in range(BUSY_FILLS):
             self.busy.fill_(1)
+        launch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
