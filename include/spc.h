@@ -242,7 +242,8 @@ spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in,
  * feats [n_in, C], nbr_out [n_out, K] (a strided spc_build_kmap's nbr), out
  * [n_out, C] in the features' dtype (exact: a copy of the winning value),
  * argk uint8 [n_out, C] (NULL ok; the backward needs it).  C a positive
- * multiple of 16, 1 <= K <= 254.  NaN inputs are outside the contract.
+ * multiple of 16, at most 512 (fp16/bf16) or 256 (fp32); 1 <= K <= 254.  NaN
+ * inputs are outside the contract.
  * SPC_ERR_UNSUPPORTED / SPC_ERR_ARG as the convolutions.
  */
 spc_status spc_sparse_maxpool_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t C,

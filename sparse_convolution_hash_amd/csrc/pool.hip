@@ -89,6 +89,42 @@ struct ArgWord<8> {
     __device__ static int get(T w, int e) { return int(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xffu); }
 };
 
+// Lane layout of both kernels: a row's cpr = C / E 16-byte chunks go to cpr
+// consecutive lanes of one wave (rpw = 64 / cpr rows per wave, the last
+// 64 - rpw * cpr lanes idle).  The row's map entries are read once, four
+// consecutive ones per lane, and handed to the row's lanes by shuffles; a
+// batch of 8 offsets that no row of the wave has is skipped.
+struct RowLanes {
+    int cpr, rpw, grp, j, row;
+    bool ok;  // this lane's row exists
+    __device__ RowLanes(int C, int E, int n_rows) {
+        cpr = C / E;
+        rpw = WAVE / cpr;
+        const int lane = int(threadIdx.x) & (WAVE - 1);
+        const int wave = (int(blockIdx.x) * PT + int(threadIdx.x)) / WAVE;
+        grp = lane / cpr;
+        j = lane - grp * cpr;
+        row = wave * rpw + grp;
+        ok = grp < rpw && row < n_rows;
+    }
+};
+
+// The entries [k0, k0 + 4 cpr) of a row: lane j holds k0 + 4j .. k0 + 4j + 3
+// (unguarded loads of a valid row, clamped to the last entry).
+__device__ __forceinline__ void load_entries(int32_t (&e)[4], const int32_t* m, int k0, int j, int K) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = k0 + 4 * j + q;
+        e[q] = m[k < K ? k : K - 1];
+    }
+}
+
+// Entry k0 + kb + t (t < 8, kb a multiple of 8) of this lane's row.
+__device__ __forceinline__ int32_t entry_at(const int32_t (&e)[4], int grp, int cpr, int kb, int t) {
+    const int src = grp * cpr + (kb >> 2) + (t >> 2);
+    return __shfl(e[t & 3], src);
+}
+
 template <typename TT>
 __global__ __launch_bounds__(PT) void k_maxpool_fwd(const void* __restrict__ x_, const int32_t* __restrict__ nbr,
                                                     int32_t n_out, int32_t n_in, int32_t C, int32_t K,
@@ -96,44 +132,52 @@ __global__ __launch_bounds__(PT) void k_maxpool_fwd(const void* __restrict__ x_,
     constexpr int E = TT::E;
     using S = typename TT::storage;
     using AW = ArgWord<E>;
-    const int cpr = C / E;  // 16-byte chunks per row
-    const int g = int(blockIdx.x) * PT + int(threadIdx.x);
-    if (g >= n_out * cpr) return;
-    const int row = g / cpr, ch = (g - row * cpr) * E;
+    const RowLanes L(C, E, n_out);
+    if ((int(blockIdx.x) * PT + int(threadIdx.x)) / WAVE * L.rpw >= n_out) return;  // whole wave past the end
+    const int ch = L.j * E;
     const S* x = static_cast<const S*>(x_);
-    const int32_t* m = nbr + int64_t(row) * K;
+    const int32_t* m = nbr + int64_t(L.ok ? L.row : n_out - 1) * K;
 
     float best[E];
     int arg[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) best[e] = -__builtin_inff(), arg[e] = NO_ARG;
     const int kend = n_in > 0 ? K : 0;  // no input rows: nothing to gather (x may be NULL)
-    for (int k0 = 0; k0 < kend; k0 += KB) {
-        int32_t idx[KB];
+    for (int k0 = 0; k0 < kend; k0 += 4 * L.cpr) {
+        int32_t e4[4];
+        load_entries(e4, m, k0, L.j, K);
+        for (int kb = 0; kb < 4 * L.cpr && k0 + kb < K; kb += KB) {
+            int32_t idx[KB];
+            bool val[KB];
+            bool any = false;
 #pragma unroll
-        for (int j = 0; j < KB; ++j) idx[j] = m[k0 + j < K ? k0 + j : K - 1];
-        u32x4 v[KB];
+            for (int t = 0; t < KB; ++t) {
+                idx[t] = entry_at(e4, L.grp, L.cpr, kb, t);
+                val[t] = L.ok && k0 + kb + t < K && (unsigned)idx[t] < (unsigned)n_in;
+                any = any || val[t];
+            }
+            if (!__any(any)) continue;  // (uniform) no row of this wave has these offsets
+            u32x4 v[KB];
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const int32_t s = (unsigned)idx[j] < (unsigned)n_in ? idx[j] : 0;
-            v[j] = ld16(x + int64_t(s) * C + ch);
-        }
+            for (int t = 0; t < KB; ++t) v[t] = ld16(x + int64_t(val[t] ? idx[t] : 0) * C + ch);
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            if (k0 + j < K && (unsigned)idx[j] < (unsigned)n_in) {
-                float f[E];
-                unpack<TT>(v[j], f);
+            for (int t = 0; t < KB; ++t) {
+                if (val[t]) {
+                    float f[E];
+                    unpack<TT>(v[t], f);
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (f[e] > best[e]) best[e] = f[e], arg[e] = k0 + j;  // strictly greater: the first max stays
+                    for (int q = 0; q < E; ++q)
+                        if (f[q] > best[q]) best[q] = f[q], arg[q] = k0 + kb + t;  // strictly greater: the first max stays
+                }
             }
         }
     }
+    if (!L.ok) return;
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (arg[e] == NO_ARG) best[e] = 0.f;
-    st16(static_cast<S*>(y_) + int64_t(row) * C + ch, pack<TT>(best));
-    if (argk) *reinterpret_cast<typename AW::T*>(argk + int64_t(row) * C + ch) = AW::pack(arg);
+    st16(static_cast<S*>(y_) + int64_t(L.row) * C + ch, pack<TT>(best));
+    if (argk) *reinterpret_cast<typename AW::T*>(argk + int64_t(L.row) * C + ch) = AW::pack(arg);
 }
 
 template <typename TT>
@@ -143,47 +187,64 @@ __global__ __launch_bounds__(PT) void k_maxpool_bwd(const void* __restrict__ dy_
     constexpr int E = TT::E;
     using S = typename TT::storage;
     using AW = ArgWord<E>;
-    const int cpr = C / E;
-    const int g = int(blockIdx.x) * PT + int(threadIdx.x);
-    if (g >= n_in * cpr) return;
-    const int row = g / cpr, ch = (g - row * cpr) * E;
+    const RowLanes L(C, E, n_in);
+    if ((int(blockIdx.x) * PT + int(threadIdx.x)) / WAVE * L.rpw >= n_in) return;  // whole wave past the end
+    const int ch = L.j * E;
     const S* dy = static_cast<const S*>(dy_);
-    const int32_t* m = nbr_in + int64_t(row) * K;
+    const int32_t* m = nbr_in + int64_t(L.ok ? L.row : n_in - 1) * K;
 
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
     const int kend = n_out > 0 ? K : 0;  // no output rows: nothing to gather (dout, argk may be NULL)
-    for (int k0 = 0; k0 < kend; k0 += KB) {
-        int32_t idx[KB];
+    for (int k0 = 0; k0 < kend; k0 += 4 * L.cpr) {
+        int32_t e4[4];
+        load_entries(e4, m, k0, L.j, K);
+        for (int kb = 0; kb < 4 * L.cpr && k0 + kb < K; kb += KB) {
+            int32_t idx[KB];
+            bool val[KB];
+            bool any = false;
 #pragma unroll
-        for (int j = 0; j < KB; ++j) idx[j] = m[k0 + j < K ? k0 + j : K - 1];
-        u32x4 v[KB];
-        typename AW::T w[KB];
+            for (int t = 0; t < KB; ++t) {
+                idx[t] = entry_at(e4, L.grp, L.cpr, kb, t);
+                val[t] = L.ok && k0 + kb + t < K && (unsigned)idx[t] < (unsigned)n_out;
+                any = any || val[t];
+            }
+            if (!__any(any)) continue;  // (uniform) no row of this wave has these offsets
+            u32x4 v[KB];
+            typename AW::T w[KB];
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const int32_t s = (unsigned)idx[j] < (unsigned)n_out ? idx[j] : 0;
-            v[j] = ld16(dy + int64_t(s) * C + ch);
-            w[j] = *reinterpret_cast<const typename AW::T*>(argk + int64_t(s) * C + ch);
-        }
+            for (int t = 0; t < KB; ++t) {
+                const int64_t off = int64_t(val[t] ? idx[t] : 0) * C + ch;
+                v[t] = ld16(dy + off);
+                w[t] = *reinterpret_cast<const typename AW::T*>(argk + off);
+            }
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            if (k0 + j < K && (unsigned)idx[j] < (unsigned)n_out) {
-                float f[E];
-                unpack<TT>(v[j], f);
+            for (int t = 0; t < KB; ++t) {
+                if (val[t]) {
+                    float f[E];
+                    unpack<TT>(v[t], f);
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (AW::get(w[j], e) == k0 + j) acc[e] += f[e];
+                    for (int q = 0; q < E; ++q)
+                        if (AW::get(w[t], q) == k0 + kb + t) acc[q] += f[q];
+                }
             }
         }
     }
-    st16(static_cast<S*>(dx_) + int64_t(row) * C + ch, pack<TT>(acc));
+    if (!L.ok) return;
+    st16(static_cast<S*>(dx_) + int64_t(L.row) * C + ch, pack<TT>(acc));
+}
+
+// Threads of a launch over `rows` rows: whole waves of 64 / cpr rows.
+inline int64_t pool_threads(int64_t rows, int32_t C, int E) {
+    const int rpw = WAVE / (C / E);
+    return ceil_div(rows, rpw) * WAVE;
 }
 
 template <typename TT>
 spc_status launch_fwd(const void* x, const int32_t* nbr, int64_t n_out, int64_t n_in, int32_t C, int32_t K, void* y,
                       uint8_t* argk, hipStream_t stream) {
-    const int64_t threads = n_out * (C / TT::E);
+    const int64_t threads = pool_threads(n_out, C, TT::E);
     hipLaunchKernelGGL(k_maxpool_fwd<TT>, dim3(unsigned(ceil_div(threads, PT))), dim3(PT), 0, stream, x, nbr,
                        int32_t(n_out), int32_t(n_in), C, K, y, argk);
     SPC_LAUNCHED("k_maxpool_fwd");
@@ -193,7 +254,7 @@ spc_status launch_fwd(const void* x, const int32_t* nbr, int64_t n_out, int64_t 
 template <typename TT>
 spc_status launch_bwd(const void* dy, const uint8_t* argk, const int32_t* nbr_in, int64_t n_in, int64_t n_out,
                       int32_t C, int32_t K, void* dx, hipStream_t stream) {
-    const int64_t threads = n_in * (C / TT::E);
+    const int64_t threads = pool_threads(n_in, C, TT::E);
     hipLaunchKernelGGL(k_maxpool_bwd<TT>, dim3(unsigned(ceil_div(threads, PT))), dim3(PT), 0, stream, dy, argk,
                        nbr_in, int32_t(n_in), int32_t(n_out), C, K, dx);
     SPC_LAUNCHED("k_maxpool_bwd");
@@ -203,10 +264,13 @@ spc_status launch_bwd(const void* dy, const uint8_t* argk, const int32_t* nbr_in
 spc_status check_pool(spc_dtype dt, int64_t n_rows, int64_t n_src, int32_t C, int32_t K) {
     if (dt != SPC_F32 && dt != SPC_F16 && dt != SPC_BF16) return fail(SPC_ERR_ARG, "unknown dtype %d", int(dt));
     if (C <= 0 || C % 16) return fail(SPC_ERR_UNSUPPORTED, "C=%d: channels must be a positive multiple of 16", C);
+    const int E = dt == SPC_F32 ? 4 : 8;
+    if (C / E > WAVE)  // a row's 16-byte chunks share one wave
+        return fail(SPC_ERR_UNSUPPORTED, "C=%d: pooling takes at most %d channels of this dtype", C, WAVE * E);
     if (K < 1 || K >= NO_ARG) return fail(SPC_ERR_UNSUPPORTED, "K=%d: pooling takes 1..%d offsets", K, NO_ARG - 1);
     if (n_rows < 0 || n_src < 0 || n_src >= (int64_t(1) << 31)) return fail(SPC_ERR_ARG, "row counts out of range");
-    // one thread per (row, 16-byte chunk), indexed in 32 bits
-    if (n_rows * (C / (dt == SPC_F32 ? 4 : 8)) >= (int64_t(1) << 31))
+    // whole waves of rows, thread indices in 32 bits
+    if (pool_threads(n_rows, C, E) >= (int64_t(1) << 31))
         return fail(SPC_ERR_UNSUPPORTED, "%lld rows of %d channels exceed one launch", (long long)n_rows, C);
     return SPC_OK;
 }

@@ -40,7 +40,7 @@ def run_pool(c, batch, shape, k, s, p, d, x, dtype, ref, seed, what=""):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape,k,s,p,d,C", [
     ((12, 14, 10), 2, 2, 0, 1, 16), ((11, 13, 12), 3, 2, 1, 1, 48), ((10, 10, 10), 3, 1, 1, 1, 32),
-    ((13, 11, 12), 3, 2, 0, 2, 64),
+    ((13, 11, 12), 3, 2, 0, 2, 64), ((14, 13, 12), 5, 2, 2, 1, 32),
 ])
 def test_maxpool_small(dtype, shape, k, s, p, d, C):
     c = W.tiny_grid(W.rng(190 + k + s + d), min(shape), 0.3, 2)
@@ -88,6 +88,11 @@ def test_maxpool_errors():
     x = torch.zeros((10, 32), device="cuda")
     with pytest.raises(spc.SpcError) as e:
         spc.sparse_maxpool_fwd(x, torch.zeros((4, 255), dtype=torch.int32, device="cuda"), 4)
+    assert e.value.status == spc.binding.SPC_ERR_UNSUPPORTED
+    # a row's 16-byte chunks must fit one wave: at most 256 fp32 channels
+    x = torch.zeros((10, 272), device="cuda")
+    with pytest.raises(spc.SpcError) as e:
+        spc.sparse_maxpool_fwd(x, torch.zeros((4, 8), dtype=torch.int32, device="cuda"), 4)
     assert e.value.status == spc.binding.SPC_ERR_UNSUPPORTED
 
 
