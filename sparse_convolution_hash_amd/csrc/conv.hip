@@ -199,7 +199,10 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BMP]
     int32_t* flags = tile + KTILE * BMP;                               // [KTILE]
     int32_t* list = flags + KTILE;                                     // [KTILE + 4] (count at KTILE; keeps 16-B alignment)
-    int32_t* rsrc = list + KTILE + 4;                                  // [BM] output row of tile row r, or -1
+    // the epilogue stages the tile's outputs over the slabs and the map tile
+    constexpr int SROW = BN * int(sizeof(S)) + 16;  // staged output row (16 bytes of padding)
+    const int main_bytes = 2 * slab_bytes + (KTILE * BMP + 2 * KTILE + 4) * 4;
+    int32_t* rsrc = reinterpret_cast<int32_t*>(lds + (main_bytes > BM * SROW ? main_bytes : BM * SROW));  // [BM]
     float* sbias = reinterpret_cast<float*>(rsrc + BM);                // [BN] bias of this column block, or 0
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
@@ -330,10 +333,13 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     }
 
     // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
-    // lg*4 .. lg*4+3 of row lr, so each store is 4 consecutive channels
-    // (bias, then the residual and the ReLU of a fused layer, all on the fp32
-    // value before its one rounding; a residual aliasing y is read by the lane
-    // that then overwrites it)
+    // lg*4 .. lg*4+3 of row lr.  Bias, then the residual and the ReLU of a
+    // fused layer, go on the fp32 value before its one rounding (a residual
+    // aliasing y is read here, before any write of this tile).  The rounded
+    // values are staged in LDS (over the slabs and the map tile, free after the
+    // last offset's barrier) and written out as whole 16-byte chunks of each
+    // row, consecutive threads on consecutive chunks: a quarter of the write
+    // requests of per-lane 8-byte stores.
     S* y = static_cast<S*>(a.y);
     const S* res = static_cast<const S*>(a.res);
     f32x4_t bv[NB];
@@ -341,12 +347,12 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(sbias + nb * 16 + lg * 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int row = rsrc[(wave * RB + rb) * 16 + lr];
-        if (row < 0) continue;
+        const int r = (wave * RB + rb) * 16 + lr;
+        const int row = rsrc[r];
         f32x4_t v[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) v[nb] = acc[rb][nb] + bv[nb];
-        if (res) {
+        if (res && row >= 0) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) v[nb] += load4<TT>(res + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4);
         }
@@ -357,7 +363,18 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                 for (int e = 0; e < 4; ++e) v[nb][e] = v[nb][e] < 0.f ? 0.f : v[nb][e];  // NaN stays NaN
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) store4<TT>(y + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4, v[nb]);
+        for (int nb = 0; nb < NB; ++nb)
+            store4<TT>(lds + r * SROW + (nb * 16 + lg * 4) * int(sizeof(S)), v[nb]);
+    }
+    __syncthreads();
+    constexpr int CPR = BN * int(sizeof(S)) / 16;  // 16-byte chunks per staged row
+    static_assert((BM * CPR) % CT == 0, "whole passes over the staged tile");
+#pragma unroll
+    for (int q = 0; q < BM * CPR / CT; ++q) {
+        const int idx = q * CT + int(threadIdx.x);
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int row = rsrc[r];
+        if (row >= 0) st16(y + int64_t(row) * a.CN + col0 + c * (16 / int(sizeof(S))), ld16(lds + r * SROW + c * 16));
     }
 }
 
@@ -369,8 +386,10 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BM = NW * RB_DEFAULT * 16;
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
     static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
-    const size_t lds = 2 * size_t(a.kch) * (BN * 16 + 16) + size_t(KTILE) * (BM + 1) * 4 + (2 * KTILE + 4) * 4 +
-                       BM * 4 + BN * 4;
+    using S = typename TT::storage;
+    const size_t main_bytes = 2 * size_t(a.kch) * (BN * 16 + 16) + (size_t(KTILE) * (BM + 1) + 2 * KTILE + 4) * 4;
+    const size_t stage_bytes = size_t(BM) * (BN * sizeof(S) + 16);  // the epilogue's staged outputs
+    const size_t lds = std::max(main_bytes, stage_bytes) + BM * 4 + BN * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
