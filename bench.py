@@ -30,6 +30,10 @@ the strided kernel map's one synchronisation), and that average is its launch
 duration.  Its HBM traffic comes from the rocprofv3 counter runs recorded in
 profiles/traffic.json, and only while the kernel source is the one measured.
 
+``--kmap-sweep`` replaces the step by the kernel-map rate on the shell sets at
+4, 8, 16 and 32 samples (one JSON line each), to show the maps as the scene grows
+past the sizes where launch latency dominates.
+
 ``extras`` times the layers beyond the step the same way, one launch each on
 this step's maps: fwd_inverse is the upsampling layer back from the strided
 layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
@@ -72,6 +76,8 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work to time at most")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--kmap-sweep", action="store_true",
+                    help="instead of the step: kernel-map rate on the shell sets at 4..32 samples (one line each)")
     return ap.parse_args()
 
 
@@ -377,6 +383,48 @@ def measured_traffic(workload: str, stage: str):
 
 # ---------------------------------------------------------------- main
 
+def kmap_sweep(batches=(4, 8, 16, 32), reps=10):
+    """Kernel-map rate as the scene grows: the 128^3 shell sets (3 k=3 SubM map
+    with pairs and order; the k3 s2 p1 strided map with pairs and both orders),
+    one JSON line per batch size; medians of `reps` calls timed with HIP events."""
+    import torch
+    import sparse_convolution_hash_amd as spc
+    import workloads as W
+
+    K = 27
+    for B in batches:
+        c = torch.from_numpy(W.mesh_shells(W.rng(3), batch=B)).cuda()
+        n = c.shape[0]
+        shape = (128, 128, 128)
+        m0 = spc.build_kmap(c, B, shape, 3, 2, 1, 1, subm=False, pairs=False)["n_out"]
+        calls = {  # (the strided call gets the exact capacity, as in the step)
+            "subm": lambda: spc.build_kmap(c, B, shape, 3, orders=True),
+            "strided": lambda: spc.build_kmap(c, B, shape, 3, 2, 1, 1, subm=False, out_cap=m0, orders=True),
+        }
+        line = {"kmap_sweep": {"samples": B, "n_voxels": n}}
+        for name, call in calls.items():
+            r = call()
+            torch.cuda.synchronize()
+            P = int(r["pair_ptr"][-1].item())
+            m = r["n_out"]
+            ms = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                torch.cuda.synchronize()
+                ms.append(a.elapsed_time(b))
+            t = sorted(ms)[reps // 2] * 1e-3
+            # algorithmic bytes: coordinates in, maps and pair lists out, orders out
+            by = (n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n if name == "subm" else
+                  16 * n + 16 * m + 4 * K * (m + n) + 8 * P + 4 * (K + 1) + 4 * (m + n))
+            line["kmap_sweep"][name] = {"ms": round(t * 1e3, 4), "voxels_per_s": round(n / t, 1),
+                                        "n_out": m, "pairs": P, "alg_GB/s": round(by / t / 1e9, 1),
+                                        "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+        print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -385,6 +433,9 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.kmap_sweep:
+        kmap_sweep()
+        return
     dev = torch.device("cuda:0")
     inp = make_inputs(args.workload)
     step = Step(inp, dev)
