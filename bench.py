@@ -40,8 +40,10 @@ layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
 residual block relu(conv(x) + x) in one kernel, and ..._unfused the same
 through the plain forward plus torch's add and relu (three launches, timed
 together); maxpool_fwd / maxpool_bwd pool x over the strided layer's map
-(3^3, stride 2); point_to_voxel voxelises a 200k-point synthetic sweep (one
-call, its host synchronisation included).  They are not part of ``value``.
+(3^3, stride 2); subm_step_graph replays the SubM half of the step (kernel map,
+forward, k=1, dinput, dfilter) as one captured HIP graph, subm_step_eager makes
+the same calls one by one; point_to_voxel voxelises a 200k-point synthetic sweep
+(one call, its host synchronisation included).  They are not part of ``value``.
 """
 
 from __future__ import annotations
@@ -214,6 +216,28 @@ class Step:
             y.add_(self.x).relu_()
 
         sub_bytes = n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s
+        inp = self.inp
+
+        def subm_step():  # the SubM half of the step: kernel map, forward, k=1, dinput, dfilter
+            kmap = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
+            y = spc.subm_conv_fwd(self.x, self.w3, None, kmap["nbr"], kmap["order"])
+            spc.subm_conv_fwd(y, self.w1, None, None)
+            spc.conv_bwd_input(self.g, self.w3, kmap["nbr"], True, n, kmap["order"])
+            spc.conv_bwd_filter(self.x, self.g, K, kmap["pair_ptr"], kmap["pair_in"], kmap["pair_out"])
+
+        if not hasattr(self, "graph"):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):  # warm the allocator on the capture stream
+                subm_step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                subm_step()
+        f, b = self.work()
+        st_f = sum(f[k] for k in ("fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm"))
+        st_b = sum(b[k] for k in ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm"))
         return {
             "fwd_inverse": (lambda: spc.sparse_inverse_conv_fwd(self.gs, self.w_inv, None, ks["nbr_in"], n,
                                                                 ks["order_in"]),
@@ -232,6 +256,10 @@ class Step:
             # a 200k-point synthetic sweep into 0.1 x 0.1 x 0.2 m voxels (one call,
             # including its one host synchronisation); bytes: the points read, the
             # voxel block, coordinates, counts and point ids written
+            # the SubM half of the step replayed as one captured HIP graph, and the
+            # same calls made one by one
+            "subm_step_graph": (self.graph.replay, st_f, st_b),
+            "subm_step_eager": (subm_step, st_f, st_b),
             "point_to_voxel": (lambda: spc.point_to_voxel(self.pts, vc["vsize_xyz"], vc["range_xyz"],
                                                           vc["max_voxels"], vc["max_points"], True, with_id=True),
                                0, self.pts.numel() * 4 + vc["max_voxels"] * (vc["max_points"] * self.pts.shape[1] * 4
