@@ -78,6 +78,7 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work to time at most")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--no-extras", action="store_true", help="skip timing the layers beyond the step")
     ap.add_argument("--kmap-sweep", action="store_true",
                     help="instead of the step: kernel-map rate on the shell sets at 4..32 samples (one line each)")
     return ap.parse_args()
@@ -520,7 +521,7 @@ def main():
     roof["kernel_ms"] = {k: round(v, 4) for k, v in kernel_ms.items()}
 
     extras = {}
-    for name, (launch, fl, by) in step.extras().items():
+    for name, (launch, fl, by) in ({} if args.no_extras else step.extras()).items():
         ms = step.time_launch(launch)
         t = ms * 1e-3
         bound = "hbm" if fl / by < ridge else "mfma"
