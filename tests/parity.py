@@ -38,3 +38,21 @@ def pairs_equal(res, ref_ptr, ref_in, ref_out):
     P = int(ptr[-1])
     assert np.array_equal(host(res["pair_in"][:P]), ref_in), "pair_in differs"
     assert np.array_equal(host(res["pair_out"][:P]), ref_out), "pair_out differs"
+
+
+def hygon_check(got, ref, cin, cout, fp32: bool, what=""):
+    """Secondary check, the acceptance test of the Hygon spconv-das README
+    (its public test-suite table): fp32 outputs pass torch.allclose with
+    atol = rtol = 1e-4; fp16 / bf16 runs pass when the L2 norm of the error is
+    below 10 * max(1, max(Cin, Cout) / 16).  Our reference is the fp64 oracle.
+    Returns the L2 norm of the error."""
+    g = torch.as_tensor(OC.f64(got))
+    r = torch.as_tensor(OC.f64(ref))
+    l2 = float(torch.linalg.vector_norm(g - r))
+    if fp32:
+        assert torch.allclose(g, r, atol=1e-4, rtol=1e-4), f"{what}: fails allclose(atol=rtol=1e-4)"
+    else:
+        bound = 10 * max(1.0, max(cin, cout) / 16)
+        assert l2 < bound, f"{what}: L2 error {l2:.3g} >= {bound:g}"
+    print(f"{what}: L2 error {l2:.3g}", flush=True)
+    return l2

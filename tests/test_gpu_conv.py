@@ -10,7 +10,7 @@ import sparse_convolution_hash_amd as spc
 import workloads as W
 from oracle import conv as OC
 from oracle import kmap as O
-from tests.parity import TOL, TOL_DW, assert_close, cuda, host
+from tests.parity import TOL, TOL_DW, assert_close, cuda, host, hygon_check
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,12 @@ def run_subm_layer(c, batch, shape, k, t, dtype, train=True, what="", ordered=Tr
     dw, db = spc.conv_bwd_filter(x, g, k ** 3, pp, pi, po, want_dbias=True)
     errs["dw"] = assert_close(dw, OC.conv_bwd_filter(t["feats"], t["grad"], nbr_ref), TOL_DW, "dw")
     errs["db"] = assert_close(db, OC.conv_bwd_bias(t["grad"]), TOL_DW, "dbias")
+    if what:  # the named workloads: the Hygon README's acceptance test as well
+        cin, cout = t["weight"].shape[1], t["weight"].shape[2]
+        fp32 = dtype == torch.float32
+        hygon_check(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr_ref), cin, cout, fp32, "fwd")
+        hygon_check(din, OC.conv_bwd_input(t["grad"], t["weight"], nbr_ref, c.shape[0]), cin, cout, fp32, "din")
+        hygon_check(dw, OC.conv_bwd_filter(t["feats"], t["grad"], nbr_ref), cin, cout, fp32, "dw")
     return errs
 
 
@@ -151,7 +157,10 @@ def test_workload_strided_lidar_fp16():
     din = spc.conv_bwd_input(gd, wt, km["nbr_in"], False, w.n, km["order_in"])
     assert_close(din, OC.conv_bwd_input(g, w.weight, ref["nbr_out"], w.n), TOL[w.dtype], "din")
     dw, _ = spc.conv_bwd_filter(x, gd, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
-    assert_close(dw, OC.conv_bwd_filter(w.feats, g, ref["nbr_out"]), TOL_DW, "dw")
+    dw_ref = OC.conv_bwd_filter(w.feats, g, ref["nbr_out"])
+    assert_close(dw, dw_ref, TOL_DW, "dw")
+    hygon_check(out, OC.conv_fwd(w.feats, w.weight, None, ref["nbr_out"]), 64, 128, False, "fwd")
+    hygon_check(dw, dw_ref, 64, 128, False, "dw")
 
 
 def test_workload_train_shells_bf16():
