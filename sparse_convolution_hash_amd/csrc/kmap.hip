@@ -39,6 +39,8 @@ constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
+constexpr uint64_t DENSE_CELLS_PER_ROW = 64;   // dense index grid below this many cells per input row
+constexpr uint64_t DENSE_MAX_BYTES = uint64_t(1) << 30;
 
 struct KGeom {
     int32_t batch, Z, Y, X;      // input grid
@@ -50,6 +52,7 @@ struct KGeom {
     // reciprocals for division by these invariants (qdiv; 0 for a divisor of 1):
     // K, the strides, and the output grid's x extent, plane and volume
     uint64_t mK, msz, msy, msx, mox, mplane, mvol;
+    int32_t dense;               // the table is a dense index grid (see make_plan)
 };
 
 // ceil(2^64 / d) for d >= 2, 0 for d == 1 (see qdiv)
@@ -171,7 +174,12 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         atomicOr(hdr + H_FLAGS, SPC_COORD_OUT_OF_RANGE);
         return;
     }
-    table_insert(table, mask, in_key(c.x, c.y, c.z, c.w, g), uint32_t(i), hdr + H_FLAGS);
+    const uint32_t key = in_key(c.x, c.y, c.z, c.w, g);
+    if (g.dense) {  // one row per cell: the first claim wins, a second is a duplicate
+        if (atomicCAS(reinterpret_cast<int32_t*>(table) + key, -1, i) != -1) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
+    } else {
+        table_insert(table, mask, key, uint32_t(i), hdr + H_FLAGS);
+    }
     if (!STRIDED) return;
     int oz[8], oy[8], ox[8];
     int nz = 0, ny = 0, nx = 0;
@@ -232,7 +240,8 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
         if (kz == g.kz / 2 && ky == g.ky / 2 && kx == g.kx / 2)
             v = i;
         else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X)
-            v = table_find(table, mask, in_key(c.x, z, y, x, g));
+            v = g.dense ? reinterpret_cast<const int32_t*>(table)[in_key(c.x, z, y, x, g)]
+                        : table_find(table, mask, in_key(c.x, z, y, x, g));
     }
     nbr[t] = v;
 }
@@ -581,10 +590,17 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     if (int64_t(p.K) * n_in >= (int64_t(1) << 31))
         return fail(SPC_ERR_UNSUPPORTED, "K*n_in=%lld must be below 2^31", (long long)(int64_t(p.K) * n_in));
     p.n = n_in;
-    // load factor <= 1/4 keeps unsuccessful probes (most of them) near one load
+    // The table.  A grid of at most DENSE_CELLS_PER_ROW cells per input row
+    // (and DENSE_MAX_BYTES) gets a dense index grid, one int32 row per cell
+    // (-1: empty): clearing it costs at most 256 bytes per row, and then an
+    // insert is one CAS and a probe one load, with no probe sequence.  Larger,
+    // sparser grids get the hash: load factor <= 1/4 keeps unsuccessful probes
+    // (most of them) near one load.  Either way the region is cap 8-byte words.
+    k.dense = in_vol <= uint64_t(DENSE_CELLS_PER_ROW) * uint64_t(std::max<int64_t>(n_in, 1)) &&
+              in_vol * 4 <= DENSE_MAX_BYTES;
     p.cap_log2 = 6;
     while ((int64_t(1) << p.cap_log2) < 4 * n_in) ++p.cap_log2;
-    p.cap = int64_t(1) << p.cap_log2;
+    p.cap = k.dense ? int64_t((in_vol + 3) / 4 * 2) : int64_t(1) << p.cap_log2;
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
     p.nwords = g.subm ? 0 : ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb;
     p.bm_blocks = p.nwords / wpb;

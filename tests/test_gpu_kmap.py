@@ -160,3 +160,20 @@ def test_strided_kmap_on_a_user_stream():
     st.synchronize()
     for key in ("out_coords", "nbr", "nbr_in", "pair_ptr", "order", "order_in"):
         assert torch.equal(res[key], ref[key]), key
+
+
+def test_dense_grid_and_hash_give_the_same_map():
+    # a small grid takes the dense index grid, a large one the hash; the same
+    # sites (far from the large grid's faces) have the same neighbours in both
+    c = W.tiny_grid(W.rng(250), 12, 0.3, 2)
+    small = check_subm(c, 2, (12, 12, 12), 3)                 # 3456 cells for ~1000 rows: dense
+    shifted = c + np.array([0, 40, 50, 60], np.int32)
+    big = check_subm(shifted, 2, (200, 220, 240), 3)          # ~10^7 cells: hash
+    assert torch.equal(small["nbr"], big["nbr"]) and torch.equal(small["order"], big["order"])
+    check_strided(shifted, 2, (200, 220, 240), 3, 2, 1, 1)
+
+
+def test_dense_grid_flags_duplicates():
+    c = np.array([[0, 1, 1, 1], [0, 2, 2, 2], [0, 1, 1, 1]], np.int32)   # 64 cells, 3 rows: dense
+    res = spc.build_kmap(cuda(c), 1, (4, 4, 4), 3)
+    assert int(host(res["coord_err"])[0]) & spc.binding.COORD_DUPLICATE
