@@ -39,8 +39,8 @@ constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
-constexpr uint64_t DENSE_CELLS_PER_ROW = 64;   // dense index grid below this many cells per input row
-constexpr uint64_t DENSE_MAX_BYTES = uint64_t(1) << 30;
+constexpr uint64_t OCC_CELLS_PER_ROW = 4096;   // occupancy bitmap up to this many input cells per row (512 B)
+constexpr uint64_t DENSE_MAX_BYTES = uint64_t(1) << 30;   // index grid limit
 
 struct KGeom {
     int32_t batch, Z, Y, X;      // input grid
@@ -52,7 +52,8 @@ struct KGeom {
     // reciprocals for division by these invariants (qdiv; 0 for a divisor of 1):
     // K, the strides, and the output grid's x extent, plane and volume
     uint64_t mK, msz, msy, msx, mox, mplane, mvol;
-    int32_t dense;               // the table is a dense index grid (see make_plan)
+    int32_t occ;                 // input occupancy bitmap in use (see make_plan)
+    int32_t dense;               // ... and, beside it, the index grid as the table
 };
 
 // ceil(2^64 / d) for d >= 2, 0 for d == 1 (see qdiv)
@@ -140,16 +141,18 @@ __device__ __forceinline__ int32_t rows_within(const uint32_t* hdr, int64_t cap)
 
 // ---------------------------------------------------------------- kernels
 
-// Fills the table with the empty marker; zeroes the bitmap, the header and
-// `zero` (nzero ints, a multiple of 4).
+// Fills `cap` hash slots with the empty marker; zeroes the output bitmap, the
+// occupancy bitmap, the header and `zero` (word counts multiples of 4).
 __global__ void k_clear(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ bitmap,
-                        int64_t nwords, uint32_t* __restrict__ hdr, int32_t* __restrict__ zero, int64_t nzero) {
+                        int64_t nwords, uint32_t* __restrict__ occ, int64_t occ_words, uint32_t* __restrict__ hdr,
+                        int32_t* __restrict__ zero, int64_t nzero) {
     const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     if (t < H_WORDS) hdr[t] = 0u;
     u32x4 ones = {~0u, ~0u, ~0u, ~0u};
     for (int64_t i = t; i < cap / 2; i += stride) st16(table + 2 * i, ones);
     for (int64_t i = t; i < nwords / 4; i += stride) st16(bitmap + 4 * i, zero4());
+    for (int64_t i = t; i < occ_words / 4; i += stride) st16(occ + 4 * i, zero4());
     for (int64_t i = t; i < nzero / 4; i += stride) st16(zero + 4 * i, zero4());
 }
 
@@ -165,7 +168,7 @@ __global__ void k_fill_map(int32_t* __restrict__ map, int K, int64_t cap, const 
 // reaches: o = (c + pad - k*dil) / stride per axis, exact and inside the grid.
 template <bool STRIDED>
 __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, int32_t n, KGeom g,
-                                               uint64_t* table, uint32_t mask,
+                                               uint64_t* table, uint32_t mask, uint32_t* occ,
                                                uint32_t* bitmap, uint32_t* hdr) {
     const int32_t i = blockIdx.x * KB + threadIdx.x;
     if (i >= n) return;
@@ -175,8 +178,10 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         return;
     }
     const uint32_t key = in_key(c.x, c.y, c.z, c.w, g);
-    if (g.dense) {  // one row per cell: the first claim wins, a second is a duplicate
-        if (atomicCAS(reinterpret_cast<int32_t*>(table) + key, -1, i) != -1) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
+    if (g.occ) {  // a cell whose bit was already set is a duplicate
+        const uint32_t bit = 1u << (key & 31u);
+        if (atomicOr(occ + (key >> 5), bit) & bit) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
+        if (g.dense) reinterpret_cast<int32_t*>(table)[key] = i;
     } else {
         table_insert(table, mask, key, uint32_t(i), hdr + H_FLAGS);
     }
@@ -221,8 +226,8 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
 // slowest.  Consecutive threads write consecutive entries.
 __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coords, int32_t n, KGeom g,
                                                    const uint64_t* __restrict__ table, uint32_t mask,
-                                                   int32_t* __restrict__ nbr, const uint32_t* hdr,
-                                                   int32_t* coord_err) {
+                                                   const uint32_t* __restrict__ occ, int32_t* __restrict__ nbr,
+                                                   const uint32_t* hdr, int32_t* coord_err) {
     __shared__ uint32_t ktab[MAX_K];
     const int K = g.kz * g.ky * g.kx;
     offset_table(ktab, g, K);
@@ -239,9 +244,13 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
         const int z = c.y + kz - g.kz / 2, y = c.z + ky - g.ky / 2, x = c.w + kx - g.kx / 2;
         if (kz == g.kz / 2 && ky == g.ky / 2 && kx == g.kx / 2)
             v = i;
-        else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X)
-            v = g.dense ? reinterpret_cast<const int32_t*>(table)[in_key(c.x, z, y, x, g)]
-                        : table_find(table, mask, in_key(c.x, z, y, x, g));
+        else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X) {
+            const uint32_t key = in_key(c.x, z, y, x, g);
+            if (!g.dense)
+                v = table_find(table, mask, key);
+            else if ((occ[key >> 5] >> (key & 31u)) & 1u)
+                v = reinterpret_cast<const int32_t*>(table)[key];
+        }
     }
     nbr[t] = v;
 }
@@ -451,6 +460,133 @@ __global__ __launch_bounds__(KB) void k_row_pass(const int32_t* __restrict__ map
     for (int k = threadIdx.x; k < K; k += KB) counts[int64_t(k) * gridDim.x + blockIdx.x] = cnt[k];
 }
 
+// Continues a hash probe sequence past its home slot h0 (which held another key).
+__device__ __noinline__ int32_t table_find_after(const uint64_t* __restrict__ table, uint32_t mask, uint32_t key,
+                                                 uint32_t h0) {
+    uint32_t h = (h0 + 1) & mask;
+    for (uint32_t step = 1; step <= mask; ++step) {
+        const uint64_t v = table[h];
+        if (v == EMPTY_SLOT) return -1;
+        if (uint32_t(v >> 32) == key) return int32_t(uint32_t(v));
+        h = (h + 1) & mask;
+    }
+    return -1;
+}
+
+// Submanifold map and row pass in one kernel, for K <= ROWPASS_KMAX: one
+// thread per row.  The K lookups of a row are issued together, so a wave has
+// all its rows' lookups in flight at once: with the index grid, the K
+// occupancy words, then the grid cells of the occupied neighbours; with the
+// hash, the keys' home slots, which answer nearly every probe at load factor
+// <= 1/4 (the few longer probe sequences continue afterwards).  Entries go to an LDS tile (row
+// stride K words) and leave as coalesced row-major stores; the thread then has
+// its row's mask (keys, K <= 32) and the block's per-offset hit counts
+// (counts[k*gridDim.x + block]), as k_row_pass makes them.  The centre entry
+// is the row itself.
+template <bool DENSE>
+__global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coords, int32_t n, KGeom g,
+                                                  const uint64_t* __restrict__ table, uint32_t mask,
+                                                  const uint32_t* __restrict__ occ,
+                                                  int32_t* __restrict__ nbr, uint32_t* __restrict__ keys,
+                                                  int32_t* __restrict__ counts, const uint32_t* hdr,
+                                                  int32_t* coord_err) {
+    __shared__ uint32_t ktab[ROWPASS_KMAX];
+    __shared__ int32_t cnt[ROWPASS_KMAX];
+    __shared__ int32_t stage[KB * ROWPASS_KMAX];
+    const int K = g.kz * g.ky * g.kx;
+    const int t = threadIdx.x;
+    if (t < K) {
+        ktab[t] = uint32_t((t / (g.kx * g.ky)) << 6 | ((t / g.kx) % g.ky) << 3 | (t % g.kx));
+        cnt[t] = 0;
+    }
+    __syncthreads();
+    // workgroups go to the XCDs round-robin; XCD x takes a contiguous run of
+    // row blocks, so the grid cells its rows look up stay in its own L2
+    const uint32_t nb = gridDim.x, xc = blockIdx.x % 8u, per = nb / 8u;
+    const uint32_t lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
+    const int32_t row0 = int32_t(lb) * KB, i = row0 + t;
+    if (coord_err && i == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (row0 >= n) return;  // uniform per block (only an empty call launches one)
+    const bool live = i < n;
+    const int4 c = coords[live ? i : n - 1];
+    const bool ok = live && in_grid(c, g);
+    const int32_t* dense = reinterpret_cast<const int32_t*>(table);
+    // 1. every lookup of the row, from valid addresses (cell 0 or its slot
+    //    when the neighbour is outside the grid; such entries are -1 regardless)
+    uint32_t key[ROWPASS_KMAX];
+    uint64_t got[ROWPASS_KMAX];
+    uint32_t inside = 0;
+#pragma unroll
+    for (int k = 0; k < ROWPASS_KMAX; ++k) {
+        const uint32_t kk = ktab[k < K ? k : 0];
+        const int z = c.y + int(kk >> 6) - g.kz / 2, y = c.z + int((kk >> 3) & 7) - g.ky / 2,
+                  x = c.w + int(kk & 7) - g.kx / 2;
+        const bool in = ok && k < K && k != K / 2 && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y &&
+                        (unsigned)x < (unsigned)g.X;
+        key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
+        inside |= uint32_t(in) << k;
+        got[k] = DENSE ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
+    }
+    if (DENSE) {  // grid cells of the occupied neighbours (cell 0, ignored, elsewhere)
+#pragma unroll
+        for (int k = 0; k < ROWPASS_KMAX; ++k) {
+            const bool hit = ((inside >> k) & (uint32_t(got[k]) >> (key[k] & 31u)) & 1u) != 0;
+            const int32_t v = dense[hit ? key[k] : 0u];
+            got[k] = uint64_t(uint32_t(hit ? v : -1));
+        }
+    }
+    // 2. resolve into LDS; hash probes that met another key finish afterwards
+    uint32_t m = 0, pending = 0;
+    int32_t* srow = stage + t * K;
+#pragma unroll
+    for (int k = 0; k < ROWPASS_KMAX; ++k) {
+        if (k >= K) continue;
+        int32_t v = -1;
+        if (k == K / 2) {
+            v = ok ? i : -1;
+        } else if ((inside >> k) & 1u) {
+            if (DENSE) {
+                v = int32_t(uint32_t(got[k]));
+            } else if (got[k] != EMPTY_SLOT) {
+                if (uint32_t(got[k] >> 32) == key[k])
+                    v = int32_t(uint32_t(got[k]));
+                else
+                    pending |= 1u << k;
+            }
+        }
+        srow[k] = v;
+        if (v >= 0) m |= 1u << k;
+    }
+    while (pending) {
+        const int k = __ffs(pending) - 1;
+        pending &= pending - 1;
+        const uint32_t kk = ktab[k];
+        const int z = c.y + int(kk >> 6) - g.kz / 2, y = c.z + int((kk >> 3) & 7) - g.ky / 2,
+                  x = c.w + int(kk & 7) - g.kx / 2;
+        const uint32_t q = in_key(c.x, z, y, x, g);
+        const int32_t v = table_find_after(table, mask, q, home_slot(q) & mask);
+        srow[k] = v;
+        if (v >= 0) m |= 1u << k;
+    }
+    // 3. per-offset hit counts of the block (wave ballots into LDS)
+    if (counts) {
+        for (int k = 0; k < K; ++k) {
+            const uint64_t b = __ballot((m >> k) & 1u);
+            if ((t & (WAVE - 1)) == 0 && b) atomicAdd(cnt + k, int(__popcll(b)));
+        }
+    }
+    if (keys && live) keys[i] = m;
+    __syncthreads();
+    // 4. the block's rows, row-major, coalesced
+    const int64_t lo = int64_t(row0) * K, len = int64_t(min(n, row0 + KB) - row0) * K;
+#pragma unroll
+    for (int e = 0; e < ROWPASS_KMAX; ++e) {
+        const int j = e * KB + t;
+        if (j < len) nbr[lo + j] = stage[j];
+    }
+    if (counts && t < K) counts[int64_t(t) * gridDim.x + lb] = cnt[t];
+}
+
 // Ordered compaction of one block of map rows into the CSR pair lists: for
 // each offset k, the block's hits go to the scanned offset offs[k*nblk +
 // block] in ascending row order.  With masks (K <= 32) the ranks of all
@@ -535,7 +671,8 @@ struct Plan {
     int64_t bm_blocks;           // bitmap count/emit blocks
     // workspace offsets
     int64_t rgroups;             // radix block groups
-    size_t off_table, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, total;
+    int64_t occ_words;           // input occupancy bitmap words (multiple of 4)
+    size_t off_table, off_occ, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, total;
     size_t sort_slot_bytes;      // per sort: keys x2, values x2, histogram matrix
 };
 
@@ -590,17 +727,24 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     if (int64_t(p.K) * n_in >= (int64_t(1) << 31))
         return fail(SPC_ERR_UNSUPPORTED, "K*n_in=%lld must be below 2^31", (long long)(int64_t(p.K) * n_in));
     p.n = n_in;
-    // The table.  A grid of at most DENSE_CELLS_PER_ROW cells per input row
-    // (and DENSE_MAX_BYTES) gets a dense index grid, one int32 row per cell
-    // (-1: empty): clearing it costs at most 256 bytes per row, and then an
-    // insert is one CAS and a probe one load, with no probe sequence.  Larger,
-    // sparser grids get the hash: load factor <= 1/4 keeps unsuccessful probes
-    // (most of them) near one load.  Either way the region is cap 8-byte words.
-    k.dense = in_vol <= uint64_t(DENSE_CELLS_PER_ROW) * uint64_t(std::max<int64_t>(n_in, 1)) &&
-              in_vol * 4 <= DENSE_MAX_BYTES;
+    // The input table.  A grid of at most OCC_CELLS_PER_ROW cells per input row
+    // gets an occupancy bitmap (one bit per cell, at most 512 bytes per row to
+    // clear): an insert sets its bit with one atomic OR, whose old value
+    // flags a duplicate.  A submanifold map (grid of at most DENSE_MAX_BYTES)
+    // keeps beside it the index grid, one int32 row per cell, written at the
+    // occupied cells only and read only where the bitmap says occupied, so it
+    // is never cleared; a probe is a bitmap word (the bitmap is small enough
+    // to stay in L2) and, for an occupied cell, one grid load.  The strided
+    // path needs the input table only for duplicates.  Larger, sparser grids
+    // get the hash: load factor <= 1/4 keeps unsuccessful probes (most of them)
+    // near one load.  The table region is cap 8-byte words.
+    const bool occ = in_vol <= OCC_CELLS_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1));
+    k.dense = g.subm && occ && in_vol * 4 <= DENSE_MAX_BYTES;
+    k.occ = g.subm ? k.dense : occ;
+    p.occ_words = k.occ ? int64_t(ceil_div(int64_t(in_vol), 128) * 4) : 0;
     p.cap_log2 = 6;
     while ((int64_t(1) << p.cap_log2) < 4 * n_in) ++p.cap_log2;
-    p.cap = k.dense ? int64_t((in_vol + 3) / 4 * 2) : int64_t(1) << p.cap_log2;
+    p.cap = k.dense ? int64_t((in_vol + 1) / 2) : k.occ ? 0 : int64_t(1) << p.cap_log2;
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
     p.nwords = g.subm ? 0 : ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb;
     p.bm_blocks = p.nwords / wpb;
@@ -610,6 +754,7 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     p.rblk = ceil_div(p.rows_max, RS_TILE);
     size_t off = 256;
     p.off_table = off;   off = align_up(off + size_t(p.cap) * 8, 256);
+    p.off_occ = off;     off = align_up(off + size_t(p.occ_words) * 4, 256);
     p.off_counts = off;  off = align_up(off + size_t(p.K) * p.cblk * 4, 256);
     p.off_bitmap = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_prefix = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
@@ -851,6 +996,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     }
     s.gsum = reinterpret_cast<int32_t*>(base + p.off_gsum);
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
+    uint32_t* occ = reinterpret_cast<uint32_t*>(base + p.off_occ);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(base + p.off_prefix);
     int32_t* bsums = reinterpret_cast<int32_t*>(base + p.off_bsums);
@@ -861,20 +1007,40 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     const int64_t entries = int64_t(n) * p.K;
 
     const int64_t nzero = (order || order_in) ? int64_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups : 0;
-    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({p.cap / 2, p.nwords / 4, nzero / 4}), KB, 4096)), dim3(KB), 0,
-                       stream, table, p.cap, bitmap, p.nwords, s.hdr, s.gsum, nzero);
+    const int64_t fill = p.g.occ ? 0 : p.cap;   // hash slots to mark empty (the index grid is never cleared)
+    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({fill / 2, p.nwords / 4, p.occ_words / 4, nzero / 4}), KB, 4096)),
+                       dim3(KB), 0, stream, table, fill, bitmap, p.nwords, occ, p.occ_words, s.hdr, s.gsum, nzero);
     SPC_LAUNCHED("k_clear");
     if (n > 0) {
         if (subm)
-            hipLaunchKernelGGL(k_insert<false>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, bitmap, s.hdr);
+            hipLaunchKernelGGL(k_insert<false>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, bitmap,
+                               s.hdr);
         else
-            hipLaunchKernelGGL(k_insert<true>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, bitmap, s.hdr);
+            hipLaunchKernelGGL(k_insert<true>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, bitmap,
+                               s.hdr);
         SPC_LAUNCHED("k_insert");
     }
 
+    if (subm && p.K <= ROWPASS_KMAX) {
+        // probes, masks and counts in one pass over the rows
+        hipLaunchKernelGGL(p.g.dense ? k_subm_rows<true> : k_subm_rows<false>, dim3(unsigned(std::max(nblk, 1))),
+                           dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, nbr, (pairs || order) ? s.mask[0] : nullptr,
+                           pairs ? s.counts : nullptr, s.hdr, coord_err);
+        SPC_LAUNCHED("k_subm_rows");
+        if (pairs) {
+            st = map_pairs(p, nbr, n, n, n, s, pair_ptr, pair_in, pair_out, stream);
+            if (st != SPC_OK) return st;
+        }
+        if (order) {
+            st = sort_rows(p, nbr, n, n, n, s, true, 0, order, stream);
+            if (st != SPC_OK) return st;
+        }
+        *n_out = n_in;
+        return SPC_OK;
+    }
     if (subm) {
         hipLaunchKernelGGL(k_subm_probe, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
-                           stream, c4, n, p.g, table, mask, nbr, s.hdr, coord_err);
+                           stream, c4, n, p.g, table, mask, occ, nbr, s.hdr, coord_err);
         SPC_LAUNCHED("k_subm_probe");
         if (pairs || order) {
             // one row pass: the masks (for the order and the compaction) and the counts
