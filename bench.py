@@ -5,7 +5,7 @@ One step runs every stage of the path once on one batch of synthetic input.
 It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
 1408 grid, fp16, 64 channels.  The stages are, in order:
 
-    kmap_subm       submanifold kernel map k=3 (hash build + probe + pair lists)
+    kmap_subm       submanifold kernel map k=3 (table build + probe + pair lists + order)
     fwd_subm        SubMConv3d k=3 forward 64 -> 64
     fwd_k1          k=1 layer 64 -> 64 on that output
     dinput_subm     dinput of the k=3 layer
@@ -14,6 +14,11 @@ It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
     fwd_strided     SparseConv3d forward 64 -> 128
     dinput_strided  its dinput
     dfilter_strided its dfilter
+
+The strided layer's kernel map depends on the coordinates only, so the step
+builds it on a second stream, issued after the SubM forward, while the SubM
+layer's remaining stages run; the strided layer waits for it.  Running the
+SubM dinput and dfilter side by side as well was slower (each fills the GPU).
 
 ``--workload shells`` runs the same stages on the mesh-shell sets: 4 x 128^3,
 bf16, 128 channels, with k=1 128 -> 128.  The strided layer there is 128 -> 128.
@@ -134,6 +139,7 @@ class Step:
         self.names = ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm",
                       "kmap_strided", "fwd_strided", "dinput_strided", "dfilter_strided")
         self.ev = None
+        self.side = None             # second stream of the step (created on first use)
         self.km, self.ks = None, km  # maps held for kernel_ms (the SubM one is built on first use)
 
     def kernel_ms(self, stage: str, reps: int = KERNEL_REPS) -> float:
@@ -155,19 +161,33 @@ class Step:
         return self.time_launch(launch, reps)
 
     def run(self, events=None):
-        spc, inp = self.spc, self.inp
+        """One step.  The strided layer's kernel map depends on the coordinates
+        only, so it is built on a second stream (default priority) while the
+        SubM layer runs; the main stream waits for it before the strided layer.
+        Each stage's events are recorded on the stream it runs on."""
+        spc, inp, torch = self.spc, self.inp, self.torch
         E = events or {}
+        main = torch.cuda.current_stream()
+        if self.side is None:
+            self.side = torch.cuda.Stream()
+        side = self.side
 
         def mark(name, i):
             if name in E:
                 E[name][i].record()
 
+        side.wait_stream(main)   # the previous step's users of the side stream's buffers are done
         mark("kmap_subm", 0)
         km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         mark("kmap_subm", 1)
         mark("fwd_subm", 0)
         y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
         mark("fwd_subm", 1)
+        with torch.cuda.stream(side):
+            mark("kmap_strided", 0)
+            ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
+                                orders=True)
+            mark("kmap_strided", 1)
         mark("fwd_k1", 0)
         spc.subm_conv_fwd(y, self.w1, None, None)
         mark("fwd_k1", 1)
@@ -177,10 +197,7 @@ class Step:
         mark("dfilter_subm", 0)
         spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
         mark("dfilter_subm", 1)
-        mark("kmap_strided", 0)
-        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
-                            orders=True)
-        mark("kmap_strided", 1)
+        main.wait_stream(side)
         mark("fwd_strided", 0)
         spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"], ks["order"])
         mark("fwd_strided", 1)
