@@ -53,7 +53,7 @@ struct KGeom {
     // K, the strides, and the output grid's x extent, plane and volume
     uint64_t mK, msz, msy, msx, mox, mplane, mvol;
     int32_t occ;                 // input occupancy bitmap in use (see make_plan)
-    int32_t dense;               // ... and, beside it, the index grid as the table
+    int32_t dense;               // ... and, beside it, the index grid as the table (both or neither)
 };
 
 // ceil(2^64 / d) for d >= 2, 0 for d == 1 (see qdiv)
@@ -255,9 +255,10 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
     nbr[t] = v;
 }
 
-// Popcount of each thread's WORDS_PER_THREAD bitmap words, summed per block.
+// Popcount of each thread's WORDS_PER_THREAD bitmap words, summed per block
+// into block_sums and added to *total (zeroed beforehand).
 __global__ __launch_bounds__(KB) void k_bitmap_count(const uint32_t* __restrict__ bitmap, int64_t nwords,
-                                                     int32_t* __restrict__ block_sums) {
+                                                     int32_t* __restrict__ block_sums, uint32_t* total) {
     __shared__ int32_t red[KB / WAVE];
     const int64_t w0 = (int64_t(blockIdx.x) * KB + threadIdx.x) * WORDS_PER_THREAD;
     int s = 0;
@@ -273,6 +274,7 @@ __global__ __launch_bounds__(KB) void k_bitmap_count(const uint32_t* __restrict_
         int t = 0;
         for (int w = 0; w < KB / WAVE; ++w) t += red[w];
         block_sums[blockIdx.x] = t;
+        if (t) atomicAdd(total, uint32_t(t));
     }
 }
 
@@ -331,23 +333,33 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_scan(int32_t* __restrict__ dat
 }
 
 // Writes each word's exclusive rank prefix and the output coordinates of
-// its set bits, in (b, z, y, x) order (coordinates only if M <= cap).
+// its set bits, in (b, z, y, x) order (coordinates only if M <= cap).  The
+// block's first rank is block_offs[block] when `scanned`, else the sum of
+// the earlier blocks' counts in block_offs, added up here (few blocks).
 __global__ __launch_bounds__(KB) void k_bitmap_emit(const uint32_t* __restrict__ bitmap, int64_t nwords,
-                                                    const int32_t* __restrict__ block_offs,
+                                                    const int32_t* __restrict__ block_offs, int32_t scanned,
                                                     uint32_t* __restrict__ prefix, int4* __restrict__ out_coords,
                                                     int64_t cap, const uint32_t* hdr, KGeom g) {
     __shared__ int waves[KB / WAVE];
     const int64_t w0 = (int64_t(blockIdx.x) * KB + threadIdx.x) * WORDS_PER_THREAD;
     uint32_t w[WORDS_PER_THREAD] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int s = 0;
     if (w0 < nwords) {
         const u32x4 a = ld16(bitmap + w0), b = ld16(bitmap + w0 + 4);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-        for (int j = 0; j < WORDS_PER_THREAD; ++j) s += __popc(w[j]);
     }
+    int first;
+    if (scanned) {
+        first = block_offs[blockIdx.x];
+    } else {
+        int e = 0;
+        for (int j = threadIdx.x; j < int(blockIdx.x); j += KB) e += block_offs[j];
+        block_exclusive_scan<KB>(e, waves, first);
+    }
+    int s = 0;
+    for (int j = 0; j < WORDS_PER_THREAD; ++j) s += __popc(w[j]);
     int total;
-    int run = block_offs[blockIdx.x] + block_exclusive_scan<KB>(s, waves, total);
+    int run = first + block_exclusive_scan<KB>(s, waves, total);
     if (w0 >= nwords) return;
     const bool emit = int64_t(hdr[H_NOUT]) <= cap;
     const uint32_t plane = uint32_t(g.oy) * uint32_t(g.ox), vol = plane * uint32_t(g.oz);
@@ -422,6 +434,7 @@ __global__ __launch_bounds__(KB) void k_strided_maps(const int4* __restrict__ co
 // K <= ROWPASS_KMAX); a row stride of K words is conflict-free for odd K.
 // rows < 0: read M from the header.
 constexpr int ROWPASS_KMAX = 27;
+constexpr int64_t EMIT_SUM_BLOCKS = 2048;   // up to this many bitmap blocks, emit sums the earlier counts itself
 
 __global__ __launch_bounds__(KB) void k_row_pass(const int32_t* __restrict__ map, int32_t rows, int K,
                                                  int64_t cap, const uint32_t* hdr, uint32_t* __restrict__ keys,
@@ -473,23 +486,26 @@ __device__ __noinline__ int32_t table_find_after(const uint64_t* __restrict__ ta
     return -1;
 }
 
-// Submanifold map and row pass in one kernel, for K <= ROWPASS_KMAX: one
-// thread per row.  The K lookups of a row are issued together, so a wave has
-// all its rows' lookups in flight at once: with the index grid, the K
-// occupancy words, then the grid cells of the occupied neighbours; with the
-// hash, the keys' home slots, which answer nearly every probe at load factor
-// <= 1/4 (the few longer probe sequences continue afterwards).  Entries go to an LDS tile (row
-// stride K words) and leave as coalesced row-major stores; the thread then has
-// its row's mask (keys, K <= 32) and the block's per-offset hit counts
-// (counts[k*gridDim.x + block]), as k_row_pass makes them.  The centre entry
-// is the row itself.
-template <bool DENSE>
-__global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coords, int32_t n, KGeom g,
-                                                  const uint64_t* __restrict__ table, uint32_t mask,
-                                                  const uint32_t* __restrict__ occ,
-                                                  int32_t* __restrict__ nbr, uint32_t* __restrict__ keys,
-                                                  int32_t* __restrict__ counts, const uint32_t* hdr,
-                                                  int32_t* coord_err) {
+// Output-side map rows and their row pass in one kernel, for K <= ROWPASS_KMAX:
+// one thread per output row o, whose entry k is the input row at cell
+// o * stride - pad + k * dil (a submanifold map has stride 1 and pad K/2, and
+// its centre entry is the row itself).  The K lookups of a row are issued
+// together, so a wave has all its rows' lookups in flight at once: with the
+// index grid, the K occupancy words, then the grid cells of the occupied
+// neighbours; with the hash, the keys' home slots, which answer nearly every
+// probe at load factor <= 1/4 (the few longer probe sequences continue
+// afterwards).  Entries go to an LDS tile (row stride K words) and leave as
+// coalesced row-major stores; the thread then has its row's mask (keys,
+// K <= 32) and the block's per-offset hit counts (counts[k*gridDim.x +
+// block]), as k_row_pass makes them.  rows < 0: M from the header (rows
+// beyond the capacity read as none).
+template <bool DENSE, bool SUBM>
+__global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoords, int32_t rows, int64_t cap, KGeom g,
+                                                 const uint64_t* __restrict__ table, uint32_t mask,
+                                                 const uint32_t* __restrict__ occ,
+                                                 int32_t* __restrict__ nbr, uint32_t* __restrict__ keys,
+                                                 int32_t* __restrict__ counts, const uint32_t* hdr,
+                                                 int32_t* coord_err) {
     __shared__ uint32_t ktab[ROWPASS_KMAX];
     __shared__ int32_t cnt[ROWPASS_KMAX];
     __shared__ int32_t stage[KB * ROWPASS_KMAX];
@@ -500,16 +516,17 @@ __global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coord
         cnt[t] = 0;
     }
     __syncthreads();
+    if (rows < 0) rows = rows_within(hdr, cap);
     // workgroups go to the XCDs round-robin; XCD x takes a contiguous run of
-    // row blocks, so the grid cells its rows look up stay in its own L2
+    // row blocks, so the cells that its rows look up stay in its own L2
     const uint32_t nb = gridDim.x, xc = blockIdx.x % 8u, per = nb / 8u;
     const uint32_t lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
     const int32_t row0 = int32_t(lb) * KB, i = row0 + t;
     if (coord_err && i == 0) *coord_err = int32_t(hdr[H_FLAGS]);
-    if (row0 >= n) return;  // uniform per block (only an empty call launches one)
-    const bool live = i < n;
-    const int4 c = coords[live ? i : n - 1];
-    const bool ok = live && in_grid(c, g);
+    if (row0 >= rows) return;  // uniform per block
+    const bool live = i < rows;
+    const int4 c = rcoords[live ? i : rows - 1];
+    const bool ok = live && (!SUBM || in_grid(c, g));  // output sites lie inside their grid
     const int32_t* dense = reinterpret_cast<const int32_t*>(table);
     // 1. every lookup of the row, from valid addresses (cell 0 or its slot
     //    when the neighbour is outside the grid; such entries are -1 regardless)
@@ -519,10 +536,10 @@ __global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coord
 #pragma unroll
     for (int k = 0; k < ROWPASS_KMAX; ++k) {
         const uint32_t kk = ktab[k < K ? k : 0];
-        const int z = c.y + int(kk >> 6) - g.kz / 2, y = c.z + int((kk >> 3) & 7) - g.ky / 2,
-                  x = c.w + int(kk & 7) - g.kx / 2;
-        const bool in = ok && k < K && k != K / 2 && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y &&
-                        (unsigned)x < (unsigned)g.X;
+        const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy,
+                  x = c.w * g.sx - g.px + int(kk & 7) * g.dx;
+        const bool in = ok && k < K && !(SUBM && k == K / 2) && (unsigned)z < (unsigned)g.Z &&
+                        (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X;
         key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
         inside |= uint32_t(in) << k;
         got[k] = DENSE ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coord
     for (int k = 0; k < ROWPASS_KMAX; ++k) {
         if (k >= K) continue;
         int32_t v = -1;
-        if (k == K / 2) {
+        if (SUBM && k == K / 2) {
             v = ok ? i : -1;
         } else if ((inside >> k) & 1u) {
             if (DENSE) {
@@ -561,8 +578,8 @@ __global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coord
         const int k = __ffs(pending) - 1;
         pending &= pending - 1;
         const uint32_t kk = ktab[k];
-        const int z = c.y + int(kk >> 6) - g.kz / 2, y = c.z + int((kk >> 3) & 7) - g.ky / 2,
-                  x = c.w + int(kk & 7) - g.kx / 2;
+        const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy,
+                  x = c.w * g.sx - g.px + int(kk & 7) * g.dx;
         const uint32_t q = in_key(c.x, z, y, x, g);
         const int32_t v = table_find_after(table, mask, q, home_slot(q) & mask);
         srow[k] = v;
@@ -578,13 +595,73 @@ __global__ __launch_bounds__(KB) void k_subm_rows(const int4* __restrict__ coord
     if (keys && live) keys[i] = m;
     __syncthreads();
     // 4. the block's rows, row-major, coalesced
-    const int64_t lo = int64_t(row0) * K, len = int64_t(min(n, row0 + KB) - row0) * K;
+    const int64_t lo = int64_t(row0) * K, len = int64_t(min(rows, row0 + KB) - row0) * K;
 #pragma unroll
     for (int e = 0; e < ROWPASS_KMAX; ++e) {
         const int j = e * KB + t;
         if (j < len) nbr[lo + j] = stage[j];
     }
     if (counts && t < K) counts[int64_t(t) * gridDim.x + lb] = cnt[t];
+}
+
+// Input-side rows of a strided map and their masks, for K <= ROWPASS_KMAX: one
+// thread per input row i, whose entry k is the row of the output site
+// o = (c + pad - k * dil) / stride when that division is exact on every axis
+// and o lies in the output grid, else -1.  Every such site has its bitmap bit
+// set, so its row is its rank: prefix[word] + the set bits below it.  Both
+// words of all K entries are requested together; the rows leave through LDS
+// as coalesced stores and the masks go to keys (K <= 32).  Nothing is written
+// when M exceeds the capacity.
+__global__ __launch_bounds__(KB) void k_in_rows(const int4* __restrict__ coords, int32_t n, int64_t cap, KGeom g,
+                                                const uint32_t* __restrict__ bitmap,
+                                                const uint32_t* __restrict__ prefix, int32_t* __restrict__ nbr_in,
+                                                uint32_t* __restrict__ keys, const uint32_t* hdr) {
+    __shared__ uint32_t ktab[ROWPASS_KMAX];
+    __shared__ int32_t stage[KB * ROWPASS_KMAX];
+    const int K = g.kz * g.ky * g.kx;
+    const int t = threadIdx.x;
+    if (t < K) ktab[t] = uint32_t((t / (g.kx * g.ky)) << 6 | ((t / g.kx) % g.ky) << 3 | (t % g.kx));
+    __syncthreads();
+    const int32_t row0 = blockIdx.x * KB, i = row0 + t;
+    if (row0 >= n || int64_t(hdr[H_NOUT]) > cap) return;  // uniform per block
+    const bool live = i < n;
+    const int4 c = coords[live ? i : n - 1];
+    const bool ok = live && in_grid(c, g);
+    uint32_t bitpos[ROWPASS_KMAX], bits[ROWPASS_KMAX], pre[ROWPASS_KMAX];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int k = 0; k < ROWPASS_KMAX; ++k) {
+        const uint32_t kk = ktab[k < K ? k : 0];
+        const int nz = c.y + g.pz - int(kk >> 6) * g.dz, ny = c.z + g.py - int((kk >> 3) & 7) * g.dy,
+                  nx = c.w + g.px - int(kk & 7) * g.dx;
+        const int oz = nz >= 0 ? int(qdiv(uint32_t(nz), g.msz)) : -1;
+        const int oy = ny >= 0 ? int(qdiv(uint32_t(ny), g.msy)) : -1;
+        const int ox = nx >= 0 ? int(qdiv(uint32_t(nx), g.msx)) : -1;
+        const bool in = ok && k < K && oz >= 0 && oy >= 0 && ox >= 0 && oz * g.sz == nz && oy * g.sy == ny &&
+                        ox * g.sx == nx && oz < g.oz && oy < g.oy && ox < g.ox;
+        const uint32_t key = in ? out_key(c.x, oz, oy, ox, g) : 0u;
+        valid |= uint32_t(in) << k;
+        bitpos[k] = key & 31u;
+        bits[k] = bitmap[key >> 5];
+        pre[k] = prefix[key >> 5];
+    }
+    uint32_t m = 0;
+    int32_t* srow = stage + t * K;
+#pragma unroll
+    for (int k = 0; k < ROWPASS_KMAX; ++k) {
+        if (k >= K) continue;
+        const bool in = (valid >> k) & 1u;
+        srow[k] = in ? int32_t(pre[k] + __popc(bits[k] & ((1u << bitpos[k]) - 1u))) : -1;
+        if (in) m |= 1u << k;
+    }
+    if (keys && live) keys[i] = m;
+    __syncthreads();
+    const int64_t lo = int64_t(row0) * K, len = int64_t(min(n, row0 + KB) - row0) * K;
+#pragma unroll
+    for (int e = 0; e < ROWPASS_KMAX; ++e) {
+        const int j = e * KB + t;
+        if (j < len) nbr_in[lo + j] = stage[j];
+    }
 }
 
 // Ordered compaction of one block of map rows into the CSR pair lists: for
@@ -606,9 +683,11 @@ __global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict_
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     if (masks) {
         __shared__ int32_t stage[KB * ROWPASS_KMAX];
+        __shared__ int32_t soff[ROWPASS_KMAX];
         const uint32_t m = live ? masks[o] : 0u;
         const uint64_t lt = (1ull << lane) - 1ull;
         const int32_t row0 = blockIdx.x * KB;
+        if (threadIdx.x < K) soff[threadIdx.x] = offs[int64_t(threadIdx.x) * gridDim.x + blockIdx.x];
         if (row0 < rows) {
             const int64_t lo = int64_t(row0) * K, hi = int64_t(min(rows, row0 + KB)) * K;
             int32_t v[ROWPASS_KMAX];
@@ -629,7 +708,7 @@ __global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict_
             if (!hit) continue;
             int before = 0;
             for (int w = 0; w < wave; ++w) before += wcnt[k][w];
-            const int64_t at = int64_t(offs[int64_t(k) * gridDim.x + blockIdx.x]) + before + __popcll(b & lt);
+            const int64_t at = int64_t(soff[k]) + before + __popcll(b & lt);
             pair_in[at] = stage[threadIdx.x * K + k];
             pair_out[at] = o;
         }
@@ -728,25 +807,23 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
         return fail(SPC_ERR_UNSUPPORTED, "K*n_in=%lld must be below 2^31", (long long)(int64_t(p.K) * n_in));
     p.n = n_in;
     // The input table.  A grid of at most OCC_CELLS_PER_ROW cells per input row
-    // gets an occupancy bitmap (one bit per cell, at most 512 bytes per row to
-    // clear): an insert sets its bit with one atomic OR, whose old value
-    // flags a duplicate.  A submanifold map (grid of at most DENSE_MAX_BYTES)
-    // keeps beside it the index grid, one int32 row per cell, written at the
-    // occupied cells only and read only where the bitmap says occupied, so it
-    // is never cleared; a probe is a bitmap word (the bitmap is small enough
-    // to stay in L2) and, for an occupied cell, one grid load.  The strided
-    // path needs the input table only for duplicates.  Larger, sparser grids
-    // get the hash: load factor <= 1/4 keeps unsuccessful probes (most of them)
-    // near one load.  The table region is cap 8-byte words.
-    const bool occ = in_vol <= OCC_CELLS_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1));
-    k.dense = g.subm && occ && in_vol * 4 <= DENSE_MAX_BYTES;
-    k.occ = g.subm ? k.dense : occ;
+    // (and an index grid of at most DENSE_MAX_BYTES) gets an occupancy bitmap,
+    // one bit per cell and at most 512 bytes per row to clear, and beside it
+    // the index grid, one int32 row per cell.  An insert sets its bit with one
+    // atomic OR, whose old value flags a duplicate, and stores its row in the
+    // grid; the grid is read only where the bitmap says occupied, so it is
+    // never cleared.  A lookup is a bitmap word and, for an occupied cell, one
+    // grid load.  Larger, sparser grids get the hash: load factor <= 1/4 keeps
+    // unsuccessful probes (most of them) near one load.  The table region is
+    // cap 8-byte words.
+    k.dense = in_vol <= OCC_CELLS_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1)) && in_vol * 4 <= DENSE_MAX_BYTES;
+    k.occ = k.dense;
     p.occ_words = k.occ ? int64_t(ceil_div(int64_t(in_vol), 128) * 4) : 0;
     p.cap_log2 = 6;
     while ((int64_t(1) << p.cap_log2) < 4 * n_in) ++p.cap_log2;
     p.cap = k.dense ? int64_t((in_vol + 1) / 2) : k.occ ? 0 : int64_t(1) << p.cap_log2;
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
-    p.nwords = g.subm ? 0 : ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb;
+    p.nwords = g.subm ? 0 : std::max<int64_t>(wpb, ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb);
     p.bm_blocks = p.nwords / wpb;
     p.m_max = g.subm ? n_in : std::min<int64_t>(int64_t(p.K) * n_in, p.out_vol);
     p.rows_max = std::max(n_in, p.m_max);
@@ -1023,10 +1100,12 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
 
     if (subm && p.K <= ROWPASS_KMAX) {
         // probes, masks and counts in one pass over the rows
-        hipLaunchKernelGGL(p.g.dense ? k_subm_rows<true> : k_subm_rows<false>, dim3(unsigned(std::max(nblk, 1))),
-                           dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, nbr, (pairs || order) ? s.mask[0] : nullptr,
-                           pairs ? s.counts : nullptr, s.hdr, coord_err);
-        SPC_LAUNCHED("k_subm_rows");
+        auto rows_kernel = p.g.dense ? k_out_rows<true, true> : k_out_rows<false, true>;
+        hipLaunchKernelGGL(rows_kernel, dim3(unsigned(std::max(nblk, 1))), dim3(KB), 0, stream, c4, n, int64_t(n), p.g,
+                           table, mask,
+                           occ, nbr, (pairs || order) ? s.mask[0] : nullptr, pairs ? s.counts : nullptr, s.hdr,
+                           coord_err);
+        SPC_LAUNCHED("k_out_rows");
         if (pairs) {
             st = map_pairs(p, nbr, n, n, n, s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
@@ -1061,14 +1140,18 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         return SPC_OK;
     }
 
-    // strided: output sites into the bitmap, then count them (total -> hdr)
-    if (p.bm_blocks > 0) {
-        hipLaunchKernelGGL(k_bitmap_count, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums);
-        SPC_LAUNCHED("k_bitmap_count");
+    // strided: output sites into the bitmap, then count them (total -> hdr,
+    // by atomics; the per-block counts are scanned separately only for large
+    // bitmaps, else each emit block sums the counts before it)
+    hipLaunchKernelGGL(k_bitmap_count, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums,
+                       s.hdr + H_NOUT);
+    SPC_LAUNCHED("k_bitmap_count");
+    const bool scanned = p.bm_blocks > EMIT_SUM_BLOCKS;
+    if (scanned) {
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, bsums, p.bm_blocks, (int32_t*)nullptr, 0,
+                           int64_t(0), (uint32_t*)nullptr);
+        SPC_LAUNCHED("k_scan");
     }
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, bsums, p.bm_blocks, (int32_t*)nullptr, 0,
-                       int64_t(0), s.hdr + H_NOUT);
-    SPC_LAUNCHED("k_scan");
     // M and the flags are final here: their copy goes first, and the host waits
     // for it alone once everything else is enqueued
     HostCount* hc = nullptr;
@@ -1080,27 +1163,47 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         // M on the device (a count above the capacity reads as 0), so nothing
         // after this point waits for the host.
         const int64_t cap = std::min<int64_t>(out_cap, p.m_max);
-        if (p.bm_blocks > 0) {
-            hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords,
-                               bsums, prefix, reinterpret_cast<int4*>(out_coords), int64_t(out_cap), s.hdr, p.g);
-            SPC_LAUNCHED("k_bitmap_emit");
-        }
-        hipLaunchKernelGGL(k_fill_map, dim3(grid_for(cap * p.K, KB, 4096)), dim3(KB), 0, stream, nbr, p.K,
-                           int64_t(out_cap), s.hdr);
-        SPC_LAUNCHED("k_fill_map");
-        hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
-                           stream, c4, n, int64_t(out_cap), p.g, bitmap, prefix, nbr, nbr_in, s.hdr, coord_err);
-        SPC_LAUNCHED("k_strided_maps");
-        // the input-side order (its own row pass and sort) runs beside the rest
+        hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums,
+                           int32_t(scanned), prefix, reinterpret_cast<int4*>(out_coords), int64_t(out_cap), s.hdr, p.g);
+        SPC_LAUNCHED("k_bitmap_emit");
         Side* sd = nullptr;
-        if (order_in) {
-            if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
-            st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, sd->stream);
-            if (st != SPC_OK) return st;
-        }
-        if (pairs || order) {
-            st = row_pass(p, nbr, -1, cap, int64_t(out_cap), s, s.mask[0], pairs ? s.counts : nullptr, stream);
-            if (st != SPC_OK) return st;
+        if (p.K <= ROWPASS_KMAX) {
+            // the input side (nbr_in, its masks and its order) runs beside the
+            // output side, whose rows gather their entries through the input
+            // table, with their masks and counts
+            if (nbr_in && n > 0) {
+                if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
+                hipLaunchKernelGGL(k_in_rows, dim3(unsigned(nblk)), dim3(KB), 0, sd->stream, c4, n, int64_t(out_cap),
+                                   p.g, bitmap, prefix, nbr_in, order_in ? s.mask[1] : nullptr, s.hdr);
+                SPC_LAUNCHED("k_in_rows");
+                if (order_in && (st = sort_rows(p, nbr_in, n, n, n, s, true, 1, order_in, sd->stream)) != SPC_OK)
+                    return st;
+            }
+            auto rows_kernel = p.g.dense ? k_out_rows<true, false> : k_out_rows<false, false>;
+            hipLaunchKernelGGL(rows_kernel, dim3(unsigned(std::max<int64_t>(ceil_div(cap, KB), 1))), dim3(KB), 0, stream,
+                               reinterpret_cast<const int4*>(out_coords), -1, int64_t(out_cap), p.g, table, mask, occ,
+                               nbr, (pairs || order) ? s.mask[0] : nullptr, pairs ? s.counts : nullptr, s.hdr,
+                               coord_err);
+            SPC_LAUNCHED("k_out_rows");
+        } else {
+            // larger kernels: the output-side map is the transpose of the
+            // input-side one, scattered into a map filled with -1
+            hipLaunchKernelGGL(k_fill_map, dim3(grid_for(cap * p.K, KB, 4096)), dim3(KB), 0, stream, nbr, p.K,
+                               int64_t(out_cap), s.hdr);
+            SPC_LAUNCHED("k_fill_map");
+            hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB),
+                               0, stream, c4, n, int64_t(out_cap), p.g, bitmap, prefix, nbr, nbr_in, s.hdr, coord_err);
+            SPC_LAUNCHED("k_strided_maps");
+            // the input-side order (its own row pass and sort) runs beside the rest
+            if (order_in) {
+                if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
+                st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, sd->stream);
+                if (st != SPC_OK) return st;
+            }
+            if (pairs || order) {
+                st = row_pass(p, nbr, -1, cap, int64_t(out_cap), s, s.mask[0], pairs ? s.counts : nullptr, stream);
+                if (st != SPC_OK) return st;
+            }
         }
         // the output-side sort needs only the row pass's masks, so it runs beside
         // the pair compaction (which reads the masks too, and writes neither the
