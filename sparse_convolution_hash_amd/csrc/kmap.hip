@@ -73,7 +73,7 @@ __device__ __forceinline__ void offset_table(uint32_t* ktab, const KGeom& g, int
 }
 
 // Header at the start of the workspace.
-enum { H_FLAGS = 0, H_NOUT = 1, H_WORDS = 64 };
+enum { H_FLAGS = 0, H_NOUT = 1, H_TOT = 32, H_WORDS = 64 };   // H_TOT: per-offset pair totals (K <= 32)
 
 __device__ __forceinline__ uint32_t mix32(uint32_t k) {
     // murmur3's 32-bit finaliser
@@ -278,15 +278,18 @@ __global__ __launch_bounds__(KB) void k_bitmap_count(const uint32_t* __restrict_
     }
 }
 
-// One-workgroup exclusive scan of data[0, L) in place, in chunks of
-// SCAN_THREADS * SCAN_PER_THREAD values staged through LDS (coalesced loads
-// and stores; each thread scans a contiguous run of the chunk).
-// With ptr != NULL, ptr[k] = data[k * nblk] (after the scan) for k < K and
-// ptr[K] = total: the CSR offsets of a (offset, block) count matrix.
-// With total_out != NULL the total is also stored there.
+// Exclusive scan of data[0, L) in place, in chunks of SCAN_THREADS *
+// SCAN_PER_THREAD values staged through LDS (coalesced loads and stores;
+// each thread scans a contiguous run of the chunk).  Workgroup b of a larger
+// grid scans its own segment data[b*L, (b+1)*L) (the rows of a [K][nblk]
+// count matrix, one per offset).  With ptr != NULL (one workgroup),
+// ptr[k] = data[k * nblk] (after the scan) for k < K and ptr[K] = total: the
+// CSR offsets of a (offset, block) count matrix.  With total_out != NULL the
+// segment's total is stored at total_out[b].
 __global__ __launch_bounds__(SCAN_THREADS) void k_scan(int32_t* __restrict__ data, int64_t L, int32_t* ptr,
                                                        int K, int64_t nblk, uint32_t* total_out) {
     constexpr int CH = SCAN_THREADS * SCAN_PER_THREAD;
+    data += int64_t(blockIdx.x) * L;
     __shared__ int waves[SCAN_THREADS / WAVE];
     __shared__ int buf[CH];
     int carry = 0;
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_scan(int32_t* __restrict__ dat
         for (int k = threadIdx.x; k < K; k += SCAN_THREADS) ptr[k] = nblk > 0 ? data[int64_t(k) * nblk] : 0;
         if (threadIdx.x == 0) ptr[K] = carry;
     }
-    if (total_out && threadIdx.x == 0) *total_out = uint32_t(carry);
+    if (total_out && threadIdx.x == 0) total_out[blockIdx.x] = uint32_t(carry);
 }
 
 // Writes each word's exclusive rank prefix and the output coordinates of
@@ -523,7 +526,10 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     const uint32_t lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
     const int32_t row0 = int32_t(lb) * KB, i = row0 + t;
     if (coord_err && i == 0) *coord_err = int32_t(hdr[H_FLAGS]);
-    if (row0 >= rows) return;  // uniform per block
+    if (row0 >= rows) {  // uniform per block: a block past M (capacity above M) has no hits
+        if (counts && t < K) counts[int64_t(t) * gridDim.x + lb] = 0;
+        return;
+    }
     const bool live = i < rows;
     const int4 c = rcoords[live ? i : rows - 1];
     const bool ok = live && (!SUBM || in_grid(c, g));  // output sites lie inside their grid
@@ -666,17 +672,20 @@ __global__ __launch_bounds__(KB) void k_in_rows(const int4* __restrict__ coords,
 
 // Ordered compaction of one block of map rows into the CSR pair lists: for
 // each offset k, the block's hits go to the scanned offset offs[k*nblk +
-// block] in ascending row order.  With masks (K <= 32) the ranks of all
-// offsets come from one ballot each and a single barrier; otherwise one
-// block scan per offset.  rows < 0: read M from the header.
+// block] in ascending row order.  With masks (K <= ROWPASS_KMAX) the ranks of
+// all offsets come from one ballot each and a single barrier, and offs holds
+// per-offset scans whose totals are at hdr[H_TOT + k]: the block adds their
+// prefix, and block 0 writes the CSR offsets to pair_ptr.  Otherwise offs is
+// one scan of the whole matrix and there is one block scan per offset.
+// rows < 0: read M from the header.
 __global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict__ map, int32_t rows, int K,
                                                       int64_t cap, const uint32_t* hdr,
                                                       const uint32_t* __restrict__ masks,
                                                       const int32_t* __restrict__ offs,
                                                       int32_t* __restrict__ pair_in,
-                                                      int32_t* __restrict__ pair_out) {
+                                                      int32_t* __restrict__ pair_out, int32_t* pair_ptr) {
     __shared__ int waves[KB / WAVE];
-    __shared__ int wcnt[MASK_BITS][KB / WAVE];
+    __shared__ int wcnt[ROWPASS_KMAX][KB / WAVE];
     if (rows < 0) rows = rows_within(hdr, cap);
     const int32_t o = blockIdx.x * KB + threadIdx.x;
     const bool live = o < rows;
@@ -687,7 +696,16 @@ __global__ __launch_bounds__(KB) void k_compact_pairs(const int32_t* __restrict_
         const uint32_t m = live ? masks[o] : 0u;
         const uint64_t lt = (1ull << lane) - 1ull;
         const int32_t row0 = blockIdx.x * KB;
-        if (threadIdx.x < K) soff[threadIdx.x] = offs[int64_t(threadIdx.x) * gridDim.x + blockIdx.x];
+        if (wave == 0) {  // this block's slot per offset: the offsets before it, then the blocks before it
+            const int32_t tk = lane < K ? int32_t(hdr[H_TOT + lane]) : 0;
+            int incl = tk;
+            for (int off = 1; off < WAVE; off <<= 1) {
+                const int u = __shfl_up(incl, off);
+                if (lane >= off) incl += u;
+            }
+            if (lane < K) soff[lane] = incl - tk + offs[int64_t(lane) * gridDim.x + blockIdx.x];
+            if (blockIdx.x == 0 && lane <= K) pair_ptr[lane] = incl - tk;
+        }
         if (row0 < rows) {
             const int64_t lo = int64_t(row0) * K, hi = int64_t(min(rows, row0 + KB)) * K;
             int32_t v[ROWPASS_KMAX];
@@ -985,12 +1003,18 @@ spc_status join_from(Side* sd, hipStream_t stream) {
 spc_status map_pairs(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
                      const Scratch& s, int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, hipStream_t stream) {
     const int64_t blk = ceil_div(rows_cap, KB);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, s.counts, int64_t(p.K) * blk, pair_ptr, p.K,
-                       blk, (uint32_t*)nullptr);
+    const bool masked = p.K <= ROWPASS_KMAX && blk > 0;
+    if (masked) {  // each offset's row of the count matrix scanned by its own workgroup
+        hipLaunchKernelGGL(k_scan, dim3(unsigned(p.K)), dim3(SCAN_THREADS), 0, stream, s.counts, blk,
+                           (int32_t*)nullptr, 0, int64_t(0), s.hdr + H_TOT);
+    } else {
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, s.counts, int64_t(p.K) * blk, pair_ptr,
+                           p.K, blk, (uint32_t*)nullptr);
+    }
     SPC_LAUNCHED("k_scan");
     if (blk > 0) {
         hipLaunchKernelGGL(k_compact_pairs, dim3(unsigned(blk)), dim3(KB), 0, stream, map, rows_dev, p.K, cap, s.hdr,
-                           p.K <= ROWPASS_KMAX ? s.mask[0] : nullptr, s.counts, pair_in, pair_out);
+                           masked ? s.mask[0] : nullptr, s.counts, pair_in, pair_out, pair_ptr);
         SPC_LAUNCHED("k_compact_pairs");
     }
     return SPC_OK;

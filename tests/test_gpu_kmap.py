@@ -114,6 +114,23 @@ def test_strided_lidar_workload():
     assert torch.equal(res["nbr"], res2["nbr"]) and torch.equal(res["out_coords"], res2["out_coords"])
 
 
+def test_strided_capacity_above_the_count():
+    # a capacity above M sizes the launches by the capacity; the rows past M
+    # add nothing, and every result equals the exact-capacity call's
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    c = cuda(w.coords)
+    ref = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
+    big = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=ref["n_out"] + 1000, orders=True)
+    for key in ("out_coords", "nbr", "nbr_in", "pair_ptr", "order", "order_in"):
+        assert torch.equal(big[key], ref[key]), key
+    P = int(ref["pair_ptr"][-1])
+    assert torch.equal(big["pair_in"][:P], ref["pair_in"][:P]) and torch.equal(big["pair_out"][:P], ref["pair_out"][:P])
+    r = W.rng(77)
+    small = W.tiny_grid(r, 9, 0.3, 2)
+    m = spc.build_kmap(cuda(small), 2, (9, 9, 9), 3, 2, 1, 1, subm=False, pairs=False)["n_out"]
+    check_strided(small, 2, (9, 9, 9), 3, 2, 1, 1, out_cap=m + 600)
+
+
 def test_strided_golden_empty_output():
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "empty_strided_output.json")))
     res = spc.build_kmap(cuda(np.array(g["coords"], np.int32)), g["batch"], g["spatial_shape"], g["ksize"],
