@@ -16,8 +16,9 @@ It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
     dfilter_strided its dfilter
 
 The strided layer's kernel map depends on the coordinates only, so the step
-builds it on a second stream, issued after the SubM forward, while the SubM
-layer's remaining stages run; the strided layer waits for it.  Running the
+builds it first, on a second stream, while the main stream runs the SubM layer
+(and the previous step's tail); the strided layer waits for it.  Its maps are
+marked as used by the main stream, so their memory is not reused early.  Running the
 SubM dinput and dfilter side by side as well was slower (each fills the GPU).
 
 ``--workload shells`` runs the same stages on the mesh-shell sets: 4 x 128^3,
@@ -26,8 +27,11 @@ bf16, 128 channels, with k=1 128 -> 128.  The strided layer there is 128 -> 128.
 value = effective TFLOP/s of the whole step: 2 * pairs * Cin * Cout summed
 over the convolution stages (pairs counted from the kernel map, k=1 counts N
 pairs), divided by the step time.  The kernel-map rate is reported as voxels/s
-(N over the kmap_subm time).  Every stage is timed with HIP events on the
-stream the library launches on.  The roofline is given for the single-kernel
+(N over the kmap_subm time).  The K timed steps run bare; a second pass of K
+steps times every stage with HIP events on the stream it runs on (the event
+records cost host time, so that pass is not the timed one) and reports each
+stage's median.  With the two streams overlapping, a stage's time includes
+what it shares the GPU with.  The roofline is given for the single-kernel
 stage with the longest kernel: each such kernel is also launched back to back
 between two HIP events, behind a few ms of queued fills so that no host time
 between launches counts (the step's stage timings include host gaps, e.g. after
@@ -176,18 +180,21 @@ class Step:
             if name in E:
                 E[name][i].record()
 
-        side.wait_stream(main)   # the previous step's users of the side stream's buffers are done
+        with torch.cuda.stream(side):
+            mark("kmap_strided", 0)
+            ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
+                                orders=True)
+            mark("kmap_strided", 1)
+        # the main stream reads these maps: their memory is not reused before it is done
+        for t in ks.values():
+            if isinstance(t, torch.Tensor):
+                t.record_stream(main)
         mark("kmap_subm", 0)
         km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         mark("kmap_subm", 1)
         mark("fwd_subm", 0)
         y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
         mark("fwd_subm", 1)
-        with torch.cuda.stream(side):
-            mark("kmap_strided", 0)
-            ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
-                                orders=True)
-            mark("kmap_strided", 1)
         mark("fwd_k1", 0)
         spc.subm_conv_fwd(y, self.w1, None, None)
         mark("fwd_k1", 1)
@@ -492,18 +499,26 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    events = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)] for k in step.names}
-    stage_ms = {k: 0.0 for k in step.names}
+    # the timed steps, as a caller runs them (no per-stage instrumentation)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step.run({k: events[k][i] for k in step.names})
+        step.run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for k in step.names:
-        stage_ms[k] = sum(a.elapsed_time(b) for a, b in events[k]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+
+    # then the same number of steps with HIP events around every stage, for the
+    # per-stage breakdown (the event records cost host time, so this pass is
+    # not the timed one)
+    events = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)] for k in step.names}
+    stage_ms = {k: 0.0 for k in step.names}
+    for i in range(args.steps):
+        step.run({k: events[k][i] for k in step.names})
+    torch.cuda.synchronize()
+    for k in step.names:
+        stage_ms[k] = sorted(a.elapsed_time(b) for a, b in events[k])[args.steps // 2]   # median
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
