@@ -15,10 +15,10 @@ It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
     dinput_strided  its dinput
     dfilter_strided its dfilter
 
-The strided layer's kernel map depends on the coordinates only, so the step
-builds it first, on a second stream, while the main stream runs the SubM layer
-(and the previous step's tail); the strided layer waits for it.  Its maps are
-marked as used by the main stream, so their memory is not reused early.  Running the
+Both kernel maps depend on the coordinates only, so the step builds each on
+a stream of its own (default priority), SubM first, while the main stream
+finishes the previous step; each layer waits for its map.  The maps are marked
+as used by the main stream, so their memory is not reused early.  Running the
 SubM dinput and dfilter side by side as well was slower (each fills the GPU).
 
 ``--workload shells`` runs the same stages on the mesh-shell sets: 4 x 128^3,
@@ -143,7 +143,7 @@ class Step:
         self.names = ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm",
                       "kmap_strided", "fwd_strided", "dinput_strided", "dfilter_strided")
         self.ev = None
-        self.side = None             # second stream of the step (created on first use)
+        self.side = None             # the kernel maps' streams (created on first use)
         self.km, self.ks = None, km  # maps held for kernel_ms (the SubM one is built on first use)
 
     def kernel_ms(self, stage: str, reps: int = KERNEL_REPS) -> float:
@@ -173,25 +173,31 @@ class Step:
         E = events or {}
         main = torch.cuda.current_stream()
         if self.side is None:
-            self.side = torch.cuda.Stream()
-        side = self.side
+            self.side = (torch.cuda.Stream(), torch.cuda.Stream())
+        side_s, side_k = self.side
 
         def mark(name, i):
             if name in E:
                 E[name][i].record()
 
-        with torch.cuda.stream(side):
+        def used_on_main(maps):
+            # the main stream reads these maps: their memory is not reused before it is done
+            for t in maps.values():
+                if isinstance(t, torch.Tensor):
+                    t.record_stream(main)
+
+        with torch.cuda.stream(side_s):
+            mark("kmap_subm", 0)
+            km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
+            mark("kmap_subm", 1)
+        with torch.cuda.stream(side_k):
             mark("kmap_strided", 0)
             ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
                                 orders=True)
             mark("kmap_strided", 1)
-        # the main stream reads these maps: their memory is not reused before it is done
-        for t in ks.values():
-            if isinstance(t, torch.Tensor):
-                t.record_stream(main)
-        mark("kmap_subm", 0)
-        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
-        mark("kmap_subm", 1)
+        used_on_main(km)
+        used_on_main(ks)
+        main.wait_stream(side_s)
         mark("fwd_subm", 0)
         y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
         mark("fwd_subm", 1)
@@ -204,7 +210,7 @@ class Step:
         mark("dfilter_subm", 0)
         spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
         mark("dfilter_subm", 1)
-        main.wait_stream(side)
+        main.wait_stream(side_k)
         mark("fwd_strided", 0)
         spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"], ks["order"])
         mark("fwd_strided", 1)

@@ -20,10 +20,10 @@
  * - Every pointer except n_out / out_shape / bytes (and the host arrays of
  *   spc_point_to_voxel) is a DEVICE pointer owned by the caller; the library
  *   allocates no device memory.  Its only state between calls is per host
- *   thread: an error string and, per device, created on first use, two side
- *   streams with their events and 64 bytes of pinned host memory with an
- *   event (for the strided kernel map).  Device pointers must be 16-byte
- *   aligned.  Every launch is ordered on `stream` (NULL = the default stream).
+ *   thread: an error string and, per device, created on first use, 64 bytes
+ *   of pinned host memory with an event (for the strided kernel map's count).
+ *   Device pointers must be 16-byte aligned.  Every launch is on `stream`
+ *   (NULL = the default stream), in order.
  * - Errors: a call returns before any launch when its host-side checks fail,
  *   leaving outputs untouched; spc_last_error() then describes the failure.
  *   Only the strided spc_build_kmap (for the output count) and

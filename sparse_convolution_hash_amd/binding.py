@@ -109,11 +109,18 @@ def _check(status: int, func: str):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(dev: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    """The current stream's handle on `dev` (torch's raw accessor when it has
+    one: a Stream object per call costs host time on every launch)."""
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _need(t: torch.Tensor, name: str, dtype=None, dev=None):
@@ -144,9 +151,12 @@ def kmap_workspace(g: Geom, n_in: int) -> int:
     return b.value
 
 
-@functools.lru_cache(maxsize=64)
-def _kmap_workspace_cached(batch, shape, ksize, stride, pad, dil, subm, n_in) -> int:
-    return kmap_workspace(make_geom(batch, shape, ksize, stride, pad, dil, subm), n_in)
+@functools.lru_cache(maxsize=256)
+def _kmap_plan(batch, shape, ksize, stride, pad, dil, subm, n_in):
+    """(Geom, K, workspace bytes) of a kernel-map call; the Geom is shared and
+    never modified."""
+    g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
+    return g, int(g.ksize[0] * g.ksize[1] * g.ksize[2]), kmap_workspace(g, n_in)
 
 
 def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
@@ -168,69 +178,62 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
         raise ValueError("coords must be [N, 4]")
     dev = coords.device
     n = coords.shape[0]
-    g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
-    K = int(g.ksize[0] * g.ksize[1] * g.ksize[2])
-    ws_bytes = _kmap_workspace_cached(batch, tuple(_t3(shape)), tuple(_t3(ksize)), tuple(_t3(stride)),
-                                      tuple(_t3(pad)), tuple(_t3(dil)), bool(subm), n)
+    key = lambda v: v if isinstance(v, int) else tuple(v)
+    g, K, ws_bytes = _kmap_plan(int(batch), key(shape), key(ksize), key(stride), key(pad), key(dil), bool(subm), n)
     stream = _stream(dev)
     n_out = ctypes.c_int64(0)
     if not subm and out_cap is None:
         ws = workspace if workspace is not None and workspace.numel() >= ws_bytes else \
             torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-        st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, None, 0, ctypes.byref(n_out), None, None,
-                                  None, None, None, 0, None, None, None, _ptr(ws), ws.numel(), stream)
+        st = lib().spc_build_kmap(ctypes.byref(g), coords.data_ptr(), n, None, 0, ctypes.byref(n_out), None, None,
+                                  None, None, None, 0, None, None, None, ws.data_ptr(), ws.numel(), stream)
         _check(st, "spc_build_kmap")
         out_cap = n_out.value
         workspace = ws
     cap = n if subm else int(out_cap)
-    # every int32 output in one allocation (views start 256-byte aligned) and the
-    # workspace in a second one, which the results do not keep alive
-    sizes = {"err": 4, "nbr": max(K * cap, 4)}
+    # every int32 output in one allocation (each part starts 256-byte aligned)
+    # and the workspace in a second one, which the results do not keep alive;
+    # the library gets raw addresses, and the result views are made afterwards
+    parts = [("err", 4), ("nbr", max(K * cap, 4))]
     if not subm:
-        sizes["out_coords"] = max(cap, 1) * 4
-    if not subm and (with_nbr_in or orders):
-        sizes["nbr_in"] = max(n * K, 4)
+        parts.append(("out_coords", max(cap, 1) * 4))
+    want_nbr_in = not subm and (with_nbr_in or orders)
+    if want_nbr_in:
+        parts.append(("nbr_in", max(n * K, 4)))
     if orders:
-        sizes["order"] = max(cap, 4)
+        parts.append(("order", max(cap, 4)))
         if not subm:
-            sizes["order_in"] = max(n, 4)
+            parts.append(("order_in", max(n, 4)))
     if pairs:
-        sizes.update(pp=K + 1, pi=max(K * n, 4), po=max(K * n, 4))
+        parts += [("pp", K + 1), ("pi", max(K * n, 4)), ("po", max(K * n, 4))]
+    sizes = []
+    for _, v in parts:
+        sizes += [v, (-v) % 64]
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    offs, total = {}, 0
-    for k, v in sizes.items():
-        offs[k] = total
-        total += (v + 63) // 64 * 64
-    buf = torch.empty(total, dtype=torch.int32, device=dev)
-    view = lambda k: buf[offs[k]:offs[k] + sizes[k]]
-    err = view("err")
-    res = {"coord_err": err[:1]}
-    out_coords = None if subm else view("out_coords").view(-1, 4)
-    nbr = view("nbr")
-    nbr_in = view("nbr_in")[:n * K].view(n, K) if "nbr_in" in sizes else None
-    order = view("order") if orders else None
-    order_in = view("order_in") if "order_in" in sizes else None
-    pp = pi = po = None
-    if pairs:
-        pp, pi, po = view("pp"), view("pi"), view("po")
-    st = lib().spc_build_kmap(ctypes.byref(g), _ptr(coords), n, _ptr(out_coords), cap, ctypes.byref(n_out),
-                              _ptr(nbr), _ptr(nbr_in), _ptr(pp), _ptr(pi), _ptr(po), max(K * n, 0) if pairs else 0,
-                              _ptr(order), _ptr(order_in), _ptr(err), _ptr(workspace), workspace.numel(), stream)
+    buf = torch.empty(sum(sizes), dtype=torch.int32, device=dev)
+    base, addr, o = buf.data_ptr(), {}, 0
+    for i, (name, _) in enumerate(parts):
+        addr[name] = base + 4 * o
+        o += sizes[2 * i] + sizes[2 * i + 1]
+    a = addr.get
+    st = lib().spc_build_kmap(ctypes.byref(g), coords.data_ptr(), n, a("out_coords"), cap, ctypes.byref(n_out),
+                              a("nbr"), a("nbr_in"), a("pp"), a("pi"), a("po"), max(K * n, 0) if pairs else 0,
+                              a("order"), a("order_in"), a("err"), workspace.data_ptr(), workspace.numel(), stream)
     _check(st, "spc_build_kmap")
     m = int(n_out.value)
-    res["n_out"] = m
-    res["nbr"] = nbr[:K * m].view(m, K)
+    views = dict(zip((name for name, _ in parts), buf.split_with_sizes(sizes)[0::2]))
+    res = {"coord_err": views["err"][:1], "n_out": m, "nbr": views["nbr"][:K * m].view(m, K)}
     if not subm:
-        res["out_coords"] = out_coords[:m]
-    if nbr_in is not None:
-        res["nbr_in"] = nbr_in
+        res["out_coords"] = views["out_coords"][:4 * m].view(m, 4)
+    if want_nbr_in:
+        res["nbr_in"] = views["nbr_in"][:n * K].view(n, K)
     if orders:
-        res["order"] = order[:m]
-        if order_in is not None:
-            res["order_in"] = order_in[:n]
+        res["order"] = views["order"][:m]
+        if not subm:
+            res["order_in"] = views["order_in"][:n]
     if pairs:
-        res["pair_ptr"], res["pair_in"], res["pair_out"] = pp, pi, po
+        res["pair_ptr"], res["pair_in"], res["pair_out"] = views["pp"], views["pi"], views["po"]
     return res
 
 

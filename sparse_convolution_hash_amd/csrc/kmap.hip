@@ -868,8 +868,8 @@ inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 1 << 16)
     return unsigned(std::min<int64_t>(std::max<int64_t>(b, 1), cap));
 }
 
-// Buffers of one radix sort (the two sorts of a call run concurrently, so
-// each has its own).
+// Buffers of one radix sort (each of the two sorts of a strided call has its
+// own, so the input side's masks stay intact while the output side sorts).
 struct SortBuf {
     uint32_t* keys[2];
     int32_t* vals[2];
@@ -940,30 +940,6 @@ spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_
     return SPC_OK;
 }
 
-// Concurrent work of one call: side streams (per host thread, device and
-// index, default priority) forked from and joined back into the caller's
-// stream.
-struct Side {
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int N_SIDES = 2;
-
-spc_status side_for_device(Side** out, int which) {
-    static thread_local Side sides[64][N_SIDES];
-    int dev = 0;
-    SPC_HIP(hipGetDevice(&dev));
-    if (dev < 0 || dev >= 64) return fail(SPC_ERR_UNSUPPORTED, "device %d", dev);
-    Side& sd = sides[dev][which];
-    if (!sd.stream) {
-        SPC_HIP(hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking));
-        SPC_HIP(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
-        SPC_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
-    }
-    *out = &sd;
-    return SPC_OK;
-}
-
 // Pinned host words and an event per host thread and device: a strided call
 // copies M and the coordinate flags there as soon as they are known and waits
 // for that copy only, so the host returns while the rest of the map is built.
@@ -983,18 +959,6 @@ spc_status host_count_for_device(HostCount** out) {
         SPC_HIP(hipEventCreateWithFlags(&h.ev, hipEventDisableTiming));
     }
     *out = &h;
-    return SPC_OK;
-}
-
-spc_status fork_to(Side* sd, hipStream_t stream) {
-    SPC_HIP(hipEventRecord(sd->fork, stream));
-    SPC_HIP(hipStreamWaitEvent(sd->stream, sd->fork, 0));
-    return SPC_OK;
-}
-
-spc_status join_from(Side* sd, hipStream_t stream) {
-    SPC_HIP(hipEventRecord(sd->join, sd->stream));
-    SPC_HIP(hipStreamWaitEvent(stream, sd->join, 0));
     return SPC_OK;
 }
 
@@ -1150,8 +1114,6 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             st = row_pass(p, nbr, n, n, n, s, s.mask[0], pairs ? s.counts : nullptr, stream);
             if (st != SPC_OK) return st;
         }
-        // (a side stream for the sort does not pay here: the compaction it
-        // would overlap is short next to the cost of the fork and join)
         if (pairs) {
             st = map_pairs(p, nbr, n, n, n, s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
@@ -1190,17 +1152,19 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
         hipLaunchKernelGGL(k_bitmap_emit, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums,
                            int32_t(scanned), prefix, reinterpret_cast<int4*>(out_coords), int64_t(out_cap), s.hdr, p.g);
         SPC_LAUNCHED("k_bitmap_emit");
-        Side* sd = nullptr;
+        // Everything goes on the caller's stream: side streams inside the call
+        // overlapped the two sides' sorts on the GPU, but their fork and join
+        // events cost more host time than they saved; a caller overlaps whole
+        // maps with its other work instead.
         if (p.K <= ROWPASS_KMAX) {
-            // the input side (nbr_in, its masks and its order) runs beside the
-            // output side, whose rows gather their entries through the input
-            // table, with their masks and counts
+            // the input side (nbr_in, its masks and its order), then the output
+            // side, whose rows gather their entries through the input table,
+            // with their masks and counts
             if (nbr_in && n > 0) {
-                if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
-                hipLaunchKernelGGL(k_in_rows, dim3(unsigned(nblk)), dim3(KB), 0, sd->stream, c4, n, int64_t(out_cap),
+                hipLaunchKernelGGL(k_in_rows, dim3(unsigned(nblk)), dim3(KB), 0, stream, c4, n, int64_t(out_cap),
                                    p.g, bitmap, prefix, nbr_in, order_in ? s.mask[1] : nullptr, s.hdr);
                 SPC_LAUNCHED("k_in_rows");
-                if (order_in && (st = sort_rows(p, nbr_in, n, n, n, s, true, 1, order_in, sd->stream)) != SPC_OK)
+                if (order_in && (st = sort_rows(p, nbr_in, n, n, n, s, true, 1, order_in, stream)) != SPC_OK)
                     return st;
             }
             auto rows_kernel = p.g.dense ? k_out_rows<true, false> : k_out_rows<false, false>;
@@ -1218,10 +1182,9 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             hipLaunchKernelGGL(k_strided_maps, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB),
                                0, stream, c4, n, int64_t(out_cap), p.g, bitmap, prefix, nbr, nbr_in, s.hdr, coord_err);
             SPC_LAUNCHED("k_strided_maps");
-            // the input-side order (its own row pass and sort) runs beside the rest
+            // the input-side order (its own row pass and sort)
             if (order_in) {
-                if ((st = side_for_device(&sd, 0)) != SPC_OK || (st = fork_to(sd, stream)) != SPC_OK) return st;
-                st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, sd->stream);
+                st = sort_rows(p, nbr_in, n, n, n, s, false, 1, order_in, stream);
                 if (st != SPC_OK) return st;
             }
             if (pairs || order) {
@@ -1229,25 +1192,14 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                 if (st != SPC_OK) return st;
             }
         }
-        // the output-side sort needs only the row pass's masks, so it runs beside
-        // the pair compaction (which reads the masks too, and writes neither the
-        // masks nor the sort's buffers)
-        Side* so = nullptr;
         if (order) {
-            hipStream_t os = stream;
-            if (pairs) {
-                if ((st = side_for_device(&so, 1)) != SPC_OK || (st = fork_to(so, stream)) != SPC_OK) return st;
-                os = so->stream;
-            }
-            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, os);
+            st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }
         if (pairs) {
             st = map_pairs(p, nbr, -1, cap, int64_t(out_cap), s, pair_ptr, pair_in, pair_out, stream);
             if (st != SPC_OK) return st;
         }
-        if (so && (st = join_from(so, stream)) != SPC_OK) return st;
-        if (sd && (st = join_from(sd, stream)) != SPC_OK) return st;
     }
     SPC_HIP(hipEventSynchronize(hc->ev));
     const uint32_t host_hdr[2] = {hc->words[H_FLAGS], hc->words[H_NOUT]};
