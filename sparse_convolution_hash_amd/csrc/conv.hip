@@ -415,6 +415,9 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
     constexpr int E = TT::E;
     a.kch = int(ceil_div(a.CK / E, 4) * 4);
     const int KC = a.kch / 4;
+    // gathered-row registers sized to the contraction: a 2-step variant frees
+    // 32 registers per lane for contractions of up to 64 (16-bit) channels
+    if (KC <= 2) return launch_conv_k<TT, TRANS, 2>(a, stream);
     if (KC <= 4) return launch_conv_k<TT, TRANS, 4>(a, stream);
     if (KC <= 8) return launch_conv_k<TT, TRANS, 8>(a, stream);
     return fail(SPC_ERR_UNSUPPORTED, "contraction of %d channels exceeds %d for this dtype", a.CK, 8 * 4 * E);
