@@ -32,6 +32,20 @@ constexpr int NW = CT / WAVE;    // waves per workgroup
 constexpr int WAIT_VMCNT0 = 0x0F70;
 constexpr int KTILE = 28;        // offsets whose map rows are staged at once (a 3x3x3 kernel in one go)
 
+// Buffer loads (CDNA buffer addressing): a 16-byte load through a buffer
+// resource whose offset lies past the resource's range returns zeros without
+// a memory access, so a masked lane costs nothing and needs no branch.
+constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit elements (gfx9 family)
+constexpr uint32_t BUF_OOB = 0x80000000u;    // past any range below 2 GiB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), BUF_FLAGS);
+}
+
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+
 
 struct ConvArgs {
     const void* x;       // gathered operand [n_src, CK]
@@ -47,6 +61,8 @@ struct ConvArgs {
     int32_t kch;         // 16-byte chunks along CK, padded to a multiple of 4
     const void* res;     // residual [n_rows, CN] added before the activation, or NULL (may alias y)
     int32_t relu;        // ReLU on the final fp32 value
+    int32_t xbuf;        // x and the weights lie within 2 GiB (buffer loads can address them)
+    int32_t dense;       // a submanifold map: tiles hit many offsets each
 };
 
 // LDS slab layout: chunk row kb (16 bytes of CK per output channel) has BN
@@ -143,6 +159,22 @@ struct WStage {
             if (lofs[p] >= 0) load_at(r + p * ITEM_REGS, w, gofs[p], a.cout);
     }
 
+    // The same through the weights' buffer resource, without branches:
+    // padding and absent items, and every item when !live, take an
+    // out-of-range offset and load zeros without a memory access.
+    __device__ void load_buf(const ConvArgs& a, __amdgpu_buffer_rsrc_t wr, int ws, bool live) {
+        const uint32_t base = uint32_t(ws) * uint32_t(a.cin) * uint32_t(a.cout);
+#pragma unroll
+        for (int p = 0; p < PRE; ++p)
+#pragma unroll
+            for (int e = 0; e < ITEM_REGS; ++e) {
+                const uint32_t off = live && gofs[p] >= 0
+                                         ? (base + uint32_t(gofs[p] + e * a.cout)) * uint32_t(sizeof(S))
+                                         : BUF_OOB;
+                r[p * ITEM_REGS + e] = buf_ld16(wr, off);
+            }
+    }
+
     __device__ void store(char* lds, const ConvArgs& a, int ws, int col0) const {
 #pragma unroll
         for (int p = 0; p < PRE; ++p)
@@ -182,7 +214,31 @@ __device__ __forceinline__ bool gather_rows(u32x4 (&af)[RB][KCMAX], const ConvAr
     return __any(any);
 }
 
-template <typename TT, int RB, int NB, bool TRANS, int KCMAX>
+// gather_rows through x's buffer resource, without branches: a missing row
+// or a chunk past the contraction (every row when !live) takes an
+// out-of-range offset and loads zeros without a memory access.
+template <typename TT, int RB, int KCMAX>
+__device__ __forceinline__ bool gather_buf(u32x4 (&af)[RB][KCMAX], const ConvArgs& a, __amdgpu_buffer_rsrc_t xr,
+                                           const int32_t* tile_k, bool live, int wave, int lr, int lg) {
+    using S = typename TT::storage;
+    constexpr int E = TT::E;
+    const uint32_t row_bytes = uint32_t(a.CK) * uint32_t(sizeof(S));
+    bool any = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int32_t src = live ? tile_k[(wave * RB + rb) * 16 + lr] : -1;
+        any |= src >= 0;
+#pragma unroll
+        for (int kc = 0; kc < KCMAX; ++kc) {
+            const int col = (kc * 4 + lg) * E;
+            const bool ok = src >= 0 && col < a.CK;
+            af[rb][kc] = buf_ld16(xr, ok ? uint32_t(src) * row_bytes + uint32_t(col) * uint32_t(sizeof(S)) : BUF_OOB);
+        }
+    }
+    return __any(any);
+}
+
+template <typename TT, int RB, int NB, bool TRANS, int KCMAX, bool PIPE>
 __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     using S = typename TT::storage;
     constexpr int BN = NB * 16;
@@ -293,6 +349,66 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
         if (nk == 0) continue;
 
         auto slab_of = [&](int j) { const int kg = kt0 + list[j]; return a.w_rev ? a.K - 1 - kg : kg; };
+        // one offset's MFMAs: gathered rows `cur` against slab buffer j & 1
+        auto mma = [&](const u32x4 (&cur)[RB][KCMAX], int j) {
+            const char* sl = lds + (j & 1) * slab_bytes;
+#pragma unroll
+            for (int kc = 0; kc < KCMAX; ++kc) {
+                if (kc >= KC) break;
+                u32x4 bf[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], cur[rb][kc], acc[rb][nb]);
+            }
+        };
+        if constexpr (PIPE) {
+            // Short contractions: two offsets of gathered rows in flight.  Three
+            // register buffers take fixed roles in a loop unrolled by three (a
+            // buffer copy would wait for its loads), the barriers wait for LDS
+            // operations only, so the gathers stay in flight across them, and
+            // every load is branch-free (masked lanes, and prefetches past the
+            // last offset, take out-of-range buffer offsets and load zeros
+            // without a memory access; the slab staged after the last offset
+            // goes to the buffer no longer read), so the compiler's wait
+            // counts stay exact.  It pays where tiles hit many offsets
+            // (submanifold maps); tiles of one or two offsets run the plain
+            // loop below, which stages nothing past the last offset.
+            // The next offset's weight slab is staged one step ahead as before
+            // (its loads hit L2).
+            u32x4 ga[RB][KCMAX], gb[RB][KCMAX], gc[RB][KCMAX];
+            bool fa = false, fb = false, fc = false;
+            auto lds_barrier = [] {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            };
+            const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.x, uint32_t(a.n_src) * uint32_t(a.CK) * uint32_t(sizeof(S)));
+            const __amdgpu_buffer_rsrc_t wr =
+                buf_rsrc(a.w, uint32_t(a.K) * uint32_t(a.cin) * uint32_t(a.cout) * uint32_t(sizeof(S)));
+            auto step = [&](int j, const u32x4 (&cur)[RB][KCMAX], bool any, u32x4 (&pre)[RB][KCMAX], bool& any_pre) {
+                const int jn = min(j + 1, nk - 1);
+                wst.load_buf(a, wr, slab_of(jn), j + 1 < nk);
+                any_pre = gather_buf<TT, RB, KCMAX>(pre, a, xr, tile + list[min(j + 2, nk - 1)] * BMP, j + 2 < nk,
+                                                    wave, lr, lg);
+                if (any) mma(cur, j);
+                wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(jn), col0);
+                lds_barrier();
+            };
+            wst.load_buf(a, wr, slab_of(0), true);
+            fa = gather_buf<TT, RB, KCMAX>(ga, a, xr, tile + list[0] * BMP, true, wave, lr, lg);
+            fb = gather_buf<TT, RB, KCMAX>(gb, a, xr, tile + list[min(1, nk - 1)] * BMP, nk > 1, wave, lr, lg);
+            wst.store(lds, a, slab_of(0), col0);
+            lds_barrier();
+            for (int j = 0; j < nk; j += 3) {
+                step(j, ga, fa, gc, fc);
+                if (j + 1 < nk) step(j + 1, gb, fb, ga, fa);
+                if (j + 2 < nk) step(j + 2, gc, fc, gb, fb);
+            }
+            continue;
+        }
         wst.load(a, slab_of(0));
         bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, tile + list[0] * BMP, wave, lr, lg);
         wst.store(lds, a, slab_of(0), col0);
@@ -308,20 +424,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                 wst.load(a, slab_of(j + 1));
                 any_next = gather_rows<TT, RB, KCMAX>(anext, a, tile + list[j + 1] * BMP, wave, lr, lg);
             }
-            if (any_cur) {
-                const char* sl = lds + (j & 1) * slab_bytes;
-#pragma unroll
-                for (int kc = 0; kc < KCMAX; ++kc) {
-                    if (kc >= KC) break;
-                    u32x4 bf[NB];
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], acur[rb][kc], acc[rb][nb]);
-                }
-            }
+            if (any_cur) mma(acur, j);
             if (has_next) wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(j + 1), col0);
             __syncthreads();
 #pragma unroll
@@ -380,11 +483,11 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
 constexpr int RB_DEFAULT = 2;
 
-template <typename TT, int NB, bool TRANS, int KCMAX>
+template <typename TT, int NB, bool TRANS, int KCMAX, bool PIPE>
 spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB_DEFAULT * 16;
-    auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX>;
+    auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX, PIPE>;
     static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
     using S = typename TT::storage;
     const size_t main_bytes = 2 * size_t(a.kch) * (BN * 16 + 16) + (size_t(KTILE) * (BM + 1) + 2 * KTILE + 4) * 4;
@@ -399,15 +502,15 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     return SPC_OK;
 }
 
-template <typename TT, bool TRANS, int KCMAX>
+template <typename TT, bool TRANS, int KCMAX, bool PIPE = false>
 spc_status launch_conv_k(const ConvArgs& a, hipStream_t stream) {
     const int blocks = a.CN / 16;
-    if (blocks % 8 == 0) return launch_conv_nb<TT, 8, TRANS, KCMAX>(a, stream);
-    if (blocks % 6 == 0) return launch_conv_nb<TT, 6, TRANS, KCMAX>(a, stream);
-    if (blocks % 4 == 0) return launch_conv_nb<TT, 4, TRANS, KCMAX>(a, stream);
-    if (blocks % 3 == 0) return launch_conv_nb<TT, 3, TRANS, KCMAX>(a, stream);
-    if (blocks % 2 == 0) return launch_conv_nb<TT, 2, TRANS, KCMAX>(a, stream);
-    return launch_conv_nb<TT, 1, TRANS, KCMAX>(a, stream);
+    if (blocks % 8 == 0) return launch_conv_nb<TT, 8, TRANS, KCMAX, PIPE>(a, stream);
+    if (blocks % 6 == 0) return launch_conv_nb<TT, 6, TRANS, KCMAX, PIPE>(a, stream);
+    if (blocks % 4 == 0) return launch_conv_nb<TT, 4, TRANS, KCMAX, PIPE>(a, stream);
+    if (blocks % 3 == 0) return launch_conv_nb<TT, 3, TRANS, KCMAX, PIPE>(a, stream);
+    if (blocks % 2 == 0) return launch_conv_nb<TT, 2, TRANS, KCMAX, PIPE>(a, stream);
+    return launch_conv_nb<TT, 1, TRANS, KCMAX, PIPE>(a, stream);
 }
 
 template <typename TT, bool TRANS>
@@ -416,7 +519,11 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
     a.kch = int(ceil_div(a.CK / E, 4) * 4);
     const int KC = a.kch / 4;
     // gathered-row registers sized to the contraction: a 2-step variant frees
-    // 32 registers per lane for contractions of up to 64 (16-bit) channels
+    // 32 registers per lane for contractions of up to 64 (16-bit) channels.
+    // On a submanifold map it spends 16 of them on a second offset of
+    // gathers in flight (addressing x and the weights through buffer
+    // resources, so both must lie within 2 GiB).
+    if (KC <= 2 && a.dense && a.xbuf) return launch_conv_k<TT, TRANS, 2, true>(a, stream);
     if (KC <= 2) return launch_conv_k<TT, TRANS, 2>(a, stream);
     if (KC <= 4) return launch_conv_k<TT, TRANS, 4>(a, stream);
     if (KC <= 8) return launch_conv_k<TT, TRANS, 8>(a, stream);
@@ -425,6 +532,8 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
 
 spc_status run_conv(spc_dtype dt, ConvArgs& a, bool trans, hipStream_t stream) {
     if (a.n_rows == 0) return SPC_OK;
+    const int64_t es = dt == SPC_F32 ? 4 : 2;
+    a.xbuf = int64_t(a.n_src) * a.CK * es < (int64_t(1) << 31) && int64_t(a.K) * a.cin * a.cout * es < (int64_t(1) << 31);
     switch (dt) {
         case SPC_F32: return trans ? launch_conv_t<F32, true>(a, stream) : launch_conv_t<F32, false>(a, stream);
         case SPC_F16: return trans ? launch_conv_t<F16, true>(a, stream) : launch_conv_t<F16, false>(a, stream);
@@ -467,6 +576,7 @@ extern "C" spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int6
     // a 1x1x1 map is the identity: skip reading it
     ConvArgs a{feats, weight, bias, K == 1 ? nullptr : nbr, K == 1 ? nullptr : order, out, int32_t(n), int32_t(n),
                K, cin, cout, cin, cout, 0, 0};
+    a.dense = K > 1;
     return run_conv(dtype, a, true, stream);
 }
 
@@ -526,5 +636,6 @@ extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int6
     // din rows gather dout rows: contraction over cout, output channels cin
     ConvArgs a{dout, weight, nullptr, map, identity ? nullptr : order, din, int32_t(n_in), int32_t(n_out), K, cout,
                cin, cin, cout, map_is_subm ? 1 : 0, 0};
+    a.dense = map_is_subm && !identity;
     return run_conv(dtype, a, false, stream);
 }
