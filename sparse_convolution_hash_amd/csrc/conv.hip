@@ -520,11 +520,12 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
     const int KC = a.kch / 4;
     // gathered-row registers sized to the contraction: a 2-step variant frees
     // 32 registers per lane for contractions of up to 64 (16-bit) channels.
-    // On a submanifold map it spends 16 of them on a second offset of
+    // On a submanifold map the 2- and 4-step variants keep a second offset of
     // gathers in flight (addressing x and the weights through buffer
     // resources, so both must lie within 2 GiB).
     if (KC <= 2 && a.dense && a.xbuf) return launch_conv_k<TT, TRANS, 2, true>(a, stream);
     if (KC <= 2) return launch_conv_k<TT, TRANS, 2>(a, stream);
+    if (KC <= 4 && a.dense && a.xbuf) return launch_conv_k<TT, TRANS, 4, true>(a, stream);
     if (KC <= 4) return launch_conv_k<TT, TRANS, 4>(a, stream);
     if (KC <= 8) return launch_conv_k<TT, TRANS, 8>(a, stream);
     return fail(SPC_ERR_UNSUPPORTED, "contraction of %d channels exceeds %d for this dtype", a.CK, 8 * 4 * E);
