@@ -73,29 +73,69 @@ __device__ __forceinline__ int slab_off(int kb, int n) {
     return kb * (BN * 16 + 16) + n * 16;
 }
 
+// The 16-bit forward keeps W's own layout in LDS instead: row kk holds the
+// BN output channels of contraction index kk (2 bytes each) plus 32 bytes of
+// padding, and the MFMA fragments are read with gfx950's transposing LDS
+// reads (ds_read_b64_tr_b16).  Within each 16-lane group, lane j points at 4
+// consecutive 16-bit values M[j][0..3]; lane i receives M[4q + (i >> 2)][i & 3]
+// for q = 0..3.  So when lane j points at row k0 + (j >> 2), channels
+// n0 + 4 (j & 3) .. +3, lane i receives channel n0 + i at k0 .. k0 + 3: half
+// of its 8-value fragment, the second read (rows k0 + 4 ..) the other half.
+// Staging is then plain 16-byte copies of W rows, with no transposes.  It
+// pays for contractions of up to 64 channels (2 MFMA steps), where staging
+// dominates an offset's work (LiDAR SubM forward 34.4 -> 30.5 us); longer
+// contractions are bound by their LDS reads, and two 8-byte transposing reads
+// per fragment instead of one 16-byte read made them slower (shell-set SubM
+// forward 281 -> 312 us), so they keep the transposed layout.
+template <int BN>
+constexpr int row_stride() { return BN * 2 + 32; }
+
+template <typename TT, bool TRANS, int KCMAX>
+constexpr bool rows_layout() { return TRANS && TT::E == 8 && KCMAX <= 2; }
+
+// Bytes of one weight slab in LDS for a contraction of kch 16-byte chunks.
+template <int BN, bool ROWS>
+__host__ __device__ constexpr int slab_bytes_of(int kch) {
+    return ROWS ? kch * 8 * row_stride<BN>() : kch * (BN * 16 + 16);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
 // Weight slab staging.  TRANS: B[kk][n] = W[ws][kk][n] (the forward; W rows
-// are output channels apart, so E x E blocks are transposed in registers).
+// are output channels apart: 16-bit rows are copied as they are (ROWS, see
+// row_stride), fp32 ones in E x E blocks transposed in registers).
 // !TRANS: B[kk][n] = W[ws][n][kk] (dinput; already contraction-contiguous).
 // Chunks beyond CK are zero.  A thread holds up to WREG 16-byte registers of
 // the slab so the next offset's slab can be in flight during the MFMAs; any
 // rest of a large slab is copied when it is stored.
 constexpr int WREG = 8;
 
-template <typename TT, int BN, bool TRANS>
+template <typename TT, int BN, bool TRANS, bool ROWS>
 struct WStage {
     using S = typename TT::storage;
     static constexpr int E = TT::E;
-    // one item: an E x E block (TRANS) or one 16-byte chunk (!TRANS)
-    static constexpr int ITEM_REGS = TRANS ? E : 1;
+    // one item: an E x E block (fp32 TRANS) or one 16-byte chunk
+    static constexpr int ITEM_REGS = (TRANS && !ROWS) ? E : 1;
     static constexpr int PRE = WREG / ITEM_REGS;  // items prefetched per thread
     u32x4 r[WREG];
     // per prefetched item, fixed for the whole kernel: element offset inside a
     // weight slab (-1: zero padding or no item) and LDS byte offset
     int32_t gofs[PRE], lofs[PRE];
 
-    __device__ static int items(const ConvArgs& a) { return TRANS ? a.kch * (BN / E) : a.kch * BN; }
+    __device__ static int items(const ConvArgs& a) { return (TRANS && !ROWS) ? a.kch * (BN / E) : a.kch * BN; }
 
     __device__ static void place(const ConvArgs& a, int col0, int idx, int32_t& g, int32_t& l) {
+        if (ROWS) {  // consecutive items along a row of W: coalesced reads, consecutive LDS writes
+            constexpr int CPR = BN / 8;  // 16-byte chunks per row
+            const int kk = idx / CPR, c = idx - kk * CPR;
+            g = kk < a.CK ? kk * a.cout + col0 + c * 8 : -1;
+            l = kk * row_stride<BN>() + c * 16;
+            return;
+        }
         const int kb = idx % a.kch, q = idx / a.kch;  // q: channel block (TRANS) or channel
         const bool real = kb < a.CK / E;
         if (TRANS) {
@@ -119,7 +159,7 @@ struct WStage {
     }
 
     __device__ static void load_at(u32x4* dst, const S* w, int32_t g, int cout) {
-        if (TRANS) {
+        if (TRANS && !ROWS) {
 #pragma unroll
             for (int e = 0; e < E; ++e) dst[e] = g >= 0 ? ld16(w + g + int64_t(e) * cout) : zero4();
         } else {
@@ -128,7 +168,7 @@ struct WStage {
     }
 
     __device__ static void store_at(char* lds, const u32x4* in, int32_t l) {
-        if (TRANS) {
+        if (TRANS && !ROWS) {
             if constexpr (E == 8) {
                 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
                 u16x8 v[8];
@@ -251,7 +291,8 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // the two slab buffers are addressed arithmetically from the __shared__
     // base (a pointer table would hide the address space and turn the LDS
     // reads into flat loads that wait on the global prefetches)
-    const int slab_bytes = a.kch * (BN * 16 + 16);
+    constexpr bool ROWS = rows_layout<TT, TRANS, KCMAX>();
+    const int slab_bytes = slab_bytes_of<BN, ROWS>(a.kch);
     int32_t* tile = reinterpret_cast<int32_t*>(lds + 2 * slab_bytes);  // [KTILE][BMP]
     int32_t* flags = tile + KTILE * BMP;                               // [KTILE]
     int32_t* list = flags + KTILE;                                     // [KTILE + 4] (count at KTILE; keeps 16-B alignment)
@@ -287,7 +328,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    WStage<TT, BN, TRANS> wst;
+    WStage<TT, BN, TRANS, ROWS> wst;
     wst.init(a, col0);
     u32x4 acur[RB][KCMAX], anext[RB][KCMAX];
     for (int kt0 = 0; kt0 < a.K; kt0 += KTILE) {
@@ -356,8 +397,18 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             for (int kc = 0; kc < KCMAX; ++kc) {
                 if (kc >= KC) break;
                 u32x4 bf[NB];
+                if constexpr (ROWS) {  // transposing reads of the row layout
+                    const char* p0 = sl + ((kc * 4 + lg) * 8 + (lr >> 2)) * row_stride<BN>() + 4 * (lr & 3) * 2;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const s16x4 lo = ds_read_tr16(p0 + nb * 32), hi = ds_read_tr16(p0 + nb * 32 + 4 * row_stride<BN>());
+                        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                        bf[nb] = u32x4{l2.x, l2.y, h2.x, h2.y};
+                    }
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+                }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -490,7 +541,8 @@ spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX, PIPE>;
     static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
     using S = typename TT::storage;
-    const size_t main_bytes = 2 * size_t(a.kch) * (BN * 16 + 16) + (size_t(KTILE) * (BM + 1) + 2 * KTILE + 4) * 4;
+    const size_t main_bytes = 2 * size_t(slab_bytes_of<BN, rows_layout<TT, TRANS, KCMAX>()>(a.kch)) +
+                              (size_t(KTILE) * (BM + 1) + 2 * KTILE + 4) * 4;
     const size_t stage_bytes = size_t(BM) * (BN * sizeof(S) + 16);  // the epilogue's staged outputs
     const size_t lds = std::max(main_bytes, stage_bytes) + BM * 4 + BN * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
