@@ -901,43 +901,83 @@ spc_status row_pass(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t
 // them).  The masks are only read, so a concurrent pair compaction may read
 // them too.  rows_dev < 0 means M from the header; grids are sized for
 // rows_cap rows.
-spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
-                     const Scratch& s, bool masks_ready, int slot, int32_t* order, hipStream_t stream) {
+// One processing order to build: the rows of `map` (rows_dev < 0: M from the
+// header; grids sized for rows_cap rows) sorted by neighbour mask into
+// `order`, with sort slot `slot`'s buffers; masks_ready: s.mask[slot] already
+// holds the masks (else a row pass makes them).
+struct OrderJob {
+    const int32_t* map;
+    int32_t rows_dev;
+    int64_t rows_cap, cap;
+    bool masks_ready;
+    int slot;
+    int32_t* order;
+};
+
+// Stable LSD radix sorts of up to two orders (the identity for K > 32).  Two
+// orders share each pass's launches: blocks [0, nb0) sort the first, the rest
+// the second.  The masks are only read, so a pair compaction may read them
+// afterwards.
+spc_status sort_orders(const Plan& p, const Scratch& s, const OrderJob* jobs, int count, hipStream_t stream) {
     const int K = p.K;
-    if (K > MASK_BITS) {
-        hipLaunchKernelGGL(k_iota, dim3(grid_for(rows_cap, KB, 4096)), dim3(KB), 0, stream, order, rows_dev, cap,
-                           s.hdr);
-        SPC_LAUNCHED("k_iota");
-        return SPC_OK;
+    const OrderJob* live[2] = {nullptr, nullptr};
+    int nl = 0;
+    for (int i = 0; i < count; ++i) {
+        const OrderJob& o = jobs[i];
+        if (K > MASK_BITS) {
+            hipLaunchKernelGGL(k_iota, dim3(grid_for(o.rows_cap, KB, 4096)), dim3(KB), 0, stream, o.order, o.rows_dev,
+                               o.cap, s.hdr);
+            SPC_LAUNCHED("k_iota");
+            continue;
+        }
+        if (o.rows_cap == 0) continue;
+        if (!o.masks_ready) {
+            spc_status st = row_pass(p, o.map, o.rows_dev, o.rows_cap, o.cap, s, s.mask[o.slot], nullptr, stream);
+            if (st != SPC_OK) return st;
+        }
+        live[nl++] = &o;
     }
-    if (rows_cap == 0) return SPC_OK;
-    if (!masks_ready) {
-        spc_status st = row_pass(p, map, rows_dev, rows_cap, cap, s, s.mask[slot], nullptr, stream);
-        if (st != SPC_OK) return st;
-    }
-    const SortBuf& sb = s.sort[slot];
-    const unsigned nb = unsigned(ceil_div(rows_cap, RS_TILE));
-    const int ng = int(ceil_div(nb, RS_GROUP));
+    if (nl == 0) return SPC_OK;
     const int passes = (K + RS_BITS - 1) / RS_BITS;
-    const uint32_t* kin = s.mask[slot];
-    const int32_t* vin = nullptr;
+    RsPass P{};
+    for (int i = 0; i < nl; ++i) {
+        RsJob& J = P.job[i];
+        J.keys_in = s.mask[live[i]->slot];
+        J.vals_in = nullptr;
+        J.n_dev = s.hdr + H_NOUT;
+        J.cap = live[i]->cap;
+        J.rows = live[i]->rows_dev;
+        J.nb = int(ceil_div(live[i]->rows_cap, RS_TILE));
+        J.ng = int(ceil_div(J.nb, RS_GROUP));
+        J.hist = s.sort[live[i]->slot].hist;
+    }
+    const unsigned blocks = unsigned(P.job[0].nb + P.job[1].nb);
     for (int pass = 0; pass < passes; ++pass) {
-        const int shift = RS_BITS * pass;
-        int32_t* gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
-        hipLaunchKernelGGL(k_rs_hist, dim3(nb), dim3(RS_THREADS), 0, stream, kin, rows_dev, cap, s.hdr + H_NOUT, shift,
-                           sb.hist, gsum, ng);
-        SPC_LAUNCHED("k_rs_hist");
+        P.shift = RS_BITS * pass;
         const bool last = pass + 1 == passes;
-        uint32_t* kout = sb.keys[pass & 1];
-        int32_t* vout = last ? order : sb.vals[pass & 1];
-        hipLaunchKernelGGL(k_rs_scatter, dim3(nb), dim3(RS_THREADS), 0, stream, kin, vin, rows_dev, cap,
-                           s.hdr + H_NOUT, shift,
-                           sb.hist, gsum, ng, kout, vout);
+        for (int i = 0; i < nl; ++i) {
+            const int slot = live[i]->slot;
+            const SortBuf& sb = s.sort[slot];
+            P.job[i].gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
+            P.job[i].keys_out = sb.keys[pass & 1];
+            P.job[i].vals_out = last ? live[i]->order : sb.vals[pass & 1];
+        }
+        hipLaunchKernelGGL(k_rs_hist, dim3(blocks), dim3(RS_THREADS), 0, stream, P);
+        SPC_LAUNCHED("k_rs_hist");
+        hipLaunchKernelGGL(k_rs_scatter, dim3(blocks), dim3(RS_THREADS), 0, stream, P);
         SPC_LAUNCHED("k_rs_scatter");
-        kin = kout;
-        vin = vout;
+        for (int i = 0; i < nl; ++i) {
+            P.job[i].keys_in = P.job[i].keys_out;
+            P.job[i].vals_in = P.job[i].vals_out;
+        }
     }
     return SPC_OK;
+}
+
+spc_status sort_rows(const Plan& p, const int32_t* map, int32_t rows_dev, int64_t rows_cap, int64_t cap,
+                     const Scratch& s, bool masks_ready, int slot, int32_t* order, hipStream_t stream) {
+    const OrderJob o{map, rows_dev, rows_cap, cap, masks_ready, slot, order};
+    return sort_orders(p, s, &o, 1, stream);
 }
 
 // Pinned host words and an event per host thread and device: a strided call
@@ -1164,8 +1204,6 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                 hipLaunchKernelGGL(k_in_rows, dim3(unsigned(nblk)), dim3(KB), 0, stream, c4, n, int64_t(out_cap),
                                    p.g, bitmap, prefix, nbr_in, order_in ? s.mask[1] : nullptr, s.hdr);
                 SPC_LAUNCHED("k_in_rows");
-                if (order_in && (st = sort_rows(p, nbr_in, n, n, n, s, true, 1, order_in, stream)) != SPC_OK)
-                    return st;
             }
             auto rows_kernel = p.g.dense ? k_out_rows<true, false> : k_out_rows<false, false>;
             hipLaunchKernelGGL(rows_kernel, dim3(unsigned(std::max<int64_t>(ceil_div(cap, KB), 1))), dim3(KB), 0, stream,
@@ -1173,6 +1211,12 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                                nbr, (pairs || order) ? s.mask[0] : nullptr, pairs ? s.counts : nullptr, s.hdr,
                                coord_err);
             SPC_LAUNCHED("k_out_rows");
+            // both orders from the row kernels' masks, sharing each pass's launches
+            OrderJob jobs[2];
+            int nj = 0;
+            if (order_in && n > 0) jobs[nj++] = OrderJob{nbr_in, n, n, n, true, 1, order_in};
+            if (order) jobs[nj++] = OrderJob{nbr, -1, cap, int64_t(out_cap), true, 0, order};
+            if ((st = sort_orders(p, s, jobs, nj, stream)) != SPC_OK) return st;
         } else {
             // larger kernels: the output-side map is the transpose of the
             // input-side one, scattered into a map filled with -1
@@ -1192,7 +1236,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                 if (st != SPC_OK) return st;
             }
         }
-        if (order) {
+        if (order && p.K > ROWPASS_KMAX) {
             st = sort_rows(p, nbr, -1, cap, int64_t(out_cap), s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }

@@ -2,8 +2,11 @@
 // to libspc; used for the kernel maps' processing orders and the point
 // voxeliser's per-voxel point order).  One pass = k_rs_hist then
 // k_rs_scatter on RS_BITS bits at `shift`; the host chains the passes over
-// two ping-pong buffers.  Row counts are host values or, with rows < 0, a
-// device count read at n_dev (treated as 0 when above cap).
+// two ping-pong buffers.  A launch can carry the same pass of two
+// independent sorts (RsPass): its first job[0].nb blocks serve job 0, the
+// rest job 1, which halves the launches of a strided kernel map's two orders.
+// Row counts are host values or, with rows < 0, a device count read at
+// n_dev (treated as 0 when above cap).
 #pragma once
 
 #include "common.h"
@@ -23,6 +26,26 @@ __device__ __forceinline__ int32_t count_within(const uint32_t* n_dev, int64_t c
     const uint32_t m = *n_dev;
     return int64_t(m) <= cap ? int32_t(m) : 0;
 }
+
+// One sort's arguments for one pass.
+struct RsJob {
+    const uint32_t* keys_in;
+    const int32_t* vals_in;     // NULL: the identity (the row index)
+    uint32_t* keys_out;
+    int32_t* vals_out;
+    int32_t* hist;              // [RS_BINS][nb] block counts
+    int32_t* gsum;              // [RS_BINS][ng] group sums, zeroed beforehand
+    const uint32_t* n_dev;      // device row count when rows < 0
+    int64_t cap;
+    int32_t rows;
+    int32_t nb, ng;             // radix blocks and block groups of this sort
+};
+
+// One pass of up to two sorts (job[1].nb == 0: one sort).
+struct RsPass {
+    RsJob job[2];
+    int32_t shift;
+};
 
 // Lanes of this wave whose (valid) digit equals this lane's, from RS_BITS ballots.
 __device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d) {
@@ -47,12 +70,16 @@ static_assert(RS_THREADS == RS_BINS, "one thread per digit");
 // (RS_BINS-1) of its tile into hist[d*nb + block] and adds them to the sums
 // of its group of RS_GROUP blocks, gsum[d*ng + block/RS_GROUP] (zeroed
 // beforehand).  rows < 0: the count at n_dev (0 when above cap).
-__global__ __launch_bounds__(RS_THREADS) void k_rs_hist(const uint32_t* __restrict__ keys, int32_t rows, int64_t cap,
-                                                        const uint32_t* n_dev, int shift, int32_t* __restrict__ hist,
-                                                        int32_t* __restrict__ gsum, int ng) {
+__global__ __launch_bounds__(RS_THREADS) void k_rs_hist(RsPass P) {
     __shared__ int32_t h[RS_BINS];
-    if (rows < 0) rows = count_within(n_dev, cap);
-    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
+    const bool second = int(blockIdx.x) >= P.job[0].nb;
+    const RsJob& J = second ? P.job[1] : P.job[0];
+    const int me = int(blockIdx.x) - (second ? P.job[0].nb : 0);
+    const uint32_t* __restrict__ keys = J.keys_in;
+    const int shift = P.shift;
+    int32_t rows = J.rows;
+    if (rows < 0) rows = count_within(J.n_dev, J.cap);
+    const int32_t tile0 = int32_t(me) * RS_TILE;
     if (tile0 >= rows) return;  // uniform per block; later blocks are never read
     const int t = threadIdx.x;
     uint32_t k[RS_ITEMS];
@@ -65,8 +92,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_hist(const uint32_t* __restri
         if (tile0 + r * RS_THREADS + t < rows) atomicAdd(h + ((k[r] >> shift) & (RS_BINS - 1)), 1);
     __syncthreads();
     const int c = h[t];
-    hist[int64_t(t) * gridDim.x + blockIdx.x] = c;
-    if (c) atomicAdd(gsum + int64_t(t) * ng + blockIdx.x / RS_GROUP, c);
+    J.hist[int64_t(t) * J.nb + me] = c;
+    if (c) atomicAdd(J.gsum + int64_t(t) * J.ng + me / RS_GROUP, c);
 }
 
 // Pass scatter, stable.  Slot base of digit d for this block: keys of
@@ -75,34 +102,44 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_hist(const uint32_t* __restri
 // counts of earlier waves of the block, then ranks its keys among equal
 // digits with RS_BITS ballots (computed once, for counting and writing) and
 // writes them in order.  vals_in == NULL means the identity (row index).
-__global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(const uint32_t* __restrict__ keys_in,
-                                                           const int32_t* __restrict__ vals_in, int32_t rows,
-                                                           int64_t cap, const uint32_t* n_dev, int shift,
-                                                           const int32_t* __restrict__ hist,
-                                                           const int32_t* __restrict__ gsum, int ng,
-                                                           uint32_t* __restrict__ keys_out,
-                                                           int32_t* __restrict__ vals_out) {
+__global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(RsPass P) {
     __shared__ int32_t base[RS_WAVES][RS_BINS];
     __shared__ uint32_t skey[RS_TILE];
     __shared__ int32_t sval[RS_TILE];
-    if (rows < 0) rows = count_within(n_dev, cap);
-    const int32_t tile0 = int32_t(blockIdx.x) * RS_TILE;
+    const bool second = int(blockIdx.x) >= P.job[0].nb;
+    const RsJob& J = second ? P.job[1] : P.job[0];
+    const int me = int(blockIdx.x) - (second ? P.job[0].nb : 0);
+    const uint32_t* __restrict__ keys_in = J.keys_in;
+    const int32_t* __restrict__ vals_in = J.vals_in;
+    const int32_t* __restrict__ hist = J.hist;
+    const int32_t* __restrict__ gsum = J.gsum;
+    uint32_t* __restrict__ keys_out = J.keys_out;
+    int32_t* __restrict__ vals_out = J.vals_out;
+    const int shift = P.shift, ng = J.ng, nb = J.nb;
+    int32_t rows = J.rows;
+    if (rows < 0) rows = count_within(J.n_dev, J.cap);
+    const int32_t tile0 = int32_t(me) * RS_TILE;
     if (tile0 >= rows) return;  // uniform per block
     const int t = threadIdx.x, lane = t & (WAVE - 1), wave = t / WAVE;
-    // 0. the block's keys and values, in index order, into LDS (coalesced,
-    //    unconditional loads so that they are all in flight together)
+    // 0. the block's keys and values (coalesced, unconditional loads) and this
+    //    thread's digit counts are all requested before any of them is used
+    uint32_t kr[RS_ITEMS];
+    int32_t vr[RS_ITEMS];
 #pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
-        const int j = r * RS_THREADS + t;
-        skey[j] = ld_clamped(keys_in, tile0 + j, rows);
-        sval[j] = vals_in ? ld_clamped(vals_in, tile0 + j, rows) : tile0 + j;
+    for (int r = 0; r < RS_ITEMS; ++r) kr[r] = ld_clamped(keys_in, tile0 + r * RS_THREADS + t, rows);
+    if (vals_in) {
+#pragma unroll
+        for (int r = 0; r < RS_ITEMS; ++r) vr[r] = ld_clamped(vals_in, tile0 + r * RS_THREADS + t, rows);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RS_ITEMS; ++r) vr[r] = tile0 + r * RS_THREADS + t;
     }
     // digit t: totals over the groups and the part before this block
-    const int me = int(blockIdx.x), g_me = me / RS_GROUP, b0 = g_me * RS_GROUP;
+    const int g_me = me / RS_GROUP, b0 = g_me * RS_GROUP;
     int tot = 0, before = 0;
     {
         const int32_t* gs = gsum + int64_t(t) * ng;
-        const int32_t* hc = hist + int64_t(t) * gridDim.x;
+        const int32_t* hc = hist + int64_t(t) * nb;
         int hv[RS_GROUP];
 #pragma unroll
         for (int u = 0; u < RS_GROUP; ++u) hv[u] = ld_clamped(hc, b0 + u, int64_t(me) + 1);
@@ -118,6 +155,11 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(const uint32_t* __res
         }
 #pragma unroll
         for (int u = 0; u < RS_GROUP; ++u) before += b0 + u < me ? hv[u] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        skey[r * RS_THREADS + t] = kr[r];
+        sval[r * RS_THREADS + t] = vr[r];
     }
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) base[w][t] = 0;

@@ -367,13 +367,23 @@ extern "C" spc_status spc_point_to_voxel(const float* points, int64_t n_points, 
     const uint32_t* kin = keys0;
     const int32_t* vin = nullptr;  // identity: the point index
     for (int pass = 0; pass < l.passes; ++pass) {
-        int32_t* gs = gsum + int64_t(pass) * RS_BINS * l.ngs;
-        hipLaunchKernelGGL(k_rs_hist, dim3(unsigned(l.nbs)), dim3(RS_THREADS), 0, stream, kin, n, int64_t(n),
-                           (const uint32_t*)nullptr, RS_BITS * pass, hist, gs, int(l.ngs));
+        RsPass P{};
+        RsJob& J = P.job[0];
+        J.keys_in = kin;
+        J.vals_in = vin;
+        J.keys_out = kbuf[pass & 1];
+        J.vals_out = vbuf[pass & 1];
+        J.hist = hist;
+        J.gsum = gsum + int64_t(pass) * RS_BINS * l.ngs;
+        J.n_dev = nullptr;
+        J.cap = n;
+        J.rows = n;
+        J.nb = int(l.nbs);
+        J.ng = int(l.ngs);
+        P.shift = RS_BITS * pass;
+        hipLaunchKernelGGL(k_rs_hist, dim3(unsigned(l.nbs)), dim3(RS_THREADS), 0, stream, P);
         SPC_LAUNCHED("k_rs_hist");
-        hipLaunchKernelGGL(k_rs_scatter, dim3(unsigned(l.nbs)), dim3(RS_THREADS), 0, stream, kin, vin, n, int64_t(n),
-                           (const uint32_t*)nullptr, RS_BITS * pass, hist, gs, int(l.ngs), kbuf[pass & 1],
-                           vbuf[pass & 1]);
+        hipLaunchKernelGGL(k_rs_scatter, dim3(unsigned(l.nbs)), dim3(RS_THREADS), 0, stream, P);
         SPC_LAUNCHED("k_rs_scatter");
         kin = kbuf[pass & 1];
         vin = vbuf[pass & 1];
