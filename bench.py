@@ -16,8 +16,9 @@ It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
     dfilter_strided its dfilter
 
 Both kernel maps depend on the coordinates only, so the step builds each on
-a stream of its own (default priority), SubM first, while the main stream
-finishes the previous step; each layer waits for its map.  The maps are marked
+a stream of its own (default priority), while the main stream finishes the
+previous step: the SubM map first (its layer is next on the main stream), the
+strided map after it, beside the SubM layer; each layer waits for its map.  The maps are marked
 as used by the main stream, so their memory is not reused early.  Running the
 SubM dinput and dfilter side by side as well was slower (each fills the GPU).
 
@@ -165,16 +166,17 @@ class Step:
         return self.time_launch(launch, reps)
 
     def run(self, events=None):
-        """One step.  The strided layer's kernel map depends on the coordinates
-        only, so it is built on a second stream (default priority) while the
-        SubM layer runs; the main stream waits for it before the strided layer.
-        Each stage's events are recorded on the stream it runs on."""
+        """One step.  Each kernel map depends on the coordinates only, so each
+        is built on a stream of its own (default priority) while the main
+        stream finishes the previous step; the main stream waits for a map
+        (a persistent event) before its layer.  Each stage's events are
+        recorded on the stream it runs on."""
         spc, inp, torch = self.spc, self.inp, self.torch
         E = events or {}
-        main = torch.cuda.current_stream()
-        if self.side is None:
-            self.side = (torch.cuda.Stream(), torch.cuda.Stream())
-        side_s, side_k = self.side
+        if self.side is None:  # the streams and the events that join them, made once
+            self.side = (torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream(),
+                         torch.cuda.Event(), torch.cuda.Event())
+        main, side_s, side_k, done_s, done_k = self.side
 
         def mark(name, i):
             if name in E:
@@ -186,18 +188,22 @@ class Step:
                 if isinstance(t, torch.Tensor):
                     t.record_stream(main)
 
-        with torch.cuda.stream(side_s):
-            mark("kmap_subm", 0)
-            km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
-            mark("kmap_subm", 1)
-        with torch.cuda.stream(side_k):
-            mark("kmap_strided", 0)
-            ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
-                                orders=True)
-            mark("kmap_strided", 1)
+        torch.cuda.set_stream(side_s)
+        mark("kmap_subm", 0)
+        km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
+        mark("kmap_subm", 1)
+        done_s.record(side_s)
+        torch.cuda.set_stream(side_k)
+        side_k.wait_event(done_s)   # the SubM map first: its layer is the next on the main stream
+        mark("kmap_strided", 0)
+        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
+                            orders=True)
+        mark("kmap_strided", 1)
+        done_k.record(side_k)
+        torch.cuda.set_stream(main)
         used_on_main(km)
         used_on_main(ks)
-        main.wait_stream(side_s)
+        main.wait_event(done_s)
         mark("fwd_subm", 0)
         y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
         mark("fwd_subm", 1)
@@ -210,7 +216,7 @@ class Step:
         mark("dfilter_subm", 0)
         spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"])
         mark("dfilter_subm", 1)
-        main.wait_stream(side_k)
+        main.wait_event(done_k)
         mark("fwd_strided", 0)
         spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"], ks["order"])
         mark("fwd_strided", 1)
