@@ -142,13 +142,15 @@ __device__ __forceinline__ int32_t rows_within(const uint32_t* hdr, int64_t cap)
 // ---------------------------------------------------------------- kernels
 
 // Fills `cap` hash slots with the empty marker; zeroes the output bitmap, the
-// occupancy bitmap, the header and `zero` (word counts multiples of 4).
+// occupancy bitmap, the header, the caller's coordinate flags (NULL ok; later
+// kernels OR their findings in) and `zero` (word counts multiples of 4).
 __global__ void k_clear(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ bitmap,
                         int64_t nwords, uint32_t* __restrict__ occ, int64_t occ_words, uint32_t* __restrict__ hdr,
-                        int32_t* __restrict__ zero, int64_t nzero) {
+                        int32_t* coord_err, int32_t* __restrict__ zero, int64_t nzero) {
     const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     if (t < H_WORDS) hdr[t] = 0u;
+    if (coord_err && t == 0) *coord_err = 0;
     u32x4 ones = {~0u, ~0u, ~0u, ~0u};
     for (int64_t i = t; i < cap / 2; i += stride) st16(table + 2 * i, ones);
     for (int64_t i = t; i < nwords / 4; i += stride) st16(bitmap + 4 * i, zero4());
@@ -178,10 +180,14 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         return;
     }
     const uint32_t key = in_key(c.x, c.y, c.z, c.w, g);
-    if (g.occ) {  // a cell whose bit was already set is a duplicate
+    if (g.occ) {
         const uint32_t bit = 1u << (key & 31u);
-        if (atomicOr(occ + (key >> 5), bit) & bit) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
-        if (g.dense) reinterpret_cast<int32_t*>(table)[key] = i;
+        if (STRIDED) {  // a cell whose bit was already set is a duplicate (the host reads it with the count)
+            if (atomicOr(occ + (key >> 5), bit) & bit) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
+        } else {        // no round trip: the SubM row kernel finds duplicates (its own cell holds another row)
+            atomicOr(occ + (key >> 5), bit);
+        }
+        reinterpret_cast<int32_t*>(table)[key] = i;
     } else {
         table_insert(table, mask, key, uint32_t(i), hdr + H_FLAGS);
     }
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
     const int K = g.kz * g.ky * g.kx;
     offset_table(ktab, g, K);
     const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
-    if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (coord_err && t == 0 && hdr[H_FLAGS]) atomicOr(coord_err, int32_t(hdr[H_FLAGS]));
     if (t >= int64_t(n) * K) return;
     const int32_t i = int32_t(qdiv(uint32_t(t), g.mK));  // K * n < 2^31
     const int k = int(t - int64_t(i) * K);
@@ -242,9 +248,12 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
     const int4 c = coords[i];
     if (in_grid(c, g)) {
         const int z = c.y + kz - g.kz / 2, y = c.z + ky - g.ky / 2, x = c.w + kx - g.kx / 2;
-        if (kz == g.kz / 2 && ky == g.ky / 2 && kx == g.kx / 2)
+        if (kz == g.kz / 2 && ky == g.ky / 2 && kx == g.kx / 2) {
             v = i;
-        else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X) {
+            // the index grid's insert did not check: another row in this cell is a duplicate
+            if (g.dense && reinterpret_cast<const int32_t*>(table)[in_key(c.x, c.y, c.z, c.w, g)] != i && coord_err)
+                atomicOr(coord_err, SPC_COORD_DUPLICATE);
+        } else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X) {
             const uint32_t key = in_key(c.x, z, y, x, g);
             if (!g.dense)
                 v = table_find(table, mask, key);
@@ -407,7 +416,7 @@ __global__ __launch_bounds__(KB) void k_strided_maps(const int4* __restrict__ co
     const int K = g.kz * g.ky * g.kx;
     offset_table(ktab, g, K);
     const int64_t t = int64_t(blockIdx.x) * KB + threadIdx.x;
-    if (coord_err && t == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (coord_err && t == 0 && hdr[H_FLAGS]) atomicOr(coord_err, int32_t(hdr[H_FLAGS]));
     if (t >= int64_t(n) * K || int64_t(hdr[H_NOUT]) > cap) return;
     const int32_t i = int32_t(qdiv(uint32_t(t), g.mK));  // K * n < 2^31
     const int k = int(t - int64_t(i) * K);
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     const uint32_t nb = gridDim.x, xc = blockIdx.x % 8u, per = nb / 8u;
     const uint32_t lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
     const int32_t row0 = int32_t(lb) * KB, i = row0 + t;
-    if (coord_err && i == 0) *coord_err = int32_t(hdr[H_FLAGS]);
+    if (coord_err && i == 0 && hdr[H_FLAGS]) atomicOr(coord_err, int32_t(hdr[H_FLAGS]));
     if (row0 >= rows) {  // uniform per block: a block past M (capacity above M) has no hits
         if (counts && t < K) counts[int64_t(t) * gridDim.x + lb] = 0;
         return;
@@ -544,7 +553,9 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
         const uint32_t kk = ktab[k < K ? k : 0];
         const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy,
                   x = c.w * g.sx - g.px + int(kk & 7) * g.dx;
-        const bool in = ok && k < K && !(SUBM && k == K / 2) && (unsigned)z < (unsigned)g.Z &&
+        // (a SubM map's centre is looked up only with the index grid, whose
+        // insert left the duplicate check to this kernel)
+        const bool in = ok && k < K && !(SUBM && !DENSE && k == K / 2) && (unsigned)z < (unsigned)g.Z &&
                         (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X;
         key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
         inside |= uint32_t(in) << k;
@@ -560,6 +571,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     }
     // 2. resolve into LDS; hash probes that met another key finish afterwards
     uint32_t m = 0, pending = 0;
+    bool dup = false;
     int32_t* srow = stage + t * K;
 #pragma unroll
     for (int k = 0; k < ROWPASS_KMAX; ++k) {
@@ -567,6 +579,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
         int32_t v = -1;
         if (SUBM && k == K / 2) {
             v = ok ? i : -1;
+            if (DENSE && ok && int32_t(uint32_t(got[k])) != i) dup = true;
         } else if ((inside >> k) & 1u) {
             if (DENSE) {
                 v = int32_t(uint32_t(got[k]));
@@ -591,6 +604,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
         srow[k] = v;
         if (v >= 0) m |= 1u << k;
     }
+    if (dup && coord_err) atomicOr(coord_err, SPC_COORD_DUPLICATE);
     // 3. per-offset hit counts of the block (wave ballots into LDS)
     if (counts) {
         for (int k = 0; k < K; ++k) {
@@ -1114,7 +1128,8 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     const int64_t nzero = (order || order_in) ? int64_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups : 0;
     const int64_t fill = p.g.occ ? 0 : p.cap;   // hash slots to mark empty (the index grid is never cleared)
     hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({fill / 2, p.nwords / 4, p.occ_words / 4, nzero / 4}), KB, 4096)),
-                       dim3(KB), 0, stream, table, fill, bitmap, p.nwords, occ, p.occ_words, s.hdr, s.gsum, nzero);
+                       dim3(KB), 0, stream, table, fill, bitmap, p.nwords, occ, p.occ_words, s.hdr, coord_err, s.gsum,
+                       nzero);
     SPC_LAUNCHED("k_clear");
     if (n > 0) {
         if (subm)
