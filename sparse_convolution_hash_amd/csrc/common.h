@@ -48,6 +48,17 @@ __device__ __forceinline__ T ld_clamped(const T* __restrict__ a, int64_t i, int6
     return a[i < n ? i : n - 1];
 }
 
+// Workgroup barrier that waits for LDS operations only: a release/acquire
+// fence scoped to the workgroup and to LDS around s_barrier.  Unlike
+// __syncthreads(), which waits for every outstanding memory operation first,
+// it lets global loads into registers stay in flight across it, so loads can
+// be issued steps ahead of their use.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block-wide exclusive scan of one int per thread; returns the block total.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {

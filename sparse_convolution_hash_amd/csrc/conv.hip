@@ -431,11 +431,6 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             // (its loads hit L2).
             u32x4 ga[RB][KCMAX], gb[RB][KCMAX], gc[RB][KCMAX];
             bool fa = false, fb = false, fc = false;
-            auto lds_barrier = [] {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-            };
             const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.x, uint32_t(a.n_src) * uint32_t(a.CK) * uint32_t(sizeof(S)));
             const __amdgpu_buffer_rsrc_t wr =
                 buf_rsrc(a.w, uint32_t(a.K) * uint32_t(a.cin) * uint32_t(a.cout) * uint32_t(sizeof(S)));

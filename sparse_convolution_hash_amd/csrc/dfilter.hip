@@ -232,7 +232,8 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     auto step = [&](Item<TT>& mine, const int32_t (&use)[E], int32_t (&fill)[E]) {
         const Step& ahead = DEPTH == 2 ? nx2 : nxt;
         const Step after = ahead.k >= 0 ? step_at(sptr, ahead.e, ahead.k, s1) : Step{0, 0, -1};
-        __syncthreads();  // the previous step's tiles are consumed
+        // LDS-only barriers: the rows of the steps ahead stay in flight across them
+        lds_barrier();  // the previous step's tiles are consumed
         if (has_item) store_item<TT>(xt, gt, mine, my, xi_items);
         for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32): not pipelined
             const ItemGeo g2(it, xi_items, E);
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
             load_rows<TT>(tmp, r2, a, g2, ci0, co0, cur);
             store_item<TT>(xt, gt, tmp, it, xi_items);
         }
-        __syncthreads();
+        lds_barrier();
         if (ahead.k >= 0) {
             load_rows<TT>(mine, use, a, geo, ci0, co0, ahead);
             if (after.k >= 0) load_idx<TT, IDENT>(fill, a, geo, after);
