@@ -349,6 +349,7 @@ def conv_bwd_input(dout: torch.Tensor, weight: torch.Tensor, map_: Optional[torc
     return din
 
 
+@functools.lru_cache(maxsize=256)
 def conv_bwd_filter_workspace(n_in, n_out, cin, cout, K, want_dbias) -> int:
     b = ctypes.c_size_t()
     _check(lib().spc_conv_bwd_filter_workspace(int(n_in), int(n_out), int(cin), int(cout), int(K),
@@ -370,7 +371,7 @@ def conv_bwd_filter(feats: torch.Tensor, dout: torch.Tensor, K: int, pair_ptr: O
         if t is not None:
             _need(t, nm, torch.int32, dev)
     cin, cout = feats.shape[1], dout.shape[1]
-    ws = conv_bwd_filter_workspace(feats.shape[0], dout.shape[0], cin, cout, K, want_dbias)
+    ws = conv_bwd_filter_workspace(feats.shape[0], dout.shape[0], cin, cout, int(K), bool(want_dbias))
     if workspace is None or workspace.numel() < ws:
         workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
     if dw is None:
