@@ -198,6 +198,32 @@ spc_status spc_conv_fwd_fused(spc_dtype dtype, const void* feats, int64_t n_src,
                               const void* residual, int32_t relu, void* out, hipStream_t stream);
 
 /*
+ * Weight transpose for the forwards below: weight_t[k][n][c] = weight[k][c][n],
+ * weight [K, cin, cout] -> weight_t [K, cout, cin], same dtype, device
+ * memory owned by the caller; the two buffers must not overlap.  One kernel
+ * on `stream`.  (The per-offset weight matrices of the MLX sparse/conv.py
+ * page's formula, stored contraction-contiguous.)
+ */
+spc_status spc_transpose_weight(spc_dtype dtype, const void* weight, int32_t K, int32_t cin, int32_t cout,
+                                void* weight_t, hipStream_t stream);
+
+/*
+ * spc_conv_fwd_fused with the weights given transposed, weight_t [K, cout,
+ * cin] from spc_transpose_weight: the same result bit for bit.  The kernel
+ * then stages each offset's weights as plain contraction-contiguous copies
+ * instead of transposing them per tile, which pays for fp32 and for
+ * contractions of more than 64 16-bit channels (shorter ones read W's own
+ * layout with transposing LDS reads).  map_is_subm != 0 says map is a
+ * submanifold nbr (n_src == n_rows), whose tiles hit many offsets: a
+ * performance hint that selects the loop keeping two offsets of gathered
+ * rows in flight.  Other arguments and errors as spc_conv_fwd_fused.
+ */
+spc_status spc_conv_fwd_wt(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                           const void* weight_t, int32_t K, int32_t cout, const float* bias,
+                           const int32_t* map, int32_t map_is_subm, const int32_t* order, int64_t n_rows,
+                           const void* residual, int32_t relu, void* out, hipStream_t stream);
+
+/*
  * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput
  * and dfilter): din[i] = sum over (k, o) with map_fwd[k][o] = i of
  * dout[o] @ W[k]^T, computed output-stationary over the input rows:

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     conv_bwd_filter,
     conv_bwd_input,
     conv_fwd_fused,
+    conv_fwd_wt,
     gather_by_voxel_id,
     lib,
     make_geom,
@@ -21,5 +22,6 @@ from .binding import (  # noqa: F401
     sparse_maxpool_bwd,
     sparse_maxpool_fwd,
     subm_conv_fwd,
+    transpose_weight,
     version,
 )

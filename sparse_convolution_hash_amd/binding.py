@@ -26,7 +26,8 @@ _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4:
            5: "SPC_ERR_WORKSPACE", 6: "SPC_ERR_HIP"}
 
 EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
-           "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_conv_bwd_input",
+           "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_transpose_weight",
+           "spc_conv_fwd_wt", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
            "spc_conv_bwd_filter", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
            "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_last_error",
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_sparse_inverse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_conv_fwd_fused": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P],
+        "spc_transpose_weight": [_I32, _P, _I32, _I32, _I32, _P, _P],
+        "spc_conv_fwd_wt": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I64, _P, _I32, _P, _P],
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -248,10 +251,67 @@ def _conv_checks(x, weight, bias, dev):
         _need(bias, "bias", torch.float32, dev)
 
 
+def _pretranspose(dtype, cin: int, flag) -> bool:
+    """Whether a forward hands the kernel pre-transposed weights: for fp32
+    and for contractions of more than 64 16-bit channels, where staging W's
+    own layout would transpose every offset's weights once per tile (shorter
+    16-bit contractions read W's own layout with transposing LDS reads)."""
+    if flag is not None:
+        return bool(flag)
+    return dtype == torch.float32 or cin > 64
+
+
+def transpose_weight(weight: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """weight [K, cin, cout] -> [K, cout, cin] on the device (spc_transpose_weight)."""
+    _need(weight, "weight")
+    if weight.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {weight.dtype}")
+    if weight.dim() != 3:
+        raise ValueError("weight must be [K, Cin, Cout]")
+    K, cin, cout = weight.shape
+    if out is None:
+        out = torch.empty((K, cout, cin), dtype=weight.dtype, device=weight.device)
+    else:
+        _need(out, "out", weight.dtype, weight.device)
+        if tuple(out.shape) != (K, cout, cin):
+            raise ValueError(f"out must be [{K}, {cout}, {cin}], got {tuple(out.shape)}")
+    st = lib().spc_transpose_weight(_DTYPES[weight.dtype], _ptr(weight), K, cin, cout, _ptr(out),
+                                    _stream(weight.device))
+    _check(st, "spc_transpose_weight")
+    return out
+
+
+def conv_fwd_wt(feats: torch.Tensor, weight_t: torch.Tensor, bias: Optional[torch.Tensor],
+                map_: Optional[torch.Tensor], n_rows: int, map_is_subm: bool = False,
+                order: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                relu: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward with pre-transposed weights weight_t [K, Cout, Cin] (spc_conv_fwd_wt);
+    otherwise as conv_fwd_fused."""
+    dev = feats.device
+    _conv_checks(feats, weight_t, bias, dev)
+    for t, nm in ((map_, "map"), (order, "order")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
+    K, cout, cin = weight_t.shape
+    if residual is not None:
+        _need(residual, "residual", feats.dtype, dev)
+        if tuple(residual.shape) != (n_rows, cout):
+            raise ValueError(f"residual must be [{n_rows}, {cout}], got {tuple(residual.shape)}")
+    if out is None:
+        out = torch.empty((n_rows, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_conv_fwd_wt(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight_t), K, cout,
+                               _ptr(bias), _ptr(map_), 1 if map_is_subm else 0, _ptr(order), int(n_rows),
+                               _ptr(residual), 1 if relu else 0, _ptr(out), _stream(dev))
+    _check(st, "spc_conv_fwd_wt")
+    return out
+
+
 def subm_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                   nbr: Optional[torch.Tensor], order: Optional[torch.Tensor] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[c] = bias + sum_k feats[nbr[c, k]] @ W[k] (spc_subm_conv_fwd)."""
+                  out: Optional[torch.Tensor] = None, pretranspose: Optional[bool] = None) -> torch.Tensor:
+    """out[c] = bias + sum_k feats[nbr[c, k]] @ W[k] (spc_subm_conv_fwd, or
+    spc_transpose_weight + spc_conv_fwd_wt when `pretranspose`, by default
+    for fp32 and Cin > 64: the same result bit for bit)."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     K, cin, cout = weight.shape
@@ -259,6 +319,11 @@ def subm_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
     for t, nm in ((nbr, "nbr"), (order, "order")):
         if t is not None:
             _need(t, nm, torch.int32, dev)
+    if _pretranspose(feats.dtype, cin, pretranspose):
+        if K > 1 and nbr is None:
+            raise ValueError("nbr is required for K > 1")
+        return conv_fwd_wt(feats, transpose_weight(weight), bias, nbr if K > 1 else None, n, K > 1,
+                           order if K > 1 else None, out=out)
     if out is None:
         out = torch.empty((n, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_subm_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), n, cin, _ptr(weight), K, cout, _ptr(bias),
@@ -269,14 +334,17 @@ def subm_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
 
 def sparse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                     nbr_out: torch.Tensor, n_out: int, order: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Strided forward over the n_out output rows of a strided kernel map (spc_sparse_conv_fwd)."""
+                    out: Optional[torch.Tensor] = None, pretranspose: Optional[bool] = None) -> torch.Tensor:
+    """Strided forward over the n_out output rows of a strided kernel map
+    (spc_sparse_conv_fwd; `pretranspose` as for subm_conv_fwd)."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     _need(nbr_out, "nbr_out", torch.int32, dev)
     if order is not None:
         _need(order, "order", torch.int32, dev)
     K, cin, cout = weight.shape
+    if _pretranspose(feats.dtype, cin, pretranspose):
+        return conv_fwd_wt(feats, transpose_weight(weight), bias, nbr_out, n_out, False, order, out=out)
     if out is None:
         out = torch.empty((n_out, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_sparse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,
@@ -287,15 +355,19 @@ def sparse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[to
 
 def sparse_inverse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                             nbr_in: torch.Tensor, n_fine: int, order_in: Optional[torch.Tensor] = None,
-                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                            out: Optional[torch.Tensor] = None,
+                            pretranspose: Optional[bool] = None) -> torch.Tensor:
     """Inverse (upsampling) forward onto the input sites of a strided kernel map
-    (spc_sparse_inverse_conv_fwd): feats [n_coarse, cin] -> [n_fine, cout]."""
+    (spc_sparse_inverse_conv_fwd): feats [n_coarse, cin] -> [n_fine, cout];
+    `pretranspose` as for subm_conv_fwd."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     _need(nbr_in, "nbr_in", torch.int32, dev)
     if order_in is not None:
         _need(order_in, "order_in", torch.int32, dev)
     K, cin, cout = weight.shape
+    if _pretranspose(feats.dtype, cin, pretranspose):
+        return conv_fwd_wt(feats, transpose_weight(weight), bias, nbr_in, n_fine, False, order_in, out=out)
     if out is None:
         out = torch.empty((n_fine, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_sparse_inverse_conv_fwd(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K,
@@ -308,9 +380,10 @@ def sparse_inverse_conv_fwd(feats: torch.Tensor, weight: torch.Tensor, bias: Opt
 def conv_fwd_fused(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                    map_: Optional[torch.Tensor], n_rows: int, order: Optional[torch.Tensor] = None,
                    residual: Optional[torch.Tensor] = None, relu: bool = False,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, pretranspose: Optional[bool] = None) -> torch.Tensor:
     """Forward over any map with the fused bias + residual + ReLU epilogue
-    (spc_conv_fwd_fused); ``out`` may be ``residual`` itself."""
+    (spc_conv_fwd_fused); ``out`` may be ``residual`` itself; `pretranspose`
+    as for subm_conv_fwd."""
     dev = feats.device
     _conv_checks(feats, weight, bias, dev)
     for t, nm in ((map_, "map"), (order, "order")):
@@ -321,6 +394,8 @@ def conv_fwd_fused(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[tor
         _need(residual, "residual", feats.dtype, dev)
         if tuple(residual.shape) != (n_rows, cout):
             raise ValueError(f"residual must be [{n_rows}, {cout}], got {tuple(residual.shape)}")
+    if _pretranspose(feats.dtype, cin, pretranspose):
+        return conv_fwd_wt(feats, transpose_weight(weight), bias, map_, n_rows, False, order, residual, relu, out)
     if out is None:
         out = torch.empty((n_rows, cout), dtype=feats.dtype, device=dev)
     st = lib().spc_conv_fwd_fused(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight), K, cout,

@@ -590,6 +590,25 @@ spc_status run_conv(spc_dtype dt, ConvArgs& a, bool trans, hipStream_t stream) {
     return fail(SPC_ERR_ARG, "unknown dtype %d", int(dt));
 }
 
+// weight_t[k][n][c] = w[k][c][n]: one 32 x 32 block of one offset's matrix
+// per workgroup, through an LDS tile padded against bank conflicts, so that
+// both the reads and the writes run along rows
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_w(const T* __restrict__ w, T* __restrict__ wt, int cin,
+                                                     int cout) {
+    __shared__ T t[32][33];
+    const int64_t base = int64_t(blockIdx.z) * cin * cout;
+    const int c0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int i = ty; i < 32; i += 8)
+        if (c0 + i < cin && n0 + tx < cout) t[i][tx] = w[base + int64_t(c0 + i) * cout + n0 + tx];
+    __syncthreads();
+#pragma unroll
+    for (int i = ty; i < 32; i += 8)
+        if (n0 + i < cout && c0 + tx < cin) wt[base + int64_t(n0 + i) * cin + c0 + tx] = t[tx][i];
+}
+
 spc_status check_common(spc_dtype dt, int64_t n_rows, int64_t n_src, int32_t cin, int32_t cout, int32_t K,
                         const void* x, const void* w, const float* bias, const void* y, const int32_t* map,
                         const int32_t* order, bool map_required) {
@@ -669,6 +688,50 @@ extern "C" spc_status spc_conv_fwd_fused(spc_dtype dtype, const void* feats, int
     ConvArgs a{feats, weight, bias, identity ? nullptr : map, identity ? nullptr : order, out, int32_t(n_rows),
                int32_t(n_src), K, cin, cout, cin, cout, 0, 0, residual, relu ? 1 : 0};
     return run_conv(dtype, a, true, stream);
+}
+
+extern "C" spc_status spc_transpose_weight(spc_dtype dtype, const void* weight, int32_t K, int32_t cin, int32_t cout,
+                                           void* weight_t, hipStream_t stream) {
+    clear_error();
+    if (dtype != SPC_F32 && dtype != SPC_F16 && dtype != SPC_BF16) return fail(SPC_ERR_ARG, "unknown dtype %d", int(dtype));
+    if (K <= 0 || K > 343 || cin <= 0 || cout <= 0 || cin > 65535 * 32 || cout > 2147483647 / 32)
+        return fail(SPC_ERR_ARG, "K=%d cin=%d cout=%d out of range", K, cin, cout);
+    if (!weight || !weight_t) return fail(SPC_ERR_ARG, "weight pointer is NULL");
+    const size_t es = dtype == SPC_F32 ? 4 : 2;
+    const size_t bytes = size_t(K) * size_t(cin) * size_t(cout) * es;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(weight), b0 = reinterpret_cast<uintptr_t>(weight_t);
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(SPC_ERR_ARG, "weight and weight_t overlap");
+    const dim3 grid(unsigned(ceil_div(cout, 32)), unsigned(ceil_div(cin, 32)), unsigned(K));
+    if (es == 4)
+        hipLaunchKernelGGL(k_transpose_w<uint32_t>, grid, dim3(256), 0, stream, static_cast<const uint32_t*>(weight),
+                           static_cast<uint32_t*>(weight_t), cin, cout);
+    else
+        hipLaunchKernelGGL(k_transpose_w<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(weight),
+                           static_cast<uint16_t*>(weight_t), cin, cout);
+    SPC_LAUNCHED("k_transpose_w");
+    return SPC_OK;
+}
+
+extern "C" spc_status spc_conv_fwd_wt(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                                      const void* weight_t, int32_t K, int32_t cout, const float* bias,
+                                      const int32_t* map, int32_t map_is_subm, const int32_t* order, int64_t n_rows,
+                                      const void* residual, int32_t relu, void* out, hipStream_t stream) {
+    clear_error();
+    const bool identity = K == 1 && map == nullptr;
+    if (identity && n_src != n_rows)
+        return fail(SPC_ERR_ARG, "an identity map needs n_src == n_rows (%lld vs %lld)", (long long)n_src,
+                    (long long)n_rows);
+    spc_status st =
+        check_common(dtype, n_rows, n_src, cin, cout, K, feats, weight_t, bias, out, map, order, !identity);
+    if (st != SPC_OK) return st;
+    if (residual && !aligned16(residual)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
+    // the dinput staging with the roles of the weight's dims exchanged:
+    // slab entry B[kk][n] = weight_t[k][n][kk], a row of weight_t per output
+    // channel, contraction-contiguous (weight dims: cout rows of cin)
+    ConvArgs a{feats, weight_t, bias, identity ? nullptr : map, identity ? nullptr : order, out, int32_t(n_rows),
+               int32_t(n_src), K, cin, cout, cout, cin, 0, 0, residual, relu ? 1 : 0};
+    a.dense = map_is_subm && !identity;
+    return run_conv(dtype, a, false, stream);
 }
 
 extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int64_t n_out, int32_t cout,

@@ -112,6 +112,25 @@ def test_conv_host_checks():
                                  8, None) == B.SPC_ERR_WORKSPACE
 
 
+def test_pretransposed_forward_host_checks():
+    L = B.lib()
+    tw = lambda dt, K, cin, cout, w=FAKE, wt=ctypes.c_void_p(0x200000): L.spc_transpose_weight(dt, w, K, cin, cout,
+                                                                                              wt, None)
+    assert tw(7, 27, 16, 16) == B.SPC_ERR_ARG                   # dtype
+    assert tw(2, 0, 16, 16) == B.SPC_ERR_ARG                    # K
+    assert tw(2, 27, 0, 16) == B.SPC_ERR_ARG                    # cin
+    assert tw(2, 27, 16, 16, w=None) == B.SPC_ERR_ARG
+    assert tw(2, 27, 256, 256) == B.SPC_ERR_ARG                 # 0x100000 + 3.5 MB overlaps 0x200000
+    assert "overlap" in L.spc_last_error().decode()
+    fwd = lambda dt, cin, cout, K, m=FAKE, n_src=100, n_rows=100: L.spc_conv_fwd_wt(
+        dt, FAKE, n_src, cin, FAKE, K, cout, None, m, 1, None, n_rows, None, 0, FAKE, None)
+    assert fwd(2, 24, 32, 27) == B.SPC_ERR_UNSUPPORTED          # cin not a multiple of 16
+    assert fwd(7, 32, 32, 27) == B.SPC_ERR_ARG                  # dtype
+    assert fwd(2, 32, 32, 27, m=None) == B.SPC_ERR_ARG          # map required for K > 1
+    assert fwd(2, 32, 32, 1, m=None, n_src=10) == B.SPC_ERR_ARG  # identity needs n_src == n_rows
+    assert fwd(2, 32, 32, 27, n_rows=0) == B.SPC_OK             # zero rows: nothing launched
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):

@@ -101,6 +101,37 @@ def test_strided_small(dtype, shape, k, s, p, d, cin, cout):
     assert_close(db, OC.conv_bwd_bias(t["grad"]), TOL_DW, "dbias")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("seed,cin,cout,k", [(11, 128, 128, 3), (12, 96, 64, 3), (13, 144, 32, 1), (14, 32, 48, 3)])
+def test_pretransposed_weights_bit_identical(dtype, seed, cin, cout, k):
+    """Pre-transposed weights (spc_transpose_weight + spc_conv_fwd_wt) stage the
+    same LDS slabs as the per-tile transpose, so every forward agrees bit for bit."""
+    if dtype == torch.float32 and cin > 128:
+        pytest.skip("fp32 contraction is limited to 128 channels")
+    print(f"pretransposed seed={seed} cin={cin} cout={cout} k={k} {dtype}", flush=True)
+    c, t = _subm_case(seed, 12, 0.35, 2, k, cin, cout, dtype)
+    x, w, b = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"])
+    assert torch.equal(spc.transpose_weight(w), w.transpose(1, 2).contiguous())
+    km = spc.build_kmap(cuda(c), 2, (12,) * 3, k, orders=True)
+    nbr, order = (km["nbr"], km["order"]) if k > 1 else (None, None)
+    n = c.shape[0]
+    direct = spc.subm_conv_fwd(x, w, b, nbr, order, pretranspose=False)
+    assert torch.equal(direct, spc.subm_conv_fwd(x, w, b, nbr, order, pretranspose=True))
+    res = cuda(t["grad"][:, :cout]) if t["grad"].shape[1] >= cout else None
+    f0 = spc.conv_fwd_fused(x, w, b, nbr, n, order, residual=res, relu=True, pretranspose=False)
+    assert torch.equal(f0, spc.conv_fwd_fused(x, w, b, nbr, n, order, residual=res, relu=True, pretranspose=True))
+    if k > 1:  # a strided layer and its inverse on the same sites
+        ks = spc.build_kmap(cuda(c), 2, (12,) * 3, 3, 2, 1, 1, subm=False, orders=True)
+        s0 = spc.sparse_conv_fwd(x, w, b, ks["nbr"], ks["n_out"], ks["order"], pretranspose=False)
+        assert torch.equal(s0, spc.sparse_conv_fwd(x, w, b, ks["nbr"], ks["n_out"], ks["order"], pretranspose=True))
+        ref = O.strided_kmap(c, 2, (12,) * 3, 3, 2, 1, 1)
+        assert_close(s0, OC.conv_fwd(t["feats"], t["weight"], t["bias"], ref["nbr_out"]), TOL[dtype], "strided")
+        wi = w.transpose(1, 2).contiguous()  # cout -> cin back onto the input sites
+        i0 = spc.sparse_inverse_conv_fwd(s0, wi, None, ks["nbr_in"], n, ks["order_in"], pretranspose=False)
+        assert torch.equal(i0, spc.sparse_inverse_conv_fwd(s0, wi, None, ks["nbr_in"], n, ks["order_in"],
+                                                            pretranspose=True))
+
+
 def test_deterministic():
     c, t = _subm_case(8, 20, 0.3, 2, 3, 64, 64, torch.bfloat16)
     km = spc.build_kmap(cuda(c), 2, (20,) * 3, 3, orders=True)
