@@ -1,0 +1,11 @@
+// The BF16 variants of the fused convolution kernel (conv_kernel.h).
+#define SPC_CONV_KERNELS
+#include "conv_kernel.h"
+
+namespace spc {
+
+spc_status run_conv_bf16(ConvArgs& a, bool trans, hipStream_t stream) {
+    return trans ? launch_conv_t<BF16, true>(a, stream) : launch_conv_t<BF16, false>(a, stream);
+}
+
+}  // namespace spc
