@@ -173,8 +173,11 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
 // the most 16x16 blocks a wave holds (channel tiles of up to 32*MIM x
 // 32*NOM).  DEPTH: steps of rows in flight (2 fits the registers only with
 // small accumulator tiles); pair indices are fetched one step earlier still.
-template <typename TT, bool IDENT, int MIM, int NOM, int DEPTH>
-__global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
+// FULL: every channel tile is exactly 2 x MIM by 2 x NOM blocks of 16, so no
+// block needs a bound check (the checks would split the MFMA loop into one
+// branch per block, each waiting for every LDS read before it)
+template <typename TT, bool IDENT, int MIM, int NOM, int DEPTH, bool FULL>
+__global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_dfilter(DfArgs a) {
     static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps of rows in flight");
     constexpr int E = TT::E;
     constexpr int ROW = lds_row<TT>();
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
     const int lr = lane & 15, lg = lane >> 4;
     const int wi = wave >> 1, wo = wave & 1;
-    const int MI = (TI / 16 + 1) / 2, NO = (TO / 16 + 1) / 2;  // 16x16 blocks per wave (<= MIM, NOM)
+    const int MI = FULL ? MIM : (TI / 16 + 1) / 2, NO = FULL ? NOM : (TO / 16 + 1) / 2;  // 16x16 blocks per wave (<= MIM, NOM)
     constexpr int PG = PS / E;
     const int xi_items = PG * (TI / E), items = xi_items + PG * (TO / E);
 
@@ -254,17 +257,17 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
             u32x4 gf[NOM], xf[MIM];
 #pragma unroll
             for (int no = 0; no < NOM; ++no)
-                if (no < NO && (wo * NO + no) * 16 < TO)
+                if (FULL || (no < NO && (wo * NO + no) * 16 < TO))
                     gf[no] = ld16(gt + ((wo * NO + no) * 16 + lr) * ROW + poff);
 #pragma unroll
             for (int mi = 0; mi < MIM; ++mi)
-                if (mi < MI && (wi * MI + mi) * 16 < TI)
+                if (FULL || (mi < MI && (wi * MI + mi) * 16 < TI))
                     xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
 #pragma unroll
             for (int mi = 0; mi < MIM; ++mi)
 #pragma unroll
                 for (int no = 0; no < NOM; ++no)
-                    if (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)
+                    if (FULL || (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO))
                         acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
         }
         if (nxt.k != cur.k) {
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(DT) void k_dfilter(DfArgs a) {
             for (int mi = 0; mi < MIM; ++mi)
 #pragma unroll
                 for (int no = 0; no < NOM; ++no) {
-                    if (!(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
+                    if (!FULL && !(mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO)) continue;
                     const int ci = ci0 + (wi * MI + mi) * 16 + lr;
                     const int co = co0 + (wo * NO + no) * 16 + lg * 4;
                     *reinterpret_cast<f32x4_t*>(part + int64_t(ci) * a.cout + co) = acc[mi][no];
@@ -450,12 +453,21 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
     // registers only next to the smaller accumulators
     const int mim = std::min<int64_t>(a.cin, TMAX) > 64 ? 4 : 2, nom = std::min<int64_t>(a.cout, TMAX) > 64 ? 4 : 2;
     const dim3 grid(unsigned(b.nseg), tiles);
-#define SPC_DFILTER(MIM_, NOM_, DEPTH_)                                                                     \
-    do {                                                                                                    \
-        if (a.ptr)                                                                                          \
-            hipLaunchKernelGGL((k_dfilter<TT, false, MIM_, NOM_, DEPTH_>), grid, dim3(DT), 0, stream, b);    \
-        else                                                                                                \
-            hipLaunchKernelGGL((k_dfilter<TT, true, MIM_, NOM_, DEPTH_>), grid, dim3(DT), 0, stream, b);     \
+    // every tile full: 64 channels for 2 blocks per wave, multiples of 128 for 4
+    const bool full = (mim == 2 ? a.cin == 64 : a.cin % TMAX == 0) && (nom == 2 ? a.cout == 64 : a.cout % TMAX == 0);
+#define SPC_DFILTER_F(MIM_, NOM_, DEPTH_, FULL_)                                                                 \
+    do {                                                                                                        \
+        if (a.ptr)                                                                                              \
+            hipLaunchKernelGGL((k_dfilter<TT, false, MIM_, NOM_, DEPTH_, FULL_>), grid, dim3(DT), 0, stream, b); \
+        else                                                                                                    \
+            hipLaunchKernelGGL((k_dfilter<TT, true, MIM_, NOM_, DEPTH_, FULL_>), grid, dim3(DT), 0, stream, b);  \
+    } while (0)
+#define SPC_DFILTER(MIM_, NOM_, DEPTH_)                                   \
+    do {                                                                  \
+        if (full)                                                         \
+            SPC_DFILTER_F(MIM_, NOM_, DEPTH_, true);                      \
+        else                                                              \
+            SPC_DFILTER_F(MIM_, NOM_, DEPTH_, false);                     \
     } while (0)
     if (mim == 2 && nom == 2)
         SPC_DFILTER(2, 2, 2);
@@ -466,6 +478,7 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
     else
         SPC_DFILTER(4, 4, 1);
 #undef SPC_DFILTER
+#undef SPC_DFILTER_F
     SPC_LAUNCHED("k_dfilter");
     const int64_t L = int64_t(a.cin) * a.cout;
     hipLaunchKernelGGL(k_reduce_segs, dim3(unsigned(L / 256), unsigned(a.K)), dim3(256), 0, stream, b, dw);
