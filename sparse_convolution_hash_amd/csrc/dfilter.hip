@@ -475,8 +475,10 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
         SPC_DFILTER(2, 4, 2);
     else if (nom == 2)
         SPC_DFILTER(4, 2, 2);
+    else if (full)  // two steps of rows in flight fit two waves per SIMD only without the bound checks
+        SPC_DFILTER_F(4, 4, 2, true);
     else
-        SPC_DFILTER(4, 4, 1);
+        SPC_DFILTER_F(4, 4, 1, false);
 #undef SPC_DFILTER
 #undef SPC_DFILTER_F
     SPC_LAUNCHED("k_dfilter");
