@@ -370,8 +370,15 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     WStage<TT, BN, TRANS, ROWS> wst;
     wst.init(a, col0);
     u32x4 acur[RB][KCMAX], anext[RB][KCMAX];
+    // the identity map (K = 1) has one offset, whose entries are the rows
+    // themselves: its column is rsrc, and nothing is staged
+    int32_t* const cols = a.map ? tile : rsrc;
     for (int kt0 = 0; kt0 < a.K; kt0 += KTILE) {
         const int kt = min(KTILE, a.K - kt0);
+        if (!a.map) {
+            if (threadIdx.x == 0) list[0] = 0, list[KTILE] = 1;
+            __syncthreads();  // rsrc, the bias and the list are in place
+        } else {
         __syncthreads();  // earlier readers of tile / list / slabs are done
         if (threadIdx.x < KTILE) flags[threadIdx.x] = 0;
         __syncthreads();
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             const int dq = CT / kt, dr = CT - dq * kt;
             const int r0 = int(threadIdx.x) / kt, j0 = int(threadIdx.x) - r0 * kt;
             int32_t v[MPT];
-            if (a.map) {
+            {
                 int r = r0, j = j0;
 #pragma unroll
                 for (int u = 0; u < MPT; ++u) {
@@ -398,16 +405,13 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                     j += dr;
                     if (j >= kt) j -= kt, ++r;
                 }
-            } else {  // identity map (K = 1): the entry is the row itself
-#pragma unroll
-                for (int u = 0; u < MPT; ++u) v[u] = 0;
             }
             int r = r0, j = j0;
 #pragma unroll
             for (int u = 0; u < MPT; ++u) {
                 if (r < BM) {
                     const int32_t src = rsrc[r];
-                    int32_t val = src < 0 ? -1 : a.map ? v[u] : src;
+                    int32_t val = src < 0 ? -1 : v[u];
                     if ((unsigned)val >= (unsigned)a.n_src) val = -1;
                     tile[j * BMP + r] = val;
                     if (val >= 0) flags[j] = 1;
@@ -425,6 +429,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             if (lane == 0) list[KTILE] = __popcll(b);
         }
         __syncthreads();
+        }
         const int nk = list[KTILE];
         if (nk == 0) continue;
 
@@ -513,15 +518,15 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             auto step = [&](int j, const u32x4 (&cur)[RB][KCMAX], bool any, u32x4 (&pre)[RB][KCMAX], bool& any_pre) {
                 const int jn = min(j + 1, nk - 1);
                 wst.load_buf(a, wr, slab_of(jn), j + 1 < nk);
-                any_pre = gather_buf<TT, RB, KCMAX>(pre, a, xr, tile + list[min(j + 2, nk - 1)] * BMP, j + 2 < nk,
+                any_pre = gather_buf<TT, RB, KCMAX>(pre, a, xr, cols + list[min(j + 2, nk - 1)] * BMP, j + 2 < nk,
                                                     wave, lr, lg);
                 if (any) mma(cur, j);
                 wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(jn));
                 lds_barrier();
             };
             wst.load_buf(a, wr, slab_of(0), true);
-            fa = gather_buf<TT, RB, KCMAX>(ga, a, xr, tile + list[0] * BMP, true, wave, lr, lg);
-            fb = gather_buf<TT, RB, KCMAX>(gb, a, xr, tile + list[min(1, nk - 1)] * BMP, nk > 1, wave, lr, lg);
+            fa = gather_buf<TT, RB, KCMAX>(ga, a, xr, cols + list[0] * BMP, true, wave, lr, lg);
+            fb = gather_buf<TT, RB, KCMAX>(gb, a, xr, cols + list[min(1, nk - 1)] * BMP, nk > 1, wave, lr, lg);
             wst.store(lds, a, slab_of(0));
             lds_barrier();
             for (int j = 0; j < nk; j += 3) {
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             continue;
         }
         wst.load(a, slab_of(0));
-        bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, tile + list[0] * BMP, wave, lr, lg);
+        bool any_cur = gather_rows<TT, RB, KCMAX>(acur, a, cols + list[0] * BMP, wave, lr, lg);
         wst.store(lds, a, slab_of(0));
         // drain the prologue's gathers here, so that inside the loop the only
         // loads in flight are the next offset's prefetches and the MFMAs need
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             bool any_next = false;
             if (has_next) {
                 wst.load(a, slab_of(j + 1));
-                any_next = gather_rows<TT, RB, KCMAX>(anext, a, tile + list[j + 1] * BMP, wave, lr, lg);
+                any_next = gather_rows<TT, RB, KCMAX>(anext, a, cols + list[j + 1] * BMP, wave, lr, lg);
             }
             if (any_cur) mma(acur, j);
             if (has_next) wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(j + 1));
