@@ -19,9 +19,10 @@
 // (or v_mfma_f32_16x16x4_f32).  The fp32 accumulators stay in registers for
 // the whole offset loop; each output row is written once, with the bias added
 // and one rounding, so there are no atomics and the result is deterministic.
-// The fused implicit-GEMM convolution kernel and its launchers, shared by the
-// per-dtype translation units conv_f32.hip, conv_f16.hip and conv_bf16.hip
-// (one each, so that the many variants compile in parallel); conv.hip holds
+//
+// This header holds the kernel and its launchers; the per-dtype translation
+// units conv_f32.hip, conv_f16.hip and conv_bf16.hip instantiate them (one
+// each, so that the many variants compile in parallel), and conv.hip holds
 // the C entry points.
 #pragma once
 
