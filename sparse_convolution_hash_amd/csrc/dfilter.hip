@@ -450,7 +450,8 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
     b.nseg = int32_t(std::max<int64_t>(64, MAX_WG / tiles));
     // accumulator extent per wave: 2 or 4 blocks of 16 per dimension (a
     // 128-channel tile needs 4); two steps of rows in flight fit the
-    // registers only next to the smaller accumulators
+    // registers next to the smaller accumulators, and next to the 4 x 4 ones
+    // only in the full-tile variant
     const int mim = std::min<int64_t>(a.cin, TMAX) > 64 ? 4 : 2, nom = std::min<int64_t>(a.cout, TMAX) > 64 ? 4 : 2;
     const dim3 grid(unsigned(b.nseg), tiles);
     // every tile full: 64 channels for 2 blocks per wave, multiples of 128 for 4
