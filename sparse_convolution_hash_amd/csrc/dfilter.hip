@@ -166,6 +166,86 @@ __device__ __forceinline__ void store_item(char* xt, char* gt, const Item<TT>& i
     }
 }
 
+// Staging with transposing reads (16-bit full tiles): a step's rows stay
+// pair-major in LDS, as they were loaded, and each MFMA fragment (8
+// consecutive pairs of one channel) comes from two ds_read_b64_tr_b16 reads
+// (within a 16-lane group, lane i receives element i & 3 of the rows that
+// lanes 4q + (i >> 2) point at).  Slot q of thread t holds 16-byte chunk
+// t + DT*q of the step: the x chunks first (TI / 8 per pair), then the dy
+// chunks (TO / 8 per pair), so 16 consecutive lanes read whole rows and a
+// load instruction touches a few rows, not one row per lane.
+template <int MIM, int NOM>
+struct TrGeo {
+    static constexpr int TI = 32 * MIM, TO = 32 * NOM;     // the full tile's channels
+    static constexpr int XC = PS * TI / 8;                 // x chunks of a step (a multiple of DT)
+    static constexpr int NQ = PS * (TI + TO) / 8 / DT;     // slots per thread
+    static constexpr int RSX = TI * 2 + 32, RSG = TO * 2 + 32;  // LDS row strides (bytes), padded against bank conflicts
+    static_assert(XC % DT == 0 && NQ * DT * 8 == PS * (TI + TO) && NQ <= 8, "whole slots per thread");
+    __device__ static constexpr bool is_x(int q) { return q * DT < XC; }
+    __device__ static constexpr int cpr(int q) { return is_x(q) ? TI / 8 : TO / 8; }
+    __device__ static int pair(int q) {
+        const int qq = is_x(q) ? q : q - XC / DT;
+        return int(threadIdx.x) / cpr(q) + qq * (DT / cpr(q));
+    }
+    __device__ static int chunk(int q) { return int(threadIdx.x) % cpr(q); }
+};
+
+template <typename TT, bool IDENT, int MIM, int NOM>
+__device__ __forceinline__ void load_idx_tr(int32_t (&r)[TT::E], const DfArgs& a, const Step& st) {
+    using G = TrGeo<MIM, NOM>;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) {
+        const int64_t p = st.b + G::pair(q);
+        const int64_t pc = p < st.e ? p : st.e - 1;
+        if constexpr (IDENT)
+            r[q] = int32_t(pc);
+        else
+            r[q] = (G::is_x(q) ? a.pin : a.pout)[pc];
+    }
+}
+
+template <typename TT, int MIM, int NOM>
+__device__ __forceinline__ void load_rows_tr(Item<TT>& it, const int32_t (&r)[TT::E], const DfArgs& a, int ci0,
+                                             int co0, const Step& st) {
+    using S = typename TT::storage;
+    using G = TrGeo<MIM, NOM>;
+    it.ok = 0;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) {
+        const bool x = G::is_x(q);
+        const S* src = x ? static_cast<const S*>(a.x) : static_cast<const S*>(a.dy);
+        const int C = x ? a.cin : a.cout;
+        const int32_t lim = x ? a.n_in : a.n_out;
+        const bool ok = st.b + G::pair(q) < st.e && (unsigned)r[q] < (unsigned)lim;
+        it.in[q] = ld16(src + int64_t(ok ? r[q] : 0) * C + (x ? ci0 : co0) + G::chunk(q) * 8);
+        it.ok |= uint32_t(ok) << q;
+    }
+}
+
+template <typename TT, int MIM, int NOM>
+__device__ __forceinline__ void store_item_tr(char* xt, char* gt, const Item<TT>& it) {
+    using G = TrGeo<MIM, NOM>;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) {
+        const bool x = G::is_x(q);
+        char* dst = (x ? xt : gt) + G::pair(q) * (x ? G::RSX : G::RSG) + G::chunk(q) * 16;
+        st16(dst, (it.ok >> q) & 1u ? it.in[q] : zero4());
+    }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// One MFMA fragment from the pair-major tile: channel n0 + (lane & 15), pairs
+// k0 .. k0 + 7 with k0 = 8 * (lane >> 4) + 32 * ks
+__device__ __forceinline__ u32x4 tr_fragment(const char* tile, int rs, int n0, int ks, int lr, int lg) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* p0 = tile + ((ks * 4 + lg) * 8 + (lr >> 2)) * rs + n0 * 2 + 8 * (lr & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * rs));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
 // Workgroup b walks segment b of the pair list in steps; each offset it
 // touches gets one partial tile, part[b + k] (b + k is distinct for every
 // (segment, offset) pair a walk can meet, as both only grow along it).
@@ -205,6 +285,20 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const int my = threadIdx.x;
     const bool has_item = my < items;
     const ItemGeo geo(has_item ? my : items - 1, xi_items, E);
+    // 16-bit full tiles stage rows pair-major and read fragments transposed
+    constexpr bool TR = FULL && E == 8;
+    auto idx_of = [&](int32_t (&r)[E], const Step& st) {
+        if constexpr (TR)
+            load_idx_tr<TT, IDENT, MIM, NOM>(r, a, st);
+        else
+            load_idx<TT, IDENT>(r, a, geo, st);
+    };
+    auto rows_of = [&](Item<TT>& it, const int32_t (&r)[E], const Step& st) {
+        if constexpr (TR)
+            load_rows_tr<TT, MIM, NOM>(it, r, a, ci0, co0, st);
+        else
+            load_rows<TT>(it, r, a, geo, ci0, co0, st);
+    };
 
     f32x4_t acc[MIM][NOM];
 #pragma unroll
@@ -221,12 +315,12 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     int32_t ia[E], ib[E];  // pair indices of the step whose rows are loaded next
     {
         int32_t r0[E], r1[E];
-        load_idx<TT, IDENT>(r0, a, geo, cur);
-        if (DEPTH == 2 && nxt.k >= 0) load_idx<TT, IDENT>(r1, a, geo, nxt);
+        idx_of(r0, cur);
+        if (DEPTH == 2 && nxt.k >= 0) idx_of(r1, nxt);
         const Step& ahead = DEPTH == 2 ? nx2 : nxt;
-        if (ahead.k >= 0) load_idx<TT, IDENT>(ia, a, geo, ahead);
-        load_rows<TT>(ra, r0, a, geo, ci0, co0, cur);
-        if (DEPTH == 2 && nxt.k >= 0) load_rows<TT>(rb, r1, a, geo, ci0, co0, nxt);
+        if (ahead.k >= 0) idx_of(ia, ahead);
+        rows_of(ra, r0, cur);
+        if (DEPTH == 2 && nxt.k >= 0) rows_of(rb, r1, nxt);
     }
 
     // one step: cur's rows are in `mine`, which is then refilled with the
@@ -237,8 +331,9 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         const Step after = ahead.k >= 0 ? step_at(sptr, ahead.e, ahead.k, s1) : Step{0, 0, -1};
         // LDS-only barriers: the rows of the steps ahead stay in flight across them
         lds_barrier();  // the previous step's tiles are consumed
-        if (has_item) store_item<TT>(xt, gt, mine, my, xi_items);
-        for (int it = my + DT; it < items; it += DT) {  // more items than threads (fp32): not pipelined
+        if constexpr (TR) store_item_tr<TT, MIM, NOM>(xt, gt, mine);
+        else if (has_item) store_item<TT>(xt, gt, mine, my, xi_items);
+        for (int it = my + DT; !TR && it < items; it += DT) {  // more items than threads (fp32): not pipelined
             const ItemGeo g2(it, xi_items, E);
             int32_t r2[E];
             Item<TT> tmp;
@@ -248,13 +343,20 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
         }
         lds_barrier();
         if (ahead.k >= 0) {
-            load_rows<TT>(mine, use, a, geo, ci0, co0, ahead);
-            if (after.k >= 0) load_idx<TT, IDENT>(fill, a, geo, after);
+            rows_of(mine, use, ahead);
+            if (after.k >= 0) idx_of(fill, after);
         }
 #pragma unroll
         for (int ks = 0; ks < PS / (4 * E); ++ks) {
             const int poff = (ks * 4 + lg) * 16;
             u32x4 gf[NOM], xf[MIM];
+            if constexpr (TR) {
+                using G = TrGeo<MIM, NOM>;
+#pragma unroll
+                for (int no = 0; no < NOM; ++no) gf[no] = tr_fragment(gt, G::RSG, (wo * NOM + no) * 16, ks, lr, lg);
+#pragma unroll
+                for (int mi = 0; mi < MIM; ++mi) xf[mi] = tr_fragment(xt, G::RSX, (wi * MIM + mi) * 16, ks, lr, lg);
+            } else {
 #pragma unroll
             for (int no = 0; no < NOM; ++no)
                 if (FULL || (no < NO && (wo * NO + no) * 16 < TO))
@@ -263,6 +365,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             for (int mi = 0; mi < MIM; ++mi)
                 if (FULL || (mi < MI && (wi * MI + mi) * 16 < TI))
                     xf[mi] = ld16(xt + ((wi * MI + mi) * 16 + lr) * ROW + poff);
+            }
 #pragma unroll
             for (int mi = 0; mi < MIM; ++mi)
 #pragma unroll
