@@ -183,11 +183,10 @@ struct TrGeo {
     static_assert(XC % DT == 0 && NQ * DT * 8 == PS * (TI + TO) && NQ <= 8, "whole slots per thread");
     __device__ static constexpr bool is_x(int q) { return q * DT < XC; }
     __device__ static constexpr int cpr(int q) { return is_x(q) ? TI / 8 : TO / 8; }
-    __device__ static int pair(int q) {
-        const int qq = is_x(q) ? q : q - XC / DT;
-        return int(threadIdx.x) / cpr(q) + qq * (DT / cpr(q));
-    }
-    __device__ static int chunk(int q) { return int(threadIdx.x) % cpr(q); }
+    // chunk index of slot q within its operand's part of the step
+    __device__ static int slot(int q) { return int(threadIdx.x) + DT * (is_x(q) ? q : q - XC / DT); }
+    __device__ static int pair(int q) { return slot(q) / cpr(q); }
+    __device__ static int chunk(int q) { return slot(q) % cpr(q); }
 };
 
 template <typename TT, bool IDENT, int MIM, int NOM>
@@ -581,6 +580,10 @@ spc_status launch_dfilter(const DfArgs& a, float* dw, float* dbias, float* bias_
         SPC_DFILTER(4, 2, 2);
     else if (full)  // two steps of rows in flight fit two waves per SIMD only without the bound checks
         SPC_DFILTER_F(4, 4, 2, true);
+    else if (TT::E == 8 && a.cin == 96 && a.cout == 96) {
+        // 96-channel 16-bit layers: full tiles of 2 x 3 blocks, with the transposing reads
+        if constexpr (TT::E == 8) SPC_DFILTER_F(3, 3, 2, true);
+    }
     else
         SPC_DFILTER_F(4, 4, 1, false);
 #undef SPC_DFILTER
