@@ -146,9 +146,20 @@ spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int64_t n, int3
                              const int32_t* nbr, const int32_t* order, void* out, hipStream_t stream);
 
 /*
- * Strided forward: out[o] = bias + sum_k feats[nbr_out[o*K + k]] @ W[k] for
- * the n_out output rows of a strided spc_build_kmap (nbr_out = its nbr,
- * order = its order, NULL ok).
+ * Strided forward, the downsampling SparseConv3d (spconv USAGE.md,
+ * "spconv.pytorch Core Concepts Definitions": a sparse convolution equals the
+ * dense convolution of the densified tensor and computes only on valid data;
+ * "spconv.pytorch Layer APIs Reference": SparseConv3d downsamples, dense
+ * version nn.Conv3d):
+ *   out[o] = bias + sum_k feats[nbr_out[o*K + k]] @ W[k]   over entries >= 0
+ * for the n_out output rows of a strided spc_build_kmap.
+ * feats [n_in, cin] (the map's input rows), weight [K, cin, cout], bias [cout]
+ * fp32 (NULL ok), nbr_out [n_out, K] = that call's nbr, order (NULL ok) = its
+ * order, out [n_out, cout] (overwritten; n_out may be 0).  Entries outside
+ * [0, n_in) count as absent.  Errors: SPC_ERR_ARG for a NULL or misaligned
+ * pointer or a negative size; SPC_ERR_UNSUPPORTED for channel counts that are
+ * not multiples of 16 or a contraction beyond the kernels' limit (256 16-bit,
+ * 128 fp32 channels).  One kernel on `stream`, asynchronous.
  */
 spc_status spc_sparse_conv_fwd(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
                                const void* weight, int32_t K, int32_t cout, const float* bias,
@@ -245,12 +256,19 @@ spc_status spc_conv_bwd_filter_workspace(int64_t n_in, int64_t n_out, int32_t ci
                                          int32_t K, int32_t want_dbias, size_t* bytes);
 
 /*
- * dfilter: dW[k] = sum over the pairs (i, o) of offset k of feats[i]^T dout[o],
+ * dfilter (Hygon spconv-das README, "Public Interface Support": training
+ * covers forward, dinput and dfilter in FP32, FP16 and BF16), the weight
+ * derivative of the forward sum:
+ *   dW[k] = sum over the pairs (i, o) of offset k of feats[i]^T dout[o],
  * fp32 [K, cin, cout] (overwritten), from the CSR pair lists of
- * spc_build_kmap.  dbias (NULL ok) = column sums of dout, fp32 [cout].
+ * spc_build_kmap (pair_in = input rows i, pair_out = output rows o; for the
+ * inverse layer pass them exchanged).  dbias (NULL ok) = column sums of dout,
+ * fp32 [cout].  feats [n_in, cin] and dout [n_out, cout] share dtype.
  * K == 1 with all pair pointers NULL pairs row i with row i (n_in == n_out).
+ * ws: spc_conv_bwd_filter_workspace bytes, 16-byte aligned, scratch.
  * Reduction: fixed-size pair chunks per offset, each a partial in the
  * workspace, summed in a fixed order, so the result is run-to-run identical.
+ * Errors as spc_sparse_conv_fwd, plus SPC_ERR_WORKSPACE for a short ws.
  */
 spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
                                const void* dout, int64_t n_out, int32_t cout, int32_t K,

@@ -157,10 +157,21 @@ def inverse_conv_bwd_filter(feats, dout, nbr) -> np.ndarray:
 
 
 def max_rel_err(got, ref) -> float:
-    """``max|got - ref| / max|ref|`` (0 when both are empty or ref is all zero)."""
+    """Parity measure of every floating-point comparison: ``max|got - ref| /
+    max|ref|`` over all elements, in float64 (the bound a result must meet is
+    ``max|err| <= tol * max|ref|``).  The shapes must be equal (no
+    broadcasting).  0 for empty arrays; for an all-zero ``ref`` the plain
+    ``max|got - ref|``; ``inf`` when ``got`` holds a NaN where ``ref`` does not
+    (NaN at the same place in both counts as equal)."""
     g, r = f64(got), f64(ref)
+    if g.shape != r.shape:
+        raise ValueError(f"max_rel_err: shapes differ, got {g.shape} vs ref {r.shape}")
     if r.size == 0:
         return 0.0
-    scale = np.abs(r).max()
-    err = np.abs(g - r).max()
+    both_nan = np.isnan(g) & np.isnan(r)
+    diff = np.abs(np.where(both_nan, 0.0, g - r))
+    if np.isnan(diff).any():
+        return float("inf")
+    scale = np.abs(np.where(np.isnan(r), 0.0, r)).max()
+    err = diff.max()
     return float(err / scale) if scale > 0 else float(err)

@@ -253,3 +253,81 @@ def test_fused_equals_dense_conv3d_add_relu():
     ref = torch.relu(sample(dense, c) + torch.as_tensor(r.numpy(), dtype=torch.float64)).numpy()
     got = C.conv_fwd_fused(t["feats"], t["weight"], t["bias"], nbr, r, relu=True)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ the parity measure itself
+#
+# Every floating-point parity assertion goes through max_rel_err: the bound is
+# max|got - ref| <= tol * max|ref|.  These cases are computed by hand, and the
+# planted variants below (a mean for the max, a missing abs, a signed
+# difference, a scale without abs, an elementwise relative error, silent
+# broadcasting) each fail at least one of them.
+
+_MRE_CASES = [
+    # (got, ref, expected)
+    ([1.0, -4.0, 2.0], [1.0, -4.0, 2.0], 0.0),
+    ([1.5, -4.0, 2.0], [1.0, -4.0, 2.0], 0.125),              # 0.5 / 4
+    ([[1.0, -3.5], [2.0, -0.25]], [[1.0, -4.0], [2.0, 0.0]], 0.125),  # max 0.5, not the mean 0.1875
+    ([-8.0, 3.0], [-8.0, 1.0], 0.25),                         # scale is max|ref| = 8, not max(ref) = 1
+    ([0.0, 4.0], [0.0, 5.0], 0.2),                            # |4 - 5| / 5: a signed max would give 0
+    ([0.0, 1e-3], [0.0, 0.0], 1e-3),                          # all-zero ref: the absolute error
+    ([2.0, 2.0, 2.0, 2.0], [1.0, 1.0, 1.0, 100.0], 0.98),     # 98 / 100, not the max elementwise ratio 1
+]
+
+
+def _check_mre(fn):
+    for got, ref, want in _MRE_CASES:
+        v = fn(np.array(got), np.array(ref))
+        if not np.isclose(v, want, rtol=1e-12, atol=0.0):
+            return False
+    if fn(np.zeros((0, 4)), np.zeros((0, 4))) != 0.0:
+        return False
+    try:
+        fn(np.ones((1, 3)), np.ones((5, 3)))
+        return False  # a [1, C] result must not broadcast against [N, C]
+    except ValueError:
+        pass
+    if fn(np.array([1.0, np.nan]), np.array([1.0, 2.0])) != float("inf"):
+        return False
+    return True
+
+
+def test_max_rel_err_hand_cases():
+    assert _check_mre(C.max_rel_err)
+    # both NaN at the same place counts as equal
+    assert C.max_rel_err(np.array([np.nan, 1.0]), np.array([np.nan, 2.0])) == 0.5
+    # 16-bit tensors are compared on their exact values: bf16 1.0078125 vs 1.0, scale 3
+    got = torch.tensor([1.0078125, 3.0], dtype=torch.bfloat16)
+    ref = torch.tensor([1.0, 3.0], dtype=torch.bfloat16)
+    assert C.max_rel_err(got, ref) == 0.0078125 / 3.0
+    # a NaN fails any tolerance
+    assert not (C.max_rel_err(np.array([np.nan]), np.array([1.0])) <= 1e-2)
+
+
+def _planted(kind):
+    def fn(got, ref):
+        g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        if kind != "broadcast" and g.shape != r.shape:
+            raise ValueError("shape")
+        if r.size == 0:
+            return 0.0
+        if kind == "mean":
+            err, scale = np.abs(g - r).mean(), np.abs(r).max()
+        elif kind == "no_abs":
+            err, scale = (g - r).max(), np.abs(r).max()
+        elif kind == "scale_no_abs":
+            err, scale = np.abs(g - r).max(), r.max()
+        elif kind == "elementwise":
+            nz = r != 0
+            return float((np.abs(g - r)[nz] / np.abs(r)[nz]).max()) if nz.any() else float(np.abs(g - r).max())
+        elif kind == "broadcast":
+            err, scale = np.abs(g - r).max(), np.abs(r).max()
+        elif kind == "nan_blind":
+            err, scale = np.nanmax(np.abs(g - r)), np.abs(r).max()
+        return float(err / scale) if scale > 0 else float(err)
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["mean", "no_abs", "scale_no_abs", "elementwise", "broadcast", "nan_blind"])
+def test_max_rel_err_planted_variants_fail(kind):
+    assert not _check_mre(_planted(kind))
