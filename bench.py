@@ -1,59 +1,55 @@
 #!/usr/bin/env python
 """Throughput of the sparse-convolution hot path on one MI355X.
 
-One step runs every stage of the path once on one batch of synthetic input.
-It starts with the LiDAR-like scene: 2 samples x 60k voxels on a 41 x 1600 x
-1408 grid, fp16, 64 channels.  The stages are, in order:
+The headline workload is the mesh-shell sets: 4 samples of 8 one-voxel sphere
+shells on 128^3 (N = 266,426), bf16, 128 channels.  One step runs every stage
+of the path once on that batch:
 
-    kmap_subm       submanifold kernel map k=3 (table build + probe + pair lists + order)
-    fwd_subm        SubMConv3d k=3 forward 64 -> 64
-    fwd_k1          k=1 layer 64 -> 64 on that output
+    kmap_subm       submanifold kernel map k=3 (hash build + probe + pair lists + order)
+    fwd_subm        SubMConv3d k=3 forward 128 -> 128
+    fwd_k1          k=1 layer 128 -> 128 on that output
     dinput_subm     dinput of the k=3 layer
     dfilter_subm    dfilter of the k=3 layer
-    kmap_strided    strided kernel map k=3 s=2 p=1 (output sites, maps, pairs)
-    fwd_strided     SparseConv3d forward 64 -> 128
+    kmap_strided    strided kernel map k=3 s=2 p=1 (output sites, maps, pairs, both orders)
+    fwd_strided     SparseConv3d forward 128 -> 128
     dinput_strided  its dinput
     dfilter_strided its dfilter
 
-Both kernel maps depend on the coordinates only, so the step builds each on
-a stream of its own (default priority), while the main stream finishes the
-previous step: the SubM map first (its layer is next on the main stream), the
-strided map after it, beside the SubM layer; each layer waits for its map.  The maps are marked
-as used by the main stream, so their memory is not reused early.  Running the
-SubM dinput and dfilter side by side as well was slower (each fills the GPU).
+value = effective TFLOP/s of the SubMConv3d k=3 forward: 2 * P * Cin * Cout
+(P = occupied pairs, counted from the kernel map) over the forward's duration,
+the mean of HIP events recorded around it (on its stream) in each of the K
+timed steps.  kmap_voxels_per_s = N over the mean duration of the SubM kernel
+map, timed the same way.  ms_per_step is the wall time of the K timed steps.
+The forward uses weights transposed once at set-up (a layer keeps its weights
+in the layout its kernel reads), so the timed forward is one kernel, which is
+also the roofline's kernel: its algorithmic FLOP over that mean duration
+against the bf16 MFMA peak, and its HBM traffic from the committed rocprofv3
+counter runs (profiles/traffic.json, only while the kernel source is the one
+measured).
 
-``--workload shells`` runs the same stages on the mesh-shell sets: 4 x 128^3,
-bf16, 128 channels, with k=1 128 -> 128.  The strided layer there is 128 -> 128.
+Both kernel maps depend on the coordinates only, so each is built on a stream
+of its own (default priority) while the main stream finishes the previous
+step; each layer waits for its map.  On the shell sets the strided map starts
+after the SubM forward has been issued, so the timed forward runs alone; on
+the LiDAR scene, whose step is bound by host time, it starts right after the
+SubM map.  A second, untimed pass of K
+steps records HIP events around every stage for the per-stage breakdown.
 
-value = effective TFLOP/s of the whole step: 2 * pairs * Cin * Cout summed
-over the convolution stages (pairs counted from the kernel map, k=1 counts N
-pairs), divided by the step time.  The kernel-map rate is reported as voxels/s
-(N over the kmap_subm time).  The K timed steps run bare; a second pass of K
-steps times every stage with HIP events on the stream it runs on (the event
-records cost host time, so that pass is not the timed one) and reports each
-stage's median.  With the two streams overlapping, a stage's time includes
-what it shares the GPU with.  The roofline is given for the single-kernel
-stage with the longest kernel: each such kernel is also launched back to back
-between two HIP events, behind a few ms of queued fills so that no host time
-between launches counts (the step's stage timings include host gaps, e.g. after
-the strided kernel map's one synchronisation), and that average is its launch
-duration.  Its HBM traffic comes from the rocprofv3 counter runs recorded in
-profiles/traffic.json, and only while the kernel source is the one measured.
-
-``--kmap-sweep`` replaces the step by the kernel-map rate on the shell sets at
-4, 8, 16 and 32 samples (one JSON line each), to show the maps as the scene grows
-past the sizes where launch latency dominates.
-
-``extras`` times the layers beyond the step the same way, one launch each on
-this step's maps: fwd_inverse is the upsampling layer back from the strided
-layer (its channels reversed); fwd_subm_add_relu_fused is the k=3 layer as a
-residual block relu(conv(x) + x) in one kernel, and ..._unfused the same
-through the plain forward plus torch's add and relu (three launches, timed
-together); maxpool_fwd / maxpool_bwd pool x over the strided layer's map
-(3^3, stride 2); subm_step_graph replays the SubM half of the step (kernel map,
-forward, k=1, dinput, dfilter) as one captured HIP graph, subm_step_eager makes
-the same calls one by one; point_to_voxel voxelises a 200k-point synthetic sweep
-(one call, its host synchronisation included).  They are not part of ``value``.
+Sections of the same JSON line (``--sections`` picks them):
+    lidar_step      the same step on the LiDAR scene (2 x 60k voxels on 41 x
+                    1600 x 1408, fp16, 64 -> 64; strided 64 -> 128), timed the
+                    same way, with its own roofline (the strided forward, HBM)
+    train96         the training step of SubMConv3d k=3, bf16, 96 -> 96 on the
+                    shell sets: forward + dinput + dfilter, 3 * 2 * P * 96^2
+                    FLOP per step; forward and forward-plus-backward separately
+    uniform32_f32   SubMConv3d k=3 fp32 16 -> 16 on 2,000 sites of 32^3: kernel
+                    map + forward + backward (latency-bound)
+    kmap_tables     each kernel map with the hash and with the index grid
+    extras          the layers beyond the path, on the LiDAR step's maps
+``--kmap-sweep`` prints kernel-map rates as the scene grows instead.
+``cpu_baseline`` times the oracle on the headline metric: the SubM kernel map
+and forward on a bounded sample of the same workload, at 1 thread, at most 24
+threads and on every core this process may use.
 """
 
 from __future__ import annotations
@@ -74,8 +70,8 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "dinput_strided")
 KERNEL_REPS = 20         # back-to-back launches per single-kernel stage for its duration
 BUSY_FILLS = 3           # 1 GiB fills queued ahead of them (~0.5 ms of GPU time)
-CPU_MIN_S = 10.0         # the oracle repeats whole steps for at least this long (within --cpu-budget)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SECTIONS = ("lidar_step", "train96", "uniform32_f32", "kmap_tables", "extras")
 
 
 def parse():
@@ -83,14 +79,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=("lidar", "shells"), default="lidar")
+    ap.add_argument("--workload", choices=("shells", "lidar"), default="shells",
+                    help="headline workload (shells: the 128^3 mesh-shell sets, bf16, 128 channels)")
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help=f"comma-separated sections to add (of {', '.join(SECTIONS)}; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work to time at most")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
-    ap.add_argument("--no-extras", action="store_true", help="skip timing the layers beyond the step")
     ap.add_argument("--kmap-sweep", action="store_true",
-                    help="instead of the step: kernel-map rate on the shell sets at 4..32 samples (one line each)")
+                    help="instead of the step: kernel-map rates as the scene grows (one line per size)")
     return ap.parse_args()
 
 
@@ -117,10 +115,27 @@ def make_inputs(kind: str):
                 feats=w.feats, w3=w.weight, w1=w.extra["weight_k1"], grad=grad, ws=wstr, grad_rng=W.rng(6, "bias"))
 
 
+def dtype_name(dt) -> str:
+    import torch
+    return {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[dt]
+
+
+def event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def mean(v):
+    return sum(v) / len(v)
+
+
 # ---------------------------------------------------------------- GPU step
 
 class Step:
     """Holds device inputs and runs the stages of one step through the library."""
+
+    names = ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm",
+             "kmap_strided", "fwd_strided", "dinput_strided", "dfilter_strided")
 
     def __init__(self, inp, dev):
         import torch
@@ -134,18 +149,35 @@ class Step:
         self.ws = t(inp["ws"])
         self.n = self.coords.shape[0]
         self.dev = dev
-        # strided output size and its upstream gradient, drawn once
+        # weights in the layout the forward kernels read, made once (a layer
+        # keeps them so); dinput reads W as it is
+        self.pre = spc.binding._pretranspose(self.x.dtype, self.w3.shape[1], None)
+        self.w3t = spc.transpose_weight(self.w3) if self.pre else None
+        self.w1t = spc.transpose_weight(self.w1) if self.pre else None
+        self.wst = spc.transpose_weight(self.ws) if self.pre else None
+        # counts for the FLOP and byte figures, and the strided layer's upstream gradient
         km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, orders=True)
         self.m = km["n_out"]
         self.gs = t(W.grad_for(inp["grad_rng"], self.m, self.ws.shape[2], inp["dtype"]))
         ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3)
         self.P = int(ks["pair_ptr"][-1].item())
         self.Ps = int(km["pair_ptr"][-1].item())
-        self.names = ("kmap_subm", "fwd_subm", "fwd_k1", "dinput_subm", "dfilter_subm",
-                      "kmap_strided", "fwd_strided", "dinput_strided", "dfilter_strided")
-        self.ev = None
         self.side = None             # the kernel maps' streams (created on first use)
+        # the strided map after the SubM forward (the forward then runs alone),
+        # or right after the SubM map, beside the SubM layer (the host-bound
+        # LiDAR step gets its count earlier)
+        self.strided_after_fwd = inp["name"].startswith("shells")
         self.km, self.ks = None, km  # maps held for kernel_ms (the SubM one is built on first use)
+
+    def fwd(self, x, w, wt, map_, n_rows, subm, order):
+        spc = self.spc
+        if wt is None:
+            if map_ is None:
+                return spc.subm_conv_fwd(x, w, None, None)
+            if subm:
+                return spc.subm_conv_fwd(x, w, None, map_, order)
+            return spc.sparse_conv_fwd(x, w, None, map_, n_rows, order)
+        return spc.conv_fwd_wt(x, wt, None, map_, n_rows, subm, order)
 
     def kernel_ms(self, stage: str, reps: int = KERNEL_REPS) -> float:
         """Average duration of one single-kernel stage launched `reps` times back to
@@ -155,43 +187,35 @@ class Step:
             self.km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         km, ks = self.km, self.ks
         y = self.x if self.w1.shape[1] == self.x.shape[1] else None
-        make = {  # stage -> a function that makes its launch
-            "fwd_subm": lambda: self.conv_only(self.x, self.w3, km["nbr"], self.n, True, km["order"]),
-            "fwd_k1": lambda: self.conv_only(y, self.w1, None, self.n, False, None),
-            "dinput_subm": lambda: lambda: spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n, km["order"]),
-            "fwd_strided": lambda: self.conv_only(self.x, self.ws, ks["nbr"], ks["n_out"], False, ks["order"]),
-            "dinput_strided": lambda: lambda: spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n,
-                                                                 ks["order_in"]),
+        make = {  # stage -> its launch
+            "fwd_subm": lambda: self.fwd(self.x, self.w3, self.w3t, km["nbr"], self.n, True, km["order"]),
+            "fwd_k1": lambda: self.fwd(y, self.w1, self.w1t, None, self.n, False, None),
+            "dinput_subm": lambda: spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n, km["order"]),
+            "fwd_strided": lambda: self.fwd(self.x, self.ws, self.wst, ks["nbr"], ks["n_out"], False, ks["order"]),
+            "dinput_strided": lambda: spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n,
+                                                         ks["order_in"]),
         }[stage]
-        return self.time_launch(make(), reps)
+        return time_launch(self, make, reps)
 
-    def conv_only(self, x, w, map_, n_rows, subm, order):
-        """A forward stage's convolution kernel alone.  Where the library hands
-        the kernel pre-transposed weights (a second, small kernel per call, which
-        the step itself runs every time), they are transposed once here, so
-        that the timed launches are the convolution's."""
-        spc = self.spc
-        if not spc.binding._pretranspose(x.dtype, w.shape[1], None):
-            if map_ is None:
-                return lambda: spc.subm_conv_fwd(x, w, None, None)
-            if subm:
-                return lambda: spc.subm_conv_fwd(x, w, None, map_, order)
-            return lambda: spc.sparse_conv_fwd(x, w, None, map_, n_rows, order)
-        wt = spc.transpose_weight(w)
-        return lambda: spc.conv_fwd_wt(x, wt, None, map_, n_rows, subm, order)
-
-    def run(self, events=None):
+    def run(self, events=None, timed=None):
         """One step.  Each kernel map depends on the coordinates only, so each
         is built on a stream of its own (default priority) while the main
         stream finishes the previous step; the main stream waits for a map
-        (a persistent event) before its layer.  Each stage's events are
-        recorded on the stream it runs on."""
+        (a persistent event) before its layer, and the strided map starts
+        after the SubM forward is issued, or after the SubM map
+        (strided_after_fwd).  `events` (stage -> pair) records
+        every stage; `timed` (stage -> list) gets event pairs around the
+        SubM map and forward only."""
         spc, inp, torch = self.spc, self.inp, self.torch
-        E = events or {}
+        E = dict(events or {})
+        if timed is not None:
+            for k in ("kmap_subm", "fwd_subm"):
+                E[k] = event_pair()
+                timed[k].append(E[k])
         if self.side is None:  # the streams and the events that join them, made once
             self.side = (torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream(),
-                         torch.cuda.Event(), torch.cuda.Event())
-        main, side_s, side_k, done_s, done_k = self.side
+                         torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event())
+        main, side_s, side_k, done_s, done_k, fwd_issued = self.side
 
         def mark(name, i):
             if name in E:
@@ -203,27 +227,35 @@ class Step:
                 if isinstance(t, torch.Tensor):
                     t.record_stream(main)
 
+        def strided_map(after):
+            torch.cuda.set_stream(side_k)
+            side_k.wait_event(after)
+            mark("kmap_strided", 0)
+            ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, orders=True)
+            mark("kmap_strided", 1)
+            done_k.record(side_k)
+            torch.cuda.set_stream(main)
+            used_on_main(ks)
+            return ks
+
         torch.cuda.set_stream(side_s)
         mark("kmap_subm", 0)
         km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
         mark("kmap_subm", 1)
         done_s.record(side_s)
-        torch.cuda.set_stream(side_k)
-        side_k.wait_event(done_s)   # the SubM map first: its layer is the next on the main stream
-        mark("kmap_strided", 0)
-        ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, out_cap=self.m,
-                            orders=True)
-        mark("kmap_strided", 1)
-        done_k.record(side_k)
+        if not self.strided_after_fwd:
+            ks = strided_map(done_s)
         torch.cuda.set_stream(main)
         used_on_main(km)
-        used_on_main(ks)
         main.wait_event(done_s)
         mark("fwd_subm", 0)
-        y = spc.subm_conv_fwd(self.x, self.w3, None, km["nbr"], km["order"])
+        y = self.fwd(self.x, self.w3, self.w3t, km["nbr"], self.n, True, km["order"])
         mark("fwd_subm", 1)
+        if self.strided_after_fwd:
+            fwd_issued.record(main)
+            ks = strided_map(fwd_issued)
         mark("fwd_k1", 0)
-        spc.subm_conv_fwd(y, self.w1, None, None)
+        self.fwd(y, self.w1, self.w1t, None, self.n, False, None)
         mark("fwd_k1", 1)
         mark("dinput_subm", 0)
         spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n, km["order"])
@@ -233,7 +265,7 @@ class Step:
         mark("dfilter_subm", 1)
         main.wait_event(done_k)
         mark("fwd_strided", 0)
-        spc.sparse_conv_fwd(self.x, self.ws, None, ks["nbr"], ks["n_out"], ks["order"])
+        self.fwd(self.x, self.ws, self.wst, ks["nbr"], ks["n_out"], False, ks["order"])
         mark("fwd_strided", 1)
         mark("dinput_strided", 0)
         spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n, ks["order_in"])
@@ -241,6 +273,32 @@ class Step:
         mark("dfilter_strided", 0)
         spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"])
         mark("dfilter_strided", 1)
+
+    # effective FLOP and algorithmic HBM bytes per stage (one launch / call)
+    def work(self):
+        n, m, P, Ps = self.n, self.m, self.P, self.Ps
+        cin, c1 = self.w3.shape[1], self.w3.shape[2]
+        cs = self.ws.shape[2]
+        s = self.x.element_size()
+        K = 27
+        f = {
+            "fwd_subm": 2 * P * cin * c1, "fwd_k1": 2 * n * c1 * self.w1.shape[2],
+            "dinput_subm": 2 * P * cin * c1, "dfilter_subm": 2 * P * cin * c1,
+            "fwd_strided": 2 * Ps * cin * cs, "dinput_strided": 2 * Ps * cin * cs,
+            "dfilter_strided": 2 * Ps * cin * cs,
+        }
+        b = {
+            "kmap_subm": n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n,
+            "fwd_subm": n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s,
+            "fwd_k1": n * c1 * s + c1 * self.w1.shape[2] * s + n * self.w1.shape[2] * s,
+            "dinput_subm": n * c1 * s + K * n * 4 + K * cin * c1 * s + n * cin * s,
+            "dfilter_subm": n * cin * s + n * c1 * s + 8 * P + 4 * (K + 1) + K * cin * c1 * 4,
+            "kmap_strided": n * 16 + m * 16 + 4 * K * (m + n) + 8 * Ps + 4 * (K + 1) + 4 * (m + n),
+            "fwd_strided": n * cin * s + K * m * 4 + K * cin * cs * s + m * cs * s,
+            "dinput_strided": m * cs * s + K * n * 4 + K * cin * cs * s + n * cin * s,
+            "dfilter_strided": n * cin * s + m * cs * s + 8 * Ps + 4 * (K + 1) + K * cin * cs * 4,
+        }
+        return f, b
 
     def extras(self):
         """The widened layers, each one launch timed like a single-kernel stage:
@@ -305,143 +363,40 @@ class Step:
                             0, m * K * 4 + n * cin * s + m * cin * s + m * cin),
             "maxpool_bwd": (lambda: spc.sparse_maxpool_bwd(self.pool_g, self.pool_a, ks["nbr_in"], n),
                             0, n * K * 4 + m * cin * s + m * cin + n * cin * s),
-            # a 200k-point synthetic sweep into 0.1 x 0.1 x 0.2 m voxels (one call,
-            # including its one host synchronisation); bytes: the points read, the
-            # voxel block, coordinates, counts and point ids written
             # the SubM half of the step replayed as one captured HIP graph, and the
             # same calls made one by one
             "subm_step_graph": (self.graph.replay, st_f, st_b),
             "subm_step_eager": (subm_step, st_f, st_b),
+            # a 200k-point synthetic sweep into 0.1 x 0.1 x 0.2 m voxels (one call,
+            # including its one host synchronisation); bytes: the points read, the
+            # voxel block, coordinates, counts and point ids written
             "point_to_voxel": (lambda: spc.point_to_voxel(self.pts, vc["vsize_xyz"], vc["range_xyz"],
                                                           vc["max_voxels"], vc["max_points"], True, with_id=True),
                                0, self.pts.numel() * 4 + vc["max_voxels"] * (vc["max_points"] * self.pts.shape[1] * 4
                                                                             + 16) + self.pts.shape[0] * 4),
         }
 
-    def time_launch(self, launch, reps: int = KERNEL_REPS) -> float:
-        """Average duration of one launch repeated back to back between two events.
-        Some GPU work is queued first (fills, then one untimed launch that brings
-        the caches back), so the host has enqueued every timed launch before the
-        first one starts and the host's per-call cost is not timed."""
-        torch = self.torch
+
+def time_launch(holder, launch, reps: int = KERNEL_REPS) -> float:
+    """Average duration of one launch repeated back to back between two events.
+    Some GPU work is queued first (fills, then one untimed launch that brings
+    the caches back), so the host has enqueued every timed launch before the
+    first one starts and the host's per-call cost is not timed."""
+    import torch
+    launch()
+    torch.cuda.synchronize()
+    if not hasattr(holder, "busy"):
+        holder.busy = torch.empty(1 << 30, dtype=torch.uint8, device=holder.dev)
+    for _ in range(BUSY_FILLS):
+        holder.busy.fill_(1)
+    launch()
+    a, b = event_pair()
+    a.record()
+    for _ in range(reps):
         launch()
-        torch.cuda.synchronize()
-        if not hasattr(self, "busy"):
-            self.busy = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
-        for _ in range(BUSY_FILLS):
-            self.busy.fill_(1)
-        launch()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            launch()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    # effective FLOP and algorithmic HBM bytes per stage (one launch / call)
-    def work(self):
-        n, m, P, Ps = self.n, self.m, self.P, self.Ps
-        cin, c1 = self.w3.shape[1], self.w3.shape[2]
-        cs = self.ws.shape[2]
-        s = self.x.element_size()
-        K = 27
-        f = {
-            "fwd_subm": 2 * P * cin * c1, "fwd_k1": 2 * n * c1 * self.w1.shape[2],
-            "dinput_subm": 2 * P * cin * c1, "dfilter_subm": 2 * P * cin * c1,
-            "fwd_strided": 2 * Ps * cin * cs, "dinput_strided": 2 * Ps * cin * cs,
-            "dfilter_strided": 2 * Ps * cin * cs,
-        }
-        b = {
-            "kmap_subm": n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n,
-            "fwd_subm": n * cin * s + K * n * 4 + K * cin * c1 * s + n * c1 * s,
-            "fwd_k1": n * c1 * s + c1 * self.w1.shape[2] * s + n * self.w1.shape[2] * s,
-            "dinput_subm": n * c1 * s + K * n * 4 + K * cin * c1 * s + n * cin * s,
-            "dfilter_subm": n * cin * s + n * c1 * s + 8 * P + 4 * (K + 1) + K * cin * c1 * 4,
-            "kmap_strided": n * 16 + m * 16 + 4 * K * (m + n) + 8 * Ps + 4 * (K + 1) + 4 * (m + n),
-            "fwd_strided": n * cin * s + K * m * 4 + K * cin * cs * s + m * cs * s,
-            "dinput_strided": m * cs * s + K * n * 4 + K * cin * cs * s + n * cin * s,
-            "dfilter_strided": n * cin * s + m * cs * s + 8 * Ps + 4 * (K + 1) + K * cin * cs * 4,
-        }
-        return f, b
-
-
-# ---------------------------------------------------------------- CPU oracle
-
-def cpu_baseline(inp, step_flops_fn, budget):
-    """Times the oracle on the same step, stage by stage, until the budget is spent."""
-    import numpy as np
-    import threadpoolctl
-    from oracle import conv as OC
-    from oracle import kmap as OK
-    import workloads as W
-
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    c, sh, b = inp["coords"], inp["shape"], inp["batch"]
-    done, spent, flops = [], 0.0, 0.0
-    state = {}
-
-    def st_kmap_subm():
-        state["nbr"] = OK.subm_kmap(c, sh, 3)
-        state["P"] = int((state["nbr"] >= 0).sum())
-
-    def st_fwd():
-        state["y"] = OC.conv_fwd(inp["feats"], inp["w3"], None, state["nbr"])
-
-    def st_k1():
-        OC.conv_fwd(state["y"], inp["w1"], None, np.arange(c.shape[0])[None])
-
-    def st_din():
-        OC.conv_bwd_input(inp["grad"], inp["w3"], state["nbr"], c.shape[0])
-
-    def st_dw():
-        OC.conv_bwd_filter(inp["feats"], inp["grad"], state["nbr"])
-
-    def st_kmap_str():
-        state["s"] = OK.strided_kmap(c, b, sh, 3, 2, 1, 1)
-        state["Ps"] = int((state["s"]["nbr_out"] >= 0).sum())
-        state["gs"] = W.grad_for(inp["grad_rng"], state["s"]["out_coords"].shape[0], inp["ws"].shape[2],
-                                 inp["dtype"])
-
-    def st_fwd_s():
-        OC.conv_fwd(inp["feats"], inp["ws"], None, state["s"]["nbr_out"])
-
-    def st_din_s():
-        OC.conv_bwd_input(state["gs"], inp["ws"], state["s"]["nbr_out"], c.shape[0])
-
-    def st_dw_s():
-        OC.conv_bwd_filter(inp["feats"], state["gs"], state["s"]["nbr_out"])
-
-    stages = [("kmap_subm", st_kmap_subm), ("fwd_subm", st_fwd), ("fwd_k1", st_k1), ("dinput_subm", st_din),
-              ("dfilter_subm", st_dw), ("kmap_strided", st_kmap_str), ("fwd_strided", st_fwd_s),
-              ("dinput_strided", st_din_s), ("dfilter_strided", st_dw_s)]
-    times = {}
-    steps = 0
-    # whole steps, repeated until CPU_MIN_S have passed; a step that would not
-    # fit the budget is cut after the stage that crosses it
-    while spent < min(CPU_MIN_S, budget):
-        for name, fn in stages:
-            if spent > budget:
-                break
-            t0 = time.perf_counter()
-            fn()
-            dt = time.perf_counter() - t0
-            times[name] = times.get(name, 0.0) + dt
-            spent += dt
-            if steps == 0:
-                done.append(name)
-            flops += step_flops_fn(name, state)
-        else:
-            steps += 1
-            continue
-        break
-    per = max(steps, 1)
-    return {"value": flops / spent / 1e12 if spent > 0 else None, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": (f"{steps} whole step(s)" if steps else f"first {len(done)} of {len(stages)} stages")
-                      + f" ({', '.join(done)}), {spent:.1f} s, numpy fp64 on {threads} BLAS threads",
-            "stage_s": {k: round(v / per, 3) for k, v in times.items()},
-            "kmap_voxels_per_s": c.shape[0] * per / times["kmap_subm"] if "kmap_subm" in times else None}
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 # ---------------------------------------------------------------- HBM traffic
@@ -461,48 +416,322 @@ def measured_traffic(workload: str, stage: str):
         return None
 
 
+def roofline(kernel: str, stage: str, flop: float, nbytes: float, ms: float, dtype: str, workload: str) -> dict:
+    """Roofline entry of one kernel: bound by MFMA when its arithmetic intensity
+    is above the ridge, else by HBM; achieved = algorithmic FLOP (or bytes) per
+    launch over the average launch duration `ms`."""
+    t = ms * 1e-3
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flop / nbytes < ridge:
+        r = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": round(flop / t / 1e12, 2), "peak": MFMA_PEAK_TFLOPS[dtype],
+             "unit": "TFLOP/s"}
+    r["frac"] = round(r["achieved"] / r["peak"], 4)
+    r["traffic"] = measured_traffic(workload, stage)
+    r["kernel"] = f"{kernel} ({stage})"
+    r["algorithmic_bytes_per_launch"] = int(nbytes)
+    r["flop_per_launch"] = int(flop)
+    r["avg_launch_ms"] = round(ms, 4)
+    return r
+
+
+# ---------------------------------------------------------------- step runs
+
+def run_step(inp, dev, steps, warmup, kernel_stages=True):
+    """Warmup, the K timed steps (events around the SubM map and forward only),
+    then an instrumented pass of K steps for the per-stage medians."""
+    import torch
+    step = Step(inp, dev)
+    flops, bytes_ = step.work()
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    timed = {"kmap_subm": [], "fwd_subm": []}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run(timed=timed)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = {k: [a.elapsed_time(b) for a, b in v] for k, v in timed.items()}
+
+    events = {k: [event_pair() for _ in range(steps)] for k in step.names}
+    for i in range(steps):
+        step.run({k: events[k][i] for k in step.names})
+    torch.cuda.synchronize()
+    stage_ms = {k: sorted(a.elapsed_time(b) for a, b in events[k])[steps // 2] for k in step.names}
+    stages = {}
+    for k in step.names:
+        t = stage_ms[k] * 1e-3
+        stages[k] = {"ms": round(stage_ms[k], 4),
+                     "TFLOP/s": round(flops[k] / t / 1e12, 2) if k in flops and t > 0 else None,
+                     "alg_GB/s": round(bytes_[k] / t / 1e9, 1) if t > 0 else None}
+    kernel_ms = {k: step.kernel_ms(k) for k in SINGLE_KERNEL_STAGES} if kernel_stages else {}
+    return step, dict(wall=wall, dur=dur, stages=stages, kernel_ms=kernel_ms, flops=flops, bytes=bytes_)
+
+
+def step_summary(inp, step, r, steps, dtype):
+    fwd_ms = mean(r["dur"]["fwd_subm"])
+    kmap_ms = mean(r["dur"]["kmap_subm"])
+    return {
+        "workload": inp["name"], "ms_per_step": round(r["wall"] * 1e3 / steps, 4),
+        "subm_fwd_TFLOP/s": round(r["flops"]["fwd_subm"] / (fwd_ms * 1e-3) / 1e12, 2),
+        "subm_fwd_ms": round(fwd_ms, 4),
+        "kmap_voxels_per_s": round(step.n / (kmap_ms * 1e-3), 1), "kmap_subm_ms": round(kmap_ms, 4),
+        "n_voxels": step.n, "pairs_subm_k3": step.P, "n_out_strided": step.m, "pairs_strided": step.Ps,
+        "channels": [int(step.w3.shape[1]), int(step.w3.shape[2]), int(step.ws.shape[2])], "dtype": dtype,
+        "stages": r["stages"], "kernel_ms": {k: round(v, 4) for k, v in r["kernel_ms"].items()},
+    }
+
+
+# ---------------------------------------------------------------- sections
+
+def section_lidar(dev, steps, warmup):
+    """The LiDAR scene's step (configs 2 and 4), with the roofline of its
+    longest single kernel."""
+    inp = make_inputs("lidar")
+    step, r = run_step(inp, dev, steps, warmup)
+    out = step_summary(inp, step, r, steps, dtype_name(inp["dtype"]))
+    dom = max(SINGLE_KERNEL_STAGES, key=lambda k: r["kernel_ms"][k])
+    out["roofline"] = roofline("k_conv", dom, r["flops"][dom], r["bytes"][dom], r["kernel_ms"][dom],
+                               dtype_name(inp["dtype"]), "lidar")
+    return step, out
+
+
+def section_train96(dev, steps, warmup):
+    """SubMConv3d k=3, bf16, 96 -> 96 on the shell sets: forward + dinput +
+    dfilter per step (the kernel map built once: the sites do not change
+    during training), with forward and forward-plus-backward timed apart."""
+    import torch
+    import sparse_convolution_hash_amd as spc
+    import workloads as W
+    w = W.workload("train_subm_k3_bf16_shells96")
+    c = torch.from_numpy(w.coords).to(dev)
+    x, wt, g = (t.to(dev) for t in (w.feats, w.weight, w.grad))
+    km = spc.build_kmap(c, w.batch, w.shape, 3, orders=True)
+    P = int(km["pair_ptr"][-1].item())
+    K = 27
+
+    def one(ev=None):
+        if ev:
+            ev[0].record()
+        spc.subm_conv_fwd(x, wt, None, km["nbr"], km["order"])   # the weights change every step: no cached transpose
+        if ev:
+            ev[1].record()
+        spc.conv_bwd_input(g, wt, km["nbr"], True, w.n, km["order"])
+        spc.conv_bwd_filter(x, g, K, km["pair_ptr"], km["pair_in"], km["pair_out"])
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        one(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = mean([a.elapsed_time(b) for a, b, _ in evs])
+    full = mean([a.elapsed_time(cc) for a, _, cc in evs])
+    flop1 = 2 * P * 96 * 96
+    return {"workload": "train_shells_4x128^3_bf16_c96", "n_voxels": w.n, "pairs": P, "dtype": "bf16",
+            "ms_per_step": round(wall * 1e3 / steps, 4), "fwd_ms": round(fwd, 4), "fwd_bwd_ms": round(full, 4),
+            "TFLOP/s": round(3 * flop1 / (full * 1e-3) / 1e12, 2),
+            "fwd_TFLOP/s": round(flop1 / (fwd * 1e-3) / 1e12, 2),
+            "mfma_frac": round(3 * flop1 / (full * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+
+
+def section_uniform32(dev, steps, warmup):
+    """SubMConv3d k=3 fp32 16 -> 16 on 2,000 sites of 32^3 with bias: kernel map,
+    forward, dinput and dfilter per step (latency-bound at this size)."""
+    import torch
+    import sparse_convolution_hash_amd as spc
+    import workloads as W
+    w = W.workload("subm_k3_f32_uniform32", with_grad=True)
+    c = torch.from_numpy(w.coords).to(dev)
+    x, wt, b, g = (t.to(dev) for t in (w.feats, w.weight, w.bias, w.grad))
+
+    def one(ev=None):
+        if ev:
+            ev[0].record()
+        km = spc.build_kmap(c, w.batch, w.shape, 3, orders=True)
+        spc.subm_conv_fwd(x, wt, b, km["nbr"], km["order"])
+        if ev:
+            ev[1].record()
+        spc.conv_bwd_input(g, wt, km["nbr"], True, w.n, km["order"])
+        spc.conv_bwd_filter(x, g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"], want_dbias=True)
+        if ev:
+            ev[2].record()
+        return km
+
+    P = int(one()["pair_ptr"][-1].item())
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        one(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = mean([a.elapsed_time(bb) for a, bb, _ in evs])
+    full = mean([a.elapsed_time(cc) for a, _, cc in evs])
+    return {"workload": "uniform_2000_of_32^3_f32_c16", "n_voxels": w.n, "pairs": P, "dtype": "f32",
+            "ms_per_step": round(wall * 1e3 / steps, 4), "kmap_fwd_ms": round(fwd, 4),
+            "kmap_fwd_bwd_ms": round(full, 4),
+            "fwd_TFLOP/s_incl_kmap": round(2 * P * 16 * 16 / (fwd * 1e-3) / 1e12, 4)}
+
+
+def kmap_time(call, reps):
+    """Mean duration of a kernel-map call between HIP events (host time before
+    the first launch counts, as a caller sees it)."""
+    import torch
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = event_pair()
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return mean(ms)
+
+
+def kmap_bytes(kind, n, m, P, K=27):
+    """Algorithmic bytes of a kernel map: coordinates in, maps, pair lists and orders out."""
+    if kind == "subm":
+        return n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n
+    return 16 * n + 16 * m + 4 * K * (m + n) + 8 * P + 4 * (K + 1) + 4 * (m + n)
+
+
+def section_kmap_tables(dev, reps=20):
+    """The SubM maps of the LiDAR scene and the shell sets and the LiDAR strided
+    map, each with the hash table and with the index grid (pairs and orders)."""
+    import torch
+    import sparse_convolution_hash_amd as spc
+    import workloads as W
+    out = {}
+    for wname, kinds in (("subm_k3_f16_lidar120k", ("subm", "strided")), ("subm_k3_k1_bf16_shells128", ("subm",))):
+        w = W.workload(wname)
+        c = torch.from_numpy(w.coords).to(dev)
+        for kind in kinds:
+            for table in ("hash", "grid"):
+                if kind == "subm":
+                    call = lambda t=table: spc.build_kmap(c, w.batch, w.shape, 3, orders=True, table=t)
+                else:
+                    call = lambda t=table: spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True,
+                                                          table=t)
+                r = call()
+                P, m = int(r["pair_ptr"][-1].item()), r["n_out"]
+                ms = kmap_time(call, reps)
+                by = kmap_bytes(kind, w.n, m, P)
+                out[f"{wname.split('_')[-1]}_{kind}_{table}"] = {
+                    "ms": round(ms, 4), "voxels_per_s": round(w.n / (ms * 1e-3), 1),
+                    "alg_GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "n_out": m, "pairs": P}
+    return out
+
+
+def section_extras(step, dtype):
+    extras = {}
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    for name, (launch, fl, by) in step.extras().items():
+        ms = time_launch(step, launch)
+        t = ms * 1e-3
+        bound = "hbm" if fl / by < ridge else "mfma"
+        ach = by / t / 1e9 if bound == "hbm" else fl / t / 1e12
+        peak = HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dtype]
+        extras[name] = {"kernel_ms": round(ms, 4), "TFLOP/s": round(fl / t / 1e12, 2) if fl else None,
+                        "alg_GB/s": round(by / t / 1e9, 1), "bound": bound, "frac": round(ach / peak, 4)}
+    return extras
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(inp, budget):
+    """The oracle on the headline metric: the SubM kernel map of the whole
+    workload, then the forward sum over a bounded sample of its output rows
+    (FLOP counted from that sample's pairs), at 1 thread, at min(24, cores)
+    threads and on every core this process may use."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import conv as OC
+    from oracle import kmap as OK
+
+    cores = len(os.sched_getaffinity(0))
+    c, sh = inp["coords"], inp["shape"]
+    t0 = time.perf_counter()
+    nbr = OK.subm_kmap(c, sh, 3)
+    t_kmap = time.perf_counter() - t0
+    cin, cout = inp["w3"].shape[1], inp["w3"].shape[2]
+    feats, w3 = inp["feats"], inp["w3"]
+    n = c.shape[0]
+    points = sorted({1, min(24, cores), cores})
+    per_point = max(1.0, (budget - t_kmap) / len(points))
+    res, sample_rows = {}, None
+    for th in points:
+        with threadpoolctl.threadpool_limits(th):
+            rows = 4096 if sample_rows is None else sample_rows
+            while True:   # grow the row sample until one forward takes a fair share of the budget
+                sub = nbr[:, :rows]
+                t0 = time.perf_counter()
+                OC.conv_fwd(feats, w3, None, sub)
+                dt = time.perf_counter() - t0
+                if dt > per_point / 3 or rows >= n or sample_rows is not None:
+                    break
+                rows = min(n, rows * 4)
+            sample_rows = rows
+            pairs = int((sub >= 0).sum())
+            res[th] = {"TFLOP/s": 2 * pairs * cin * cout / dt / 1e12, "s": dt}
+    top = res[cores]
+    return {"value": round(top["TFLOP/s"], 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"SubM k=3 forward (numpy fp64) over the first {sample_rows} of {n} output rows "
+                      f"({top['s']:.1f} s on {cores} threads), after the oracle's SubM kernel map of all {n} rows",
+            "threads": {str(k): round(v["TFLOP/s"], 6) for k, v in res.items()},
+            "kmap_voxels_per_s": round(n / t_kmap, 1), "kmap_s": round(t_kmap, 3)}
+
+
 # ---------------------------------------------------------------- main
 
-def kmap_sweep(batches=(4, 8, 16, 32), reps=10):
-    """Kernel-map rate as the scene grows: the 128^3 shell sets (3 k=3 SubM map
-    with pairs and order; the k3 s2 p1 strided map with pairs and both orders),
-    one JSON line per batch size; medians of `reps` calls timed with HIP events."""
+def kmap_sweep(reps=10):
+    """Kernel-map rate as the scene grows: the 128^3 shell sets at 4..32
+    samples and the LiDAR scene at 2..32 samples (k=3 SubM map with pairs and
+    order; k3 s2 p1 strided map with pairs and both orders; each with the hash
+    and the index grid where the grid fits), one JSON line per size."""
     import torch
     import sparse_convolution_hash_amd as spc
     import workloads as W
 
-    K = 27
-    for B in batches:
-        c = torch.from_numpy(W.mesh_shells(W.rng(3), batch=B)).cuda()
+    cases = [("shells", B, lambda B=B: W.mesh_shells(W.rng(3), batch=B), (128, 128, 128)) for B in (4, 8, 16, 32)]
+    cases += [("lidar", B, lambda B=B: W.lidar_scene(W.rng(20 + B), batch=B), (41, 1600, 1408)) for B in (2, 8, 32)]
+    for scene, B, gen, shape in cases:
+        c = torch.from_numpy(gen()).cuda()
         n = c.shape[0]
-        shape = (128, 128, 128)
-        m0 = spc.build_kmap(c, B, shape, 3, 2, 1, 1, subm=False, pairs=False)["n_out"]
-        calls = {  # (the strided call gets the exact capacity, as in the step)
-            "subm": lambda: spc.build_kmap(c, B, shape, 3, orders=True),
-            "strided": lambda: spc.build_kmap(c, B, shape, 3, 2, 1, 1, subm=False, out_cap=m0, orders=True),
-        }
-        line = {"kmap_sweep": {"samples": B, "n_voxels": n}}
-        for name, call in calls.items():
-            r = call()
-            torch.cuda.synchronize()
-            P = int(r["pair_ptr"][-1].item())
-            m = r["n_out"]
-            ms = []
-            for _ in range(reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                call()
-                b.record()
+        cells = B * shape[0] * shape[1] * shape[2]
+        line = {"kmap_sweep": {"scene": scene, "samples": B, "n_voxels": n}}
+        for table in ("hash", "grid"):
+            if table == "grid" and cells * 4.125 > 16e9:
+                continue
+            calls = {
+                "subm": lambda t=table: spc.build_kmap(c, B, shape, 3, orders=True, table=t),
+                "strided": lambda t=table: spc.build_kmap(c, B, shape, 3, 2, 1, 1, subm=False, orders=True, table=t),
+            }
+            for name, call in calls.items():
+                r = call()
                 torch.cuda.synchronize()
-                ms.append(a.elapsed_time(b))
-            t = sorted(ms)[reps // 2] * 1e-3
-            # algorithmic bytes: coordinates in, maps and pair lists out, orders out
-            by = (n * (16 + 4 * K) + 8 * P + 4 * (K + 1) + 4 * n if name == "subm" else
-                  16 * n + 16 * m + 4 * K * (m + n) + 8 * P + 4 * (K + 1) + 4 * (m + n))
-            line["kmap_sweep"][name] = {"ms": round(t * 1e3, 4), "voxels_per_s": round(n / t, 1),
-                                        "n_out": m, "pairs": P, "alg_GB/s": round(by / t / 1e9, 1),
-                                        "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+                P, m = int(r["pair_ptr"][-1].item()), r["n_out"]
+                t = kmap_time(call, reps) * 1e-3
+                by = kmap_bytes(name, n, m, P)
+                line["kmap_sweep"][f"{name}_{table}"] = {
+                    "ms": round(t * 1e3, 4), "voxels_per_s": round(n / t, 1), "n_out": m, "pairs": P,
+                    "alg_GB/s": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+                del r
         print(json.dumps(line), flush=True)
+        del c
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -516,36 +745,16 @@ def main():
     if args.kmap_sweep:
         kmap_sweep()
         return
+    sections = [] if args.sections in ("", "none") else [s for s in args.sections.split(",")]
+    bad = [s for s in sections if s not in SECTIONS]
+    if bad:
+        sys.exit(f"unknown sections {bad}; known: {SECTIONS}")
     dev = torch.device("cuda:0")
     inp = make_inputs(args.workload)
-    step = Step(inp, dev)
-    flops, bytes_ = step.work()
-    total_flop = sum(flops.values())
-
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-
-    # the timed steps, as a caller runs them (no per-stage instrumentation)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step.run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # then the same number of steps with HIP events around every stage, for the
-    # per-stage breakdown (the event records cost host time, so this pass is
-    # not the timed one)
-    events = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)] for k in step.names}
-    stage_ms = {k: 0.0 for k in step.names}
-    for i in range(args.steps):
-        step.run({k: events[k][i] for k in step.names})
-    torch.cuda.synchronize()
-    for k in step.names:
-        stage_ms[k] = sorted(a.elapsed_time(b) for a, b in events[k])[args.steps // 2]   # median
+    dtype = dtype_name(inp["dtype"])
+    step, r = run_step(inp, dev, args.steps, args.warmup)
+    head = step_summary(inp, step, r, args.steps, dtype)
+    fwd_ms = head["subm_fwd_ms"]
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -553,51 +762,17 @@ def main():
         bb.copy_(a)
         torch.cuda.synchronize()
 
-    dtype = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[inp["dtype"]]
-    stages = {}
-    for k in step.names:
-        t = stage_ms[k] * 1e-3
-        stages[k] = {"ms": round(stage_ms[k], 4),
-                     "TFLOP/s": round(flops[k] / t / 1e12, 2) if k in flops and t > 0 else None,
-                     "alg_GB/s": round(bytes_[k] / t / 1e9, 1) if t > 0 else None}
-    kernel_ms = {k: step.kernel_ms(k) for k in SINGLE_KERNEL_STAGES}
-    dom = max(SINGLE_KERNEL_STAGES, key=lambda k: kernel_ms[k])
-    t_dom = kernel_ms[dom] * 1e-3
-    ai = flops[dom] / bytes_[dom]
-    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(bytes_[dom] / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(flops[dom] / t_dom / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, dom)
-    roof["kernel"] = f"k_conv ({dom})"
-    roof["algorithmic_bytes_per_launch"] = bytes_[dom]
-    roof["flop_per_launch"] = flops[dom]
-    roof["avg_launch_ms"] = round(kernel_ms[dom], 4)
-    roof["kernel_ms"] = {k: round(v, 4) for k, v in kernel_ms.items()}
-
-    extras = {}
-    for name, (launch, fl, by) in ({} if args.no_extras else step.extras()).items():
-        ms = step.time_launch(launch)
-        t = ms * 1e-3
-        bound = "hbm" if fl / by < ridge else "mfma"
-        ach = by / t / 1e9 if bound == "hbm" else fl / t / 1e12
-        peak = HBM_PEAK_GBS if bound == "hbm" else MFMA_PEAK_TFLOPS[dtype]
-        extras[name] = {"kernel_ms": round(ms, 4), "TFLOP/s": round(fl / t / 1e12, 2) if fl else None,
-                        "alg_GB/s": round(by / t / 1e9, 1), "bound": bound, "frac": round(ach / peak, 4)}
-
-    kmap_vps = step.n / (stage_ms["kmap_subm"] * 1e-3)
+    roof = roofline("k_conv", "fwd_subm", r["flops"]["fwd_subm"], r["bytes"]["fwd_subm"], fwd_ms, dtype,
+                    args.workload)
+    roof["kernel_ms_back_to_back"] = round(r["kernel_ms"]["fwd_subm"], 4)
     out = {
         "metric": "effective TFLOP/s of SubMConv3d fwd (occupied pairs) + kmap voxels/s, 1 MI355X",
-        "value": round(total_flop / (ms_per_step * 1e-3) / 1e12, 3),
+        "value": head["subm_fwd_TFLOP/s"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -605,23 +780,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": inp["name"], "n_voxels": step.n, "pairs_subm_k3": step.P,
                    "n_out_strided": step.m, "pairs_strided": step.Ps,
-                   "channels": [int(step.w3.shape[1]), int(step.w3.shape[2]), int(step.ws.shape[2])]},
-        "subm_fwd_TFLOP/s": stages["fwd_subm"]["TFLOP/s"],
-        "kmap_voxels_per_s": round(kmap_vps, 1),
-        "stages": stages,
+                   "channels": head["channels"], "kmap_table": "hash"},
+        "kmap_voxels_per_s": head["kmap_voxels_per_s"],
+        "subm_fwd_ms": fwd_ms,
+        "kmap_subm_ms": head["kmap_subm_ms"],
+        "stages": head["stages"],
+        "kernel_ms": head["kernel_ms"],
         "roofline": roof,
-        "extras": extras,
     }
+    lidar_step = None
+    if "lidar_step" in sections or "extras" in sections:
+        lidar_step, lid = section_lidar(dev, args.steps, args.warmup)
+        if "lidar_step" in sections:
+            out["lidar_step"] = lid
+    if "train96" in sections:
+        out["train96"] = section_train96(dev, args.steps, args.warmup)
+    if "uniform32_f32" in sections:
+        out["uniform32_f32"] = section_uniform32(dev, args.steps, args.warmup)
+    if "kmap_tables" in sections:
+        out["kmap_tables"] = section_kmap_tables(dev)
+    if "extras" in sections:
+        out["extras"] = section_extras(lidar_step, dtype_name(lidar_step.x.dtype))
     if not args.no_cpu_baseline:
-        def stage_flops(name, state):
-            cin, c1, cs = inp["w3"].shape[1], inp["w3"].shape[2], inp["ws"].shape[2]
-            n = inp["coords"].shape[0]
-            return {"fwd_subm": 2 * state.get("P", 0) * cin * c1, "fwd_k1": 2 * n * c1 * inp["w1"].shape[2],
-                    "dinput_subm": 2 * state.get("P", 0) * cin * c1, "dfilter_subm": 2 * state.get("P", 0) * cin * c1,
-                    "fwd_strided": 2 * state.get("Ps", 0) * cin * cs,
-                    "dinput_strided": 2 * state.get("Ps", 0) * cin * cs,
-                    "dfilter_strided": 2 * state.get("Ps", 0) * cin * cs}.get(name, 0)
-        out["cpu_baseline"] = cpu_baseline(inp, stage_flops, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

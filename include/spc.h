@@ -58,6 +58,14 @@ typedef enum spc_dtype { SPC_F32 = 0, SPC_F16 = 1, SPC_BF16 = 2 } spc_dtype;
 #define SPC_COORD_OUT_OF_RANGE 1  /* b not in [0, batch) or z/y/x outside shape  */
 #define SPC_COORD_DUPLICATE    2  /* two rows share (b, z, y, x)                  */
 
+/* Input table of spc_build_kmap (spc_geom.table). */
+#define SPC_TABLE_HASH 0  /* open-addressing hash over the packed keys, 2^ceil(log2 4N)
+                             slots of 8 bytes (the default; any grid)               */
+#define SPC_TABLE_GRID 1  /* occupancy bitmap (1 bit per cell, cleared per call) and an
+                             int32 index grid (4 bytes per cell, never cleared) over
+                             the whole input grid: batch*Z*Y*X*4.125 bytes of
+                             workspace, for grids that are small next to N          */
+
 /*
  * Convolution geometry.  subm != 0 selects a submanifold convolution (spconv
  * USAGE.md, "Submanifold Convolution": output sites are the input sites): each
@@ -66,6 +74,8 @@ typedef enum spc_dtype { SPC_F32 = 0, SPC_F16 = 1, SPC_BF16 = 2 } spc_dtype;
  * convolution whose output extent per axis is
  * floor((shape + 2*pad - dil*(ksize-1) - 1) / stride) + 1.
  * batch * Z * Y * X (and the output grid's volume) must stay below 2^32.
+ * table selects the kernel map's input table (SPC_TABLE_*); both give the
+ * same results bit for bit.
  */
 typedef struct spc_geom {
     int32_t batch;      /* samples; coords[:,0] in [0, batch)           */
@@ -75,6 +85,7 @@ typedef struct spc_geom {
     int32_t pad[3];
     int32_t dil[3];
     int32_t subm;
+    int32_t table;      /* SPC_TABLE_HASH (0) or SPC_TABLE_GRID          */
 } spc_geom;
 
 /* Host only.  Output spatial extent of a strided geometry (the input shape for
@@ -88,8 +99,10 @@ spc_status spc_kmap_workspace(const spc_geom* g, int64_t n_in, size_t* bytes);
 /*
  * Kernel map ("indice pairs"; spconv's get_indice_pairs_implicit_gemm on the
  * context7 spconv page, INT8_GUIDE.md snippet).  Builds a GPU hash table over
- * the packed keys ((b*Z + z)*Y + y)*X + x of the input rows.  Maps are
- * row-major: entry k of a row is that row's neighbour through offset k.
+ * the packed keys ((b*Z + z)*Y + y)*X + x of the input rows (the single-slot
+ * hash.HashTable of the spconv page; g->table may select the index grid
+ * instead) and probes it for every kernel offset.  Maps are row-major: entry
+ * k of a row is that row's neighbour through offset k.
  *
  * subm != 0 (the MLX page's build_indice_map, computed on the GPU):
  *   nbr       [n_in, K] int32: nbr[i*K + k] = row j with coords[j] =

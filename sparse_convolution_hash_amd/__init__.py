@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     lib,
     make_geom,
     out_shape,
+    strided_out_bound,
     point_to_voxel,
     sparse_conv_fwd,
     sparse_inverse_conv_fwd,

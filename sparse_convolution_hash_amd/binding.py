@@ -43,7 +43,10 @@ class SpcError(RuntimeError):
 class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("shape", ctypes.c_int32 * 3), ("ksize", ctypes.c_int32 * 3),
                 ("stride", ctypes.c_int32 * 3), ("pad", ctypes.c_int32 * 3), ("dil", ctypes.c_int32 * 3),
-                ("subm", ctypes.c_int32)]
+                ("subm", ctypes.c_int32), ("table", ctypes.c_int32)]
+
+
+TABLES = {"hash": 0, "grid": 1}   # SPC_TABLE_HASH, SPC_TABLE_GRID
 
 
 def _t3(v) -> tuple:
@@ -55,9 +58,11 @@ def _t3(v) -> tuple:
     return v
 
 
-def make_geom(batch: int, shape, ksize, stride=1, pad=0, dil=1, subm: bool = True) -> Geom:
+def make_geom(batch: int, shape, ksize, stride=1, pad=0, dil=1, subm: bool = True, table: str = "hash") -> Geom:
     a = lambda v: (ctypes.c_int32 * 3)(*_t3(v))
-    return Geom(int(batch), a(shape), a(ksize), a(stride), a(pad), a(dil), 1 if subm else 0)
+    if table not in TABLES:
+        raise ValueError(f"table must be one of {tuple(TABLES)}, got {table!r}")
+    return Geom(int(batch), a(shape), a(ksize), a(stride), a(pad), a(dil), 1 if subm else 0, TABLES[table])
 
 
 _lib = None
@@ -155,16 +160,35 @@ def kmap_workspace(g: Geom, n_in: int) -> int:
 
 
 @functools.lru_cache(maxsize=256)
-def _kmap_plan(batch, shape, ksize, stride, pad, dil, subm, n_in):
+def _kmap_plan(batch, shape, ksize, stride, pad, dil, subm, n_in, table):
     """(Geom, K, workspace bytes) of a kernel-map call; the Geom is shared and
     never modified."""
-    g = make_geom(batch, shape, ksize, stride, pad, dil, subm)
+    g = make_geom(batch, shape, ksize, stride, pad, dil, subm, table)
     return g, int(g.ksize[0] * g.ksize[1] * g.ksize[2]), kmap_workspace(g, n_in)
+
+
+def strided_out_bound(n_in: int, batch: int, shape, ksize, stride=1, pad=0, dil=1) -> int:
+    """Upper bound of a strided map's output-site count that follows from the
+    geometry alone (the role of spconv's ``out_inds_num_limit``): along an
+    axis the offsets k*dil, k < ksize, reach an exact multiple of the stride at
+    most ceil(ksize / (stride / gcd(stride, dil))) times, so an input feeds at
+    most the product of those over the axes; and never more than the output
+    grid holds."""
+    import math
+    ks, st, dl = _t3(ksize), _t3(stride), _t3(dil)
+    per = 1
+    for k, s, d in zip(ks, st, dl):
+        per *= -(-k // (s // math.gcd(s, d)))
+    vol = int(batch)
+    for o in out_shape(batch, shape, ksize, stride, pad, dil, subm=False):
+        vol *= max(o, 0)
+    return int(min(int(n_in) * per, vol))
 
 
 def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
                subm: bool = True, pairs: bool = True, with_nbr_in: bool = True, orders: bool = False,
-               out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> dict:
+               out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+               table: str = "hash", count_first: bool = False) -> dict:
     """Kernel map of int32 [N, 4] (b, z, y, x) coordinates (spc_build_kmap).
 
     Returns a dict with ``nbr`` [n_out, K] (submanifold neighbour map or the
@@ -173,8 +197,12 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     the CSR pair lists ``pair_ptr`` [K+1], ``pair_in`` / ``pair_out`` (first
     pair_ptr[K] entries valid) and the processing orders ``order`` (rows of
     nbr) and ``order_in`` (rows of nbr_in).  A strided call without
-    ``out_cap`` first asks the library for the output count, then allocates
-    exactly.
+    ``out_cap`` sizes its outputs by ``strided_out_bound`` (one library call,
+    which returns the count M; the result views hold M rows), or with
+    ``count_first`` asks the library for M first and allocates exactly (two
+    calls).  ``table`` picks the input table: ``"hash"`` (default) or
+    ``"grid"`` (occupancy bitmap + index grid over the whole input grid, 4.125
+    bytes of workspace per cell); the results are the same.
     """
     _need(coords, "coords", torch.int32)
     if coords.dim() != 2 or coords.shape[1] != 4:
@@ -182,9 +210,12 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     dev = coords.device
     n = coords.shape[0]
     key = lambda v: v if isinstance(v, int) else tuple(v)
-    g, K, ws_bytes = _kmap_plan(int(batch), key(shape), key(ksize), key(stride), key(pad), key(dil), bool(subm), n)
+    g, K, ws_bytes = _kmap_plan(int(batch), key(shape), key(ksize), key(stride), key(pad), key(dil), bool(subm), n,
+                                table)
     stream = _stream(dev)
     n_out = ctypes.c_int64(0)
+    if not subm and out_cap is None and not count_first:
+        out_cap = strided_out_bound(n, batch, shape, ksize, stride, pad, dil)
     if not subm and out_cap is None:
         ws = workspace if workspace is not None and workspace.numel() >= ws_bytes else \
             torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)

@@ -39,8 +39,8 @@ constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
-constexpr uint64_t OCC_CELLS_PER_ROW = 4096;   // occupancy bitmap up to this many input cells per row (512 B)
-constexpr uint64_t DENSE_MAX_BYTES = uint64_t(1) << 30;   // index grid limit
+constexpr uint64_t OCC_FILTER_CELLS_PER_ROW = 8192;        // hash filter: at most 1 KiB of bitmap per row
+constexpr uint64_t OCC_FILTER_MAX_BYTES = uint64_t(1) << 30;
 
 struct KGeom {
     int32_t batch, Z, Y, X;      // input grid
@@ -53,7 +53,7 @@ struct KGeom {
     // K, the strides, and the output grid's x extent, plane and volume
     uint64_t mK, msz, msy, msx, mox, mplane, mvol;
     int32_t occ;                 // input occupancy bitmap in use (see make_plan)
-    int32_t dense;               // ... and, beside it, the index grid as the table (both or neither)
+    int32_t dense;               // the index grid is the table (with the bitmap); else the hash is
 };
 
 // ceil(2^64 / d) for d >= 2, 0 for d == 1 (see qdiv)
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         return;
     }
     const uint32_t key = in_key(c.x, c.y, c.z, c.w, g);
-    if (g.occ) {
+    if (g.dense) {
         const uint32_t bit = 1u << (key & 31u);
         if (STRIDED) {  // a cell whose bit was already set is a duplicate (the host reads it with the count)
             if (atomicOr(occ + (key >> 5), bit) & bit) atomicOr(hdr + H_FLAGS, SPC_COORD_DUPLICATE);
@@ -189,6 +189,8 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         }
         reinterpret_cast<int32_t*>(table)[key] = i;
     } else {
+        // the hash flags duplicates itself; its bitmap filter only needs the bit
+        if (g.occ) atomicOr(occ + (key >> 5), 1u << (key & 31u));
         table_insert(table, mask, key, uint32_t(i), hdr + H_FLAGS);
     }
     if (!STRIDED) return;
@@ -255,9 +257,11 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
                 atomicOr(coord_err, SPC_COORD_DUPLICATE);
         } else if ((unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X) {
             const uint32_t key = in_key(c.x, z, y, x, g);
-            if (!g.dense)
+            if (g.occ && !((occ[key >> 5] >> (key & 31u)) & 1u))
+                v = -1;
+            else if (!g.dense)
                 v = table_find(table, mask, key);
-            else if ((occ[key >> 5] >> (key & 31u)) & 1u)
+            else
                 v = reinterpret_cast<const int32_t*>(table)[key];
         }
     }
@@ -503,15 +507,19 @@ __device__ __noinline__ int32_t table_find_after(const uint64_t* __restrict__ ta
 // o * stride - pad + k * dil (a submanifold map has stride 1 and pad K/2, and
 // its centre entry is the row itself).  The K lookups of a row are issued
 // together, so a wave has all its rows' lookups in flight at once: with the
-// index grid, the K occupancy words, then the grid cells of the occupied
-// neighbours; with the hash, the keys' home slots, which answer nearly every
-// probe at load factor <= 1/4 (the few longer probe sequences continue
-// afterwards).  Entries go to an LDS tile (row stride K words) and leave as
+// index grid (TBL_GRID), the K occupancy words, then the grid cells of the
+// occupied neighbours; with the hash behind its bitmap filter (TBL_FILTERED),
+// the K occupancy words, then the home slots of the occupied neighbours only;
+// with the plain hash (TBL_HASH), all K home slots.  At load factor <= 1/4 a
+// home slot answers nearly every probe (the few longer probe sequences
+// continue afterwards).  Entries go to an LDS tile (row stride K words) and leave as
 // coalesced row-major stores; the thread then has its row's mask (keys,
 // K <= 32) and the block's per-offset hit counts (counts[k*gridDim.x +
 // block]), as k_row_pass makes them.  rows < 0: M from the header (rows
 // beyond the capacity read as none).
-template <bool DENSE, bool SUBM>
+enum { TBL_HASH = 0, TBL_FILTERED = 1, TBL_GRID = 2 };
+
+template <int TBL, bool SUBM>
 __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoords, int32_t rows, int64_t cap, KGeom g,
                                                  const uint64_t* __restrict__ table, uint32_t mask,
                                                  const uint32_t* __restrict__ occ,
@@ -542,6 +550,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     const bool live = i < rows;
     const int4 c = rcoords[live ? i : rows - 1];
     const bool ok = live && (!SUBM || in_grid(c, g));  // output sites lie inside their grid
+    constexpr bool DENSE = TBL == TBL_GRID, BITS = TBL != TBL_HASH;
     const int32_t* dense = reinterpret_cast<const int32_t*>(table);
     // 1. every lookup of the row, from valid addresses (cell 0 or its slot
     //    when the neighbour is outside the grid; such entries are -1 regardless)
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
                         (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X;
         key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
         inside |= uint32_t(in) << k;
-        got[k] = DENSE ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
+        got[k] = BITS ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
     }
     if (DENSE) {  // grid cells of the occupied neighbours (cell 0, ignored, elsewhere)
 #pragma unroll
@@ -567,6 +576,13 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
             const bool hit = ((inside >> k) & (uint32_t(got[k]) >> (key[k] & 31u)) & 1u) != 0;
             const int32_t v = dense[hit ? key[k] : 0u];
             got[k] = uint64_t(uint32_t(hit ? v : -1));
+        }
+    } else if (BITS) {  // home slots of the occupied neighbours (slot 0, ignored, elsewhere)
+#pragma unroll
+        for (int k = 0; k < ROWPASS_KMAX; ++k) {
+            const bool hit = ((inside >> k) & (uint32_t(got[k]) >> (key[k] & 31u)) & 1u) != 0;
+            const uint64_t v = table[hit ? home_slot(key[k]) & mask : 0u];
+            got[k] = hit ? v : EMPTY_SLOT;
         }
     }
     // 2. resolve into LDS; hash probes that met another key finish afterwards
@@ -838,22 +854,28 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     if (int64_t(p.K) * n_in >= (int64_t(1) << 31))
         return fail(SPC_ERR_UNSUPPORTED, "K*n_in=%lld must be below 2^31", (long long)(int64_t(p.K) * n_in));
     p.n = n_in;
-    // The input table.  A grid of at most OCC_CELLS_PER_ROW cells per input row
-    // (and an index grid of at most DENSE_MAX_BYTES) gets an occupancy bitmap,
-    // one bit per cell and at most 512 bytes per row to clear, and beside it
-    // the index grid, one int32 row per cell.  An insert sets its bit with one
-    // atomic OR, whose old value flags a duplicate, and stores its row in the
-    // grid; the grid is read only where the bitmap says occupied, so it is
-    // never cleared.  A lookup is a bitmap word and, for an occupied cell, one
-    // grid load.  Larger, sparser grids get the hash: load factor <= 1/4 keeps
-    // unsuccessful probes (most of them) near one load.  The table region is
-    // cap 8-byte words.
-    k.dense = in_vol <= OCC_CELLS_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1)) && in_vol * 4 <= DENSE_MAX_BYTES;
-    k.occ = k.dense;
+    // The input table.  SPC_TABLE_HASH: the hash, whose load factor <= 1/4
+    // keeps unsuccessful probes (most of them) near one load.
+    // SPC_TABLE_GRID: an occupancy bitmap, one bit per cell, cleared per call,
+    // and beside it the index grid, one int32 row per cell.  An insert sets
+    // its bit with one atomic OR, whose old value flags a duplicate, and
+    // stores its row in the grid; the grid is read only where the bitmap says
+    // occupied, so it is never cleared.  A lookup is a bitmap word and, for an
+    // occupied cell, one grid load.  The table region is cap 8-byte words.
+    // The hash gets the occupancy bitmap beside it as an exact filter when the
+    // bitmap is small next to the rows (at most 1 KiB per row, at most 1 GiB):
+    // most of a sparse scene's K lookups per row find an empty cell, and then
+    // cost a bitmap word (neighbouring cells share words) instead of a hash
+    // probe at a random slot; the hash is probed for occupied cells only.
+    if (g.table != SPC_TABLE_HASH && g.table != SPC_TABLE_GRID)
+        return fail(SPC_ERR_ARG, "table=%d must be SPC_TABLE_HASH or SPC_TABLE_GRID", g.table);
+    k.dense = g.table == SPC_TABLE_GRID;
+    k.occ = k.dense || (in_vol <= OCC_FILTER_CELLS_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1)) &&
+                        in_vol / 8 <= OCC_FILTER_MAX_BYTES);
     p.occ_words = k.occ ? int64_t(ceil_div(int64_t(in_vol), 128) * 4) : 0;
     p.cap_log2 = 6;
     while ((int64_t(1) << p.cap_log2) < 4 * n_in) ++p.cap_log2;
-    p.cap = k.dense ? int64_t((in_vol + 1) / 2) : k.occ ? 0 : int64_t(1) << p.cap_log2;
+    p.cap = k.dense ? int64_t((in_vol + 1) / 2) : int64_t(1) << p.cap_log2;
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
     p.nwords = g.subm ? 0 : std::max<int64_t>(wpb, ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb);
     p.bm_blocks = p.nwords / wpb;
@@ -1126,7 +1148,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     const int64_t entries = int64_t(n) * p.K;
 
     const int64_t nzero = (order || order_in) ? int64_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups : 0;
-    const int64_t fill = p.g.occ ? 0 : p.cap;   // hash slots to mark empty (the index grid is never cleared)
+    const int64_t fill = p.g.dense ? 0 : p.cap;   // hash slots to mark empty (the index grid is never cleared)
     hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({fill / 2, p.nwords / 4, p.occ_words / 4, nzero / 4}), KB, 4096)),
                        dim3(KB), 0, stream, table, fill, bitmap, p.nwords, occ, p.occ_words, s.hdr, coord_err, s.gsum,
                        nzero);
@@ -1143,7 +1165,8 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
 
     if (subm && p.K <= ROWPASS_KMAX) {
         // probes, masks and counts in one pass over the rows
-        auto rows_kernel = p.g.dense ? k_out_rows<true, true> : k_out_rows<false, true>;
+        auto rows_kernel = p.g.dense ? k_out_rows<TBL_GRID, true>
+                                     : p.g.occ ? k_out_rows<TBL_FILTERED, true> : k_out_rows<TBL_HASH, true>;
         hipLaunchKernelGGL(rows_kernel, dim3(unsigned(std::max(nblk, 1))), dim3(KB), 0, stream, c4, n, int64_t(n), p.g,
                            table, mask,
                            occ, nbr, (pairs || order) ? s.mask[0] : nullptr, pairs ? s.counts : nullptr, s.hdr,
@@ -1220,7 +1243,8 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
                                    p.g, bitmap, prefix, nbr_in, order_in ? s.mask[1] : nullptr, s.hdr);
                 SPC_LAUNCHED("k_in_rows");
             }
-            auto rows_kernel = p.g.dense ? k_out_rows<true, false> : k_out_rows<false, false>;
+            auto rows_kernel = p.g.dense ? k_out_rows<TBL_GRID, false>
+                                         : p.g.occ ? k_out_rows<TBL_FILTERED, false> : k_out_rows<TBL_HASH, false>;
             hipLaunchKernelGGL(rows_kernel, dim3(unsigned(std::max<int64_t>(ceil_div(cap, KB), 1))), dim3(KB), 0, stream,
                                reinterpret_cast<const int4*>(out_coords), -1, int64_t(out_cap), p.g, table, mask, occ,
                                nbr, (pairs || order) ? s.mask[0] : nullptr, pairs ? s.counts : nullptr, s.hdr,

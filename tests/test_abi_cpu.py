@@ -135,3 +135,36 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         B.subm_conv_fwd(torch.zeros(4, 16), torch.zeros(27, 16, 16), None, torch.zeros(27, 4, dtype=torch.int32))
+
+
+def test_kmap_table_choice():
+    # the hash (default) needs 2^ceil(log2 4N) 8-byte slots; the index grid
+    # 4 bytes per cell plus a bit per cell; any other table value is refused
+    lidar = dict(batch=2, shape=(41, 1600, 1408), ksize=3)
+    st, hash_bytes = _ws(B.make_geom(**lidar), 120000)
+    st2, grid_bytes = _ws(B.make_geom(**lidar, table="grid"), 120000)
+    cells = 2 * 41 * 1600 * 1408
+    assert st == st2 == B.SPC_OK
+    assert hash_bytes >= (1 << 19) * 8 and hash_bytes < 64 << 20
+    assert grid_bytes >= cells * 4 + cells // 8
+    g = B.make_geom(**lidar)
+    g.table = 2
+    assert _ws(g, 120000)[0] == B.SPC_ERR_ARG
+    assert "table" in B.lib().spc_last_error().decode()
+    with pytest.raises(ValueError):
+        B.make_geom(**lidar, table="dense")
+
+
+@pytest.mark.parametrize("shape,k,s,p,d", [
+    ((7, 8, 6), 3, 2, 1, 1), ((8, 8, 8), 2, 2, 0, 1), ((9, 7, 8), 3, 1, 0, 2), ((8, 9, 7), 3, 3, 2, 1),
+    ((12, 12, 12), 5, 2, 2, 1), ((10, 10, 10), 3, 2, 1, 2),
+])
+def test_strided_out_bound_holds(shape, k, s, p, d):
+    # the geometric bound the binding sizes strided outputs by is never below
+    # the oracle's output count, and equals 8N for k3 s2 on a large grid
+    import workloads as W
+    c = W.tiny_grid(W.rng(400 + k * s), min(shape), 0.3, 2)
+    m = O.strided_kmap(c, 2, shape, k, s, p, d)["out_coords"].shape[0]
+    assert m <= B.strided_out_bound(c.shape[0], 2, shape, k, s, p, d)
+    assert B.strided_out_bound(1000, 2, (41, 1600, 1408), 3, 2, 1, 1) == 8000
+    assert B.strided_out_bound(10 ** 7, 1, (8, 8, 8), 3, 2, 1, 1) == 4 * 4 * 4

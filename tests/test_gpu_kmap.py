@@ -27,32 +27,45 @@ def mask_order(map_kn):
     return np.argsort(m, kind="stable")
 
 
-def check_subm(coords, batch, shape, k, pairs=True, orders=True):
-    print(f"subm kmap n={coords.shape[0]} shape={shape} k={k}", flush=True)
-    res = spc.build_kmap(cuda(coords), batch, shape, k, subm=True, pairs=pairs, orders=orders)
+TABLES = ("hash", "grid")   # both input tables, checked against the same oracle map
+
+
+def check_subm(coords, batch, shape, k, pairs=True, orders=True, tables=TABLES):
+    """Both tables' maps equal the oracle's; returns the hash table's result."""
     ref = O.subm_kmap(coords, shape, k)
-    assert res["n_out"] == coords.shape[0]
-    assert np.array_equal(host(res["nbr"]), ref.T)
-    assert int(host(res["coord_err"])[0]) == 0
-    if pairs:
-        pairs_equal(res, *O.pairs_from_map(ref))
-    if orders:
-        assert np.array_equal(host(res["order"]), mask_order(ref))
-    return res
+    out = {}
+    c = cuda(coords)
+    for table in tables:
+        print(f"subm kmap table={table} n={coords.shape[0]} shape={shape} k={k}", flush=True)
+        res = spc.build_kmap(c, batch, shape, k, subm=True, pairs=pairs, orders=orders, table=table)
+        assert res["n_out"] == coords.shape[0]
+        assert np.array_equal(host(res["nbr"]), ref.T), table
+        assert int(host(res["coord_err"])[0]) == 0
+        if pairs:
+            pairs_equal(res, *O.pairs_from_map(ref))
+        if orders:
+            assert np.array_equal(host(res["order"]), mask_order(ref)), table
+        out[table] = res
+    return out[tables[0]]
 
 
-def check_strided(coords, batch, shape, k, s, p, d, out_cap=None):
-    print(f"strided kmap n={coords.shape[0]} shape={shape} k={k} s={s} p={p} d={d}", flush=True)
-    res = spc.build_kmap(cuda(coords), batch, shape, k, s, p, d, subm=False, out_cap=out_cap, orders=True)
+def check_strided(coords, batch, shape, k, s, p, d, out_cap=None, tables=TABLES):
+    """Both tables' strided maps equal the oracle's; returns the hash table's result."""
     ref = O.strided_kmap(coords, batch, shape, k, s, p, d)
-    assert res["n_out"] == ref["out_coords"].shape[0]
-    assert np.array_equal(host(res["out_coords"]), ref["out_coords"])
-    assert np.array_equal(host(res["nbr"]), ref["nbr_out"].T)
-    assert np.array_equal(host(res["nbr_in"]), ref["nbr_in"].T)
-    pairs_equal(res, *O.pairs_from_map(ref["nbr_out"]))
-    assert np.array_equal(host(res["order"]), mask_order(ref["nbr_out"]))
-    assert np.array_equal(host(res["order_in"]), mask_order(ref["nbr_in"]))
-    return res
+    out = {}
+    c = cuda(coords)
+    for table in tables:
+        print(f"strided kmap table={table} n={coords.shape[0]} shape={shape} k={k} s={s} p={p} d={d}", flush=True)
+        res = spc.build_kmap(c, batch, shape, k, s, p, d, subm=False, out_cap=out_cap, orders=True, table=table)
+        assert res["n_out"] == ref["out_coords"].shape[0]
+        assert np.array_equal(host(res["out_coords"]), ref["out_coords"]), table
+        assert np.array_equal(host(res["nbr"]), ref["nbr_out"].T), table
+        assert np.array_equal(host(res["nbr_in"]), ref["nbr_in"].T), table
+        pairs_equal(res, *O.pairs_from_map(ref["nbr_out"]))
+        assert np.array_equal(host(res["order"]), mask_order(ref["nbr_out"])), table
+        assert np.array_equal(host(res["order_in"]), mask_order(ref["nbr_in"])), table
+        out[table] = res
+    return out[tables[0]]
 
 
 @pytest.mark.parametrize("seed,side,fill,batch,k", [
@@ -78,16 +91,49 @@ def test_subm_edge_cases():
     check_subm(c, 2, (7, 5, 3), 3)
 
 
-def test_subm_flags_bad_coordinates():
+@pytest.mark.parametrize("table", TABLES)
+def test_subm_flags_bad_coordinates(table):
     shape = (6, 6, 6)
     c = np.array([[0, 1, 1, 1], [0, 1, 1, 1], [0, 2, 2, 2]], np.int32)
-    res = spc.build_kmap(cuda(c), 1, shape, 3)
+    res = spc.build_kmap(cuda(c), 1, shape, 3, table=table)
     assert int(host(res["coord_err"])[0]) & spc.binding.COORD_DUPLICATE
     c = np.array([[0, 1, 1, 1], [0, 6, 1, 1], [1, 2, 2, 2], [0, -1, 0, 0]], np.int32)
-    res = spc.build_kmap(cuda(c), 1, shape, 3)
+    res = spc.build_kmap(cuda(c), 1, shape, 3, table=table)
     assert int(host(res["coord_err"])[0]) == spc.binding.COORD_OUT_OF_RANGE
     nbr = host(res["nbr"])
     assert nbr[0, 13] == 0 and (nbr[1:, :] == -1).all()      # bad rows are left out
+
+
+@pytest.mark.parametrize("table", TABLES)
+def test_bad_coordinates_at_workload_size(table):
+    # the LiDAR scene (120k rows) with 500 out-of-range rows and then 300
+    # duplicates of existing rows appended: the flags are raised, the bad rows
+    # are left out, every other entry equals the oracle's map of the clean
+    # scene except that a duplicated site may resolve to either of its rows
+    w = W.workload("subm_k3_f16_lidar120k")
+    r = W.rng(301)
+    n = w.n
+    oob = w.coords[r.choice(n, 500, replace=False)].copy()
+    axis = r.integers(0, 4, 500)
+    oob[np.arange(500), axis] = np.array([w.batch, *w.shape])[axis] + r.integers(0, 3, 500)
+    ref = O.subm_kmap(w.coords, w.shape, 3)
+    res = spc.build_kmap(cuda(np.concatenate([w.coords, oob])), w.batch, w.shape, 3, table=table)
+    assert int(host(res["coord_err"])[0]) == spc.binding.COORD_OUT_OF_RANGE
+    nbr = host(res["nbr"])
+    assert np.array_equal(nbr[:n], ref.T) and (nbr[n:] == -1).all()
+    src = r.choice(n, 300, replace=False)
+    res = spc.build_kmap(cuda(np.concatenate([w.coords, w.coords[src]])), w.batch, w.shape, 3, table=table)
+    assert int(host(res["coord_err"])[0]) & spc.binding.COORD_DUPLICATE
+    nbr = host(res["nbr"])[:n]
+    twin = np.full(n, -1, np.int64)
+    twin[src] = n + np.arange(300)
+    want = ref.T
+    alt = np.where(want >= 0, twin[np.maximum(want, 0)], -1)
+    assert ((nbr == want) | ((alt >= 0) & (nbr == alt))).all()
+    with pytest.raises(spc.SpcError) as e:
+        spc.build_kmap(cuda(np.concatenate([w.coords, w.coords[src]])), w.batch, w.shape, 3, 2, 1, 1, subm=False,
+                       table=table)
+    assert e.value.status == spc.binding.SPC_ERR_COORD
 
 
 @pytest.mark.parametrize("seed,shape,fill,batch,k,s,p,d", [
@@ -141,16 +187,17 @@ def test_strided_golden_empty_output():
     assert res["nbr"].shape == (0, 27)
 
 
-def test_strided_capacity_and_errors():
+@pytest.mark.parametrize("table", TABLES)
+def test_strided_capacity_and_errors(table):
     w = W.workload("strided_k3s2_f16_lidar120k")
     with pytest.raises(spc.SpcError) as e:
-        spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=100)
+        spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=100, table=table)
     assert e.value.status == spc.binding.SPC_ERR_CAPACITY
     bad = np.array([[0, 1, 1, 1], [0, 1, 1, 1]], np.int32)
     with pytest.raises(spc.SpcError) as e:
-        spc.build_kmap(cuda(bad), 1, (4, 4, 4), 3, 2, 1, 1, subm=False)
+        spc.build_kmap(cuda(bad), 1, (4, 4, 4), 3, 2, 1, 1, subm=False, table=table)
     assert e.value.status == spc.binding.SPC_ERR_COORD
-    check_strided(np.zeros((0, 4), np.int32), 1, (4, 4, 4), 3, 2, 1, 1)
+    check_strided(np.zeros((0, 4), np.int32), 1, (4, 4, 4), 3, 2, 1, 1, tables=(table,))
 
 
 def test_kmap_repeatable():
@@ -165,8 +212,8 @@ def test_kmap_repeatable():
 
 
 def test_strided_kmap_on_a_user_stream():
-    # the input-side order is built on a side stream forked from the caller's:
-    # the result on a caller-made stream matches the default stream's bit for bit
+    # every launch goes on the caller's stream: a map built on a caller-made
+    # stream is bit-identical to one built on the default stream
     w = W.workload("strided_k3s2_f16_lidar120k")
     c = cuda(w.coords)
     ref = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
@@ -179,18 +226,22 @@ def test_strided_kmap_on_a_user_stream():
         assert torch.equal(res[key], ref[key]), key
 
 
-def test_dense_grid_and_hash_give_the_same_map():
-    # a small grid takes the dense index grid, a large one the hash; the same
-    # sites (far from the large grid's faces) have the same neighbours in both
+def test_shifted_sites_give_the_same_map():
+    # the same sites in a small grid and shifted into a large one (far from
+    # its faces) have the same neighbours, with either table
     c = W.tiny_grid(W.rng(250), 12, 0.3, 2)
-    small = check_subm(c, 2, (12, 12, 12), 3)                 # 3456 cells for ~1000 rows: dense
+    small = check_subm(c, 2, (12, 12, 12), 3)
     shifted = c + np.array([0, 40, 50, 60], np.int32)
-    big = check_subm(shifted, 2, (200, 220, 240), 3)          # ~10^7 cells: hash
+    big = check_subm(shifted, 2, (200, 220, 240), 3)
     assert torch.equal(small["nbr"], big["nbr"]) and torch.equal(small["order"], big["order"])
     check_strided(shifted, 2, (200, 220, 240), 3, 2, 1, 1)
 
 
-def test_dense_grid_flags_duplicates():
-    c = np.array([[0, 1, 1, 1], [0, 2, 2, 2], [0, 1, 1, 1]], np.int32)   # 64 cells, 3 rows: dense
-    res = spc.build_kmap(cuda(c), 1, (4, 4, 4), 3)
-    assert int(host(res["coord_err"])[0]) & spc.binding.COORD_DUPLICATE
+def test_hash_at_four_lidar_samples():
+    # four LiDAR samples (240k rows on a 4 x 41 x 1600 x 1408 grid): the hash
+    # only (the index grid would need 1.5 GB); the SubM map and the strided
+    # map bit-exact against the oracle
+    c = W.lidar_scene(W.rng(12), batch=4)
+    shape = (41, 1600, 1408)
+    check_subm(c, 4, shape, 3, tables=("hash",))
+    check_strided(c, 4, shape, 3, 2, 1, 1, tables=("hash",))
