@@ -290,6 +290,26 @@ spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * spc_conv_bwd_filter without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc.  Same arguments (minus ws
+ * and ws_bytes), result bit for bit, and errors as spc_conv_bwd_filter.  Its
+ * scratch is one static device array of SPC_DFILTER_SCRATCH_BYTES per GPU,
+ * which each GPU the library runs on holds until the process ends; a call
+ * whose spc_conv_bwd_filter_workspace size exceeds it returns
+ * SPC_ERR_UNSUPPORTED (128 x 128 channels with K = 27 and dbias fit).  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on the same GPU (on other streams, or from other
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero: a call writes every scratch byte it reads.
+ */
+#define SPC_DFILTER_SCRATCH_BYTES (36u << 20)
+spc_status spc_conv_bwd_filter_noalloc(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
+                                       const void* dout, int64_t n_out, int32_t cout, int32_t K,
+                                       const int32_t* pair_ptr, const int32_t* pair_in,
+                                       const int32_t* pair_out, float* dw, float* dbias, hipStream_t stream);
+
+/*
  * Sparse max pooling, forward (SparseMaxPool3d, spconv USAGE.md layer table:
  * downsampling whose dense version is nn.MaxPool3d, on the kernel map of a
  * strided layer with the pool's kernel size, stride and padding):

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     SpcError,
     build_kmap,
     conv_bwd_filter,
+    conv_bwd_filter_noalloc,
     conv_bwd_input,
     conv_fwd_fused,
     conv_fwd_wt,

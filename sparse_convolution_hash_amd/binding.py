@@ -29,7 +29,7 @@ EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_co
            "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_transpose_weight",
            "spc_conv_fwd_wt", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
-           "spc_conv_bwd_filter", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
+           "spc_conv_bwd_filter", "spc_conv_bwd_filter_noalloc", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
            "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_last_error",
            "spc_version")
 
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "spc_conv_bwd_filter_noalloc": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P],
         "spc_sparse_maxpool_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I64, _P, _P, _P],
         "spc_sparse_maxpool_bwd": [_I32, _P, _I64, _I32, _P, _P, _I32, _I64, _P, _P],
         "spc_point_to_voxel_workspace": [_I64, _I32, _I64, _I32, ctypes.POINTER(_SZ)],
@@ -488,6 +489,33 @@ def conv_bwd_filter(feats: torch.Tensor, dout: torch.Tensor, K: int, pair_ptr: O
                                    _ptr(dw), _ptr(db), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "spc_conv_bwd_filter")
     return dw, db
+
+
+def conv_bwd_filter_noalloc(feats: torch.Tensor, dout: torch.Tensor, K: int, pair_ptr: Optional[torch.Tensor],
+                            pair_in: Optional[torch.Tensor], pair_out: Optional[torch.Tensor], dw: torch.Tensor,
+                            dbias: Optional[torch.Tensor] = None) -> None:
+    """spc_conv_bwd_filter_noalloc: the weight (and optionally bias) gradient
+    into the caller's ``dw`` [K, Cin, Cout] fp32 (and ``dbias`` [Cout] fp32),
+    with the library's static scratch instead of a workspace; neither the
+    binding nor the library allocates anything."""
+    dev = feats.device
+    _need(feats, "feats", dev=dev)
+    _need(dout, "dout", feats.dtype, dev)
+    for t, nm in ((pair_ptr, "pair_ptr"), (pair_in, "pair_in"), (pair_out, "pair_out")):
+        if t is not None:
+            _need(t, nm, torch.int32, dev)
+    cin, cout = feats.shape[1], dout.shape[1]
+    _need(dw, "dw", torch.float32, dev)
+    if tuple(dw.shape) != (int(K), cin, cout):
+        raise ValueError(f"dw must be [{K}, {cin}, {cout}], got {tuple(dw.shape)}")
+    if dbias is not None:
+        _need(dbias, "dbias", torch.float32, dev)
+        if tuple(dbias.shape) != (cout,):
+            raise ValueError(f"dbias must be [{cout}], got {tuple(dbias.shape)}")
+    st = lib().spc_conv_bwd_filter_noalloc(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(dout),
+                                           dout.shape[0], cout, int(K), _ptr(pair_ptr), _ptr(pair_in),
+                                           _ptr(pair_out), _ptr(dw), _ptr(dbias), _stream(dev))
+    _check(st, "spc_conv_bwd_filter_noalloc")
 
 
 def sparse_maxpool_fwd(feats: torch.Tensor, nbr_out: torch.Tensor, n_out: int, want_argk: bool = True,

@@ -14,6 +14,7 @@
 // kernel sums each offset's partials in segment order, so the result does
 // not depend on scheduling.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -617,11 +618,40 @@ extern "C" spc_status spc_conv_bwd_filter_workspace(int64_t n_in, int64_t n_out,
     return SPC_OK;
 }
 
-extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
-                                          const void* dout, int64_t n_out, int32_t cout, int32_t K,
-                                          const int32_t* pair_ptr, const int32_t* pair_in, const int32_t* pair_out,
-                                          float* dw, float* dbias, void* ws, size_t ws_bytes, hipStream_t stream) {
-    clear_error();
+// Scratch of spc_conv_bwd_filter_noalloc: one static array per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device (dfilter_scratch), never the array's name.
+static __device__ __align__(256) char scratch[SPC_DFILTER_SCRATCH_BYTES];
+
+namespace spc {
+namespace {
+
+std::mutex scratch_mu;
+void* scratch_ptr[64];  // per device, guarded by scratch_mu
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device.
+spc_status dfilter_scratch(void** out) {
+    int dev = 0;
+    SPC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(SPC_ERR_UNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        SPC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || !aligned16(p)) return fail(SPC_ERR_HIP, "scratch symbol address %p", p);
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return SPC_OK;
+}
+
+// Checks of spc_conv_bwd_filter's arguments other than the workspace; the
+// workspace layout on success.
+spc_status dfilter_checks(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin, const void* dout,
+                          int64_t n_out, int32_t cout, int32_t K, const int32_t* pair_ptr, const int32_t* pair_in,
+                          const int32_t* pair_out, const float* dw, const float* dbias, DfLayout& l) {
     if (dtype != SPC_F32 && dtype != SPC_F16 && dtype != SPC_BF16) return fail(SPC_ERR_ARG, "unknown dtype %d", int(dtype));
     if (n_in < 0 || n_out < 0 || n_in >= (int64_t(1) << 31) || n_out >= (int64_t(1) << 31))
         return fail(SPC_ERR_ARG, "row counts out of range");
@@ -634,12 +664,17 @@ extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, in
     if (!identity && !(pair_ptr && pair_in && pair_out)) return fail(SPC_ERR_ARG, "pair_ptr/pair_in/pair_out must be all set or all NULL");
     if (!dw) return fail(SPC_ERR_ARG, "dw is NULL");
     if ((n_in > 0 && !feats) || (n_out > 0 && !dout)) return fail(SPC_ERR_ARG, "feats or dout is NULL");
-    const void* ptrs[] = {feats, dout, pair_ptr, pair_in, pair_out, dw, dbias, ws};
+    const void* ptrs[] = {feats, dout, pair_ptr, pair_in, pair_out, dw, dbias};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
-    const DfLayout l = df_layout(n_in, n_out, cin, cout, K, dbias != nullptr);
-    if (!ws) return fail(SPC_ERR_ARG, "workspace is NULL");
-    if (ws_bytes < l.total) return fail(SPC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    l = df_layout(n_in, n_out, cin, cout, K, dbias != nullptr);
+    return SPC_OK;
+}
+
+spc_status dfilter_run(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin, const void* dout,
+                       int64_t n_out, int32_t cout, int32_t K, const int32_t* pair_ptr, const int32_t* pair_in,
+                       const int32_t* pair_out, float* dw, float* dbias, void* ws, const DfLayout& l,
+                       hipStream_t stream) {
     DfArgs a{feats, dout, pair_ptr, pair_in, pair_out, static_cast<float*>(ws), int32_t(n_in), int32_t(n_out),
              cin, cout, K, 0};
     float* bias_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.off_dbias);
@@ -648,5 +683,45 @@ extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, in
         case SPC_F16: return launch_dfilter<F16>(a, dw, dbias, bias_part, l.rparts, stream);
         case SPC_BF16: return launch_dfilter<BF16>(a, dw, dbias, bias_part, l.rparts, stream);
     }
-    return SPC_ERR_ARG;
+    return fail(SPC_ERR_ARG, "unknown dtype %d", int(dtype));
+}
+
+}  // namespace
+}  // namespace spc
+
+extern "C" spc_status spc_conv_bwd_filter(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
+                                          const void* dout, int64_t n_out, int32_t cout, int32_t K,
+                                          const int32_t* pair_ptr, const int32_t* pair_in, const int32_t* pair_out,
+                                          float* dw, float* dbias, void* ws, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    DfLayout l;
+    spc_status st = dfilter_checks(dtype, feats, n_in, cin, dout, n_out, cout, K, pair_ptr, pair_in, pair_out, dw,
+                                   dbias, l);
+    if (st != SPC_OK) return st;
+    if (!ws) return fail(SPC_ERR_ARG, "workspace is NULL");
+    if (!aligned16(ws)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (ws_bytes < l.total) return fail(SPC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    return dfilter_run(dtype, feats, n_in, cin, dout, n_out, cout, K, pair_ptr, pair_in, pair_out, dw, dbias, ws, l,
+                       stream);
+}
+
+extern "C" spc_status spc_conv_bwd_filter_noalloc(spc_dtype dtype, const void* feats, int64_t n_in, int32_t cin,
+                                                  const void* dout, int64_t n_out, int32_t cout, int32_t K,
+                                                  const int32_t* pair_ptr, const int32_t* pair_in,
+                                                  const int32_t* pair_out, float* dw, float* dbias,
+                                                  hipStream_t stream) {
+    clear_error();
+    DfLayout l;
+    spc_status st = dfilter_checks(dtype, feats, n_in, cin, dout, n_out, cout, K, pair_ptr, pair_in, pair_out, dw,
+                                   dbias, l);
+    if (st != SPC_OK) return st;
+    if (l.total > SPC_DFILTER_SCRATCH_BYTES)
+        return fail(SPC_ERR_UNSUPPORTED,
+                    "cin=%d cout=%d K=%d needs %zu bytes of scratch; the allocation-free call holds %zu "
+                    "(use spc_conv_bwd_filter with a workspace)",
+                    cin, cout, K, l.total, size_t(SPC_DFILTER_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if ((st = dfilter_scratch(&ws)) != SPC_OK) return st;
+    return dfilter_run(dtype, feats, n_in, cin, dout, n_out, cout, K, pair_ptr, pair_in, pair_out, dw, dbias, ws, l,
+                       stream);
 }

@@ -168,3 +168,20 @@ def test_strided_out_bound_holds(shape, k, s, p, d):
     assert m <= B.strided_out_bound(c.shape[0], 2, shape, k, s, p, d)
     assert B.strided_out_bound(1000, 2, (41, 1600, 1408), 3, 2, 1, 1) == 8000
     assert B.strided_out_bound(10 ** 7, 1, (8, 8, 8), 3, 2, 1, 1) == 4 * 4 * 4
+
+
+def test_noalloc_dfilter_host_checks():
+    # the allocation-free dfilter refuses, before any HIP call, sizes whose
+    # scratch exceeds its static array, and bad arguments as the workspace form
+    L = B.lib()
+    call = lambda cin, cout, K, pp=FAKE, x=FAKE: L.spc_conv_bwd_filter_noalloc(
+        2, x, 100, cin, FAKE, 100, cout, K, pp, FAKE, FAKE, FAKE, None, None)
+    assert call(256, 256, 27) == B.SPC_ERR_UNSUPPORTED
+    assert "scratch" in L.spc_last_error().decode()
+    assert call(128, 128, 125) == B.SPC_ERR_UNSUPPORTED
+    assert call(24, 32, 27) == B.SPC_ERR_UNSUPPORTED              # channels not multiples of 16
+    assert call(128, 128, 27, x=MISALIGNED) == B.SPC_ERR_ARG
+    assert call(128, 128, 27, pp=None) == B.SPC_ERR_ARG            # pair lists: all or none
+    b = ctypes.c_size_t()
+    assert L.spc_conv_bwd_filter_workspace(10 ** 6, 10 ** 6, 128, 128, 27, 1, ctypes.byref(b)) == B.SPC_OK
+    assert b.value <= 36 << 20                                     # the named workloads' largest layer fits
