@@ -19,7 +19,10 @@ value = effective TFLOP/s of the SubMConv3d k=3 forward: 2 * P * Cin * Cout
 (P = occupied pairs, counted from the kernel map) over the forward's duration,
 the mean of HIP events recorded around it (on its stream) in each of the K
 timed steps.  kmap_voxels_per_s = N over the mean duration of the SubM kernel
-map, timed the same way.  ms_per_step is the wall time of the K timed steps.
+map (hash table, pair lists, processing order) called 20 times alone between
+HIP events; in the step it overlaps the convolutions on a side stream, and
+that time is kmap_subm_ms_in_step.  ms_per_step is the wall time of the K
+timed steps.
 The forward uses weights transposed once at set-up (a layer keeps its weights
 in the layout its kernel reads), so the timed forward is one kernel, which is
 also the roofline's kernel: its algorithmic FLOP over that mean duration
@@ -89,6 +92,9 @@ def parse():
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--kmap-sweep", action="store_true",
                     help="instead of the step: kernel-map rates as the scene grows (one line per size)")
+    ap.add_argument("--calibration", action="store_true",
+                    help="instead of the step: measured MFMA rates (both bf16 shapes, 1-8 waves per SIMD) "
+                         "and a streaming-copy HBM rate")
     return ap.parse_args()
 
 
@@ -734,6 +740,42 @@ def kmap_sweep(reps=10):
         torch.cuda.empty_cache()
 
 
+def calibration(iters=4000):
+    """Measured rates of this part for reading the roofline: the bf16 MFMA
+    shapes' FLOP rate on register operands (spc_calibrate_mfma) at 1, 2, 4 and
+    8 waves per SIMD, and a 4 GiB device-to-device copy (read + write bytes over
+    time).  One JSON line."""
+    import torch
+    import sparse_convolution_hash_amd as spc
+    dev = torch.device("cuda:0")
+    sink = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    out = {"calibration": {"mfma_bf16_TFLOP/s": {}, "published_peak": {"bf16_TFLOP/s": MFMA_PEAK_TFLOPS["bf16"],
+                                                                       "hbm_GB/s": HBM_PEAK_GBS}}}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        for blocks in (256, 512, 1024, 2048):
+            spc.calibrate_mfma(shape, blocks, iters, sink)
+            torch.cuda.synchronize()
+            a, b = event_pair()
+            a.record()
+            flop = spc.calibrate_mfma(shape, blocks, iters, sink)
+            b.record()
+            torch.cuda.synchronize()
+            tf = flop / (a.elapsed_time(b) * 1e-3) / 1e12
+            out["calibration"]["mfma_bf16_TFLOP/s"][f"{name}_{blocks * 4 // 1024}waves_per_simd"] = round(tf, 1)
+    x = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = event_pair()
+    a.record()
+    for _ in range(5):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    out["calibration"]["copy_GB/s"] = round(5 * 2 * x.numel() / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -744,6 +786,9 @@ def main():
 
     if args.kmap_sweep:
         kmap_sweep()
+        return
+    if args.calibration:
+        calibration()
         return
     sections = [] if args.sections in ("", "none") else [s for s in args.sections.split(",")]
     bad = [s for s in sections if s not in SECTIONS]
@@ -762,6 +807,8 @@ def main():
         bb.copy_(a)
         torch.cuda.synchronize()
 
+    # the kernel-map rate from the SubM map alone (in the step it shares the GPU with the convolutions)
+    kmap_alone_ms = kmap_time(lambda: step.spc.build_kmap(step.coords, inp["batch"], inp["shape"], 3, orders=True), 20)
     roof = roofline("k_conv", "fwd_subm", r["flops"]["fwd_subm"], r["bytes"]["fwd_subm"], fwd_ms, dtype,
                     args.workload)
     roof["kernel_ms_back_to_back"] = round(r["kernel_ms"]["fwd_subm"], 4)
@@ -781,9 +828,10 @@ def main():
         "config": {"workload": inp["name"], "n_voxels": step.n, "pairs_subm_k3": step.P,
                    "n_out_strided": step.m, "pairs_strided": step.Ps,
                    "channels": head["channels"], "kmap_table": "hash"},
-        "kmap_voxels_per_s": head["kmap_voxels_per_s"],
+        "kmap_voxels_per_s": round(step.n / (kmap_alone_ms * 1e-3), 1),
+        "kmap_subm_ms": round(kmap_alone_ms, 4),
         "subm_fwd_ms": fwd_ms,
-        "kmap_subm_ms": head["kmap_subm_ms"],
+        "kmap_subm_ms_in_step": head["kmap_subm_ms"],
         "stages": head["stages"],
         "kernel_ms": head["kernel_ms"],
         "roofline": roof,

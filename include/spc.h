@@ -381,6 +381,19 @@ spc_status spc_gather_by_voxel_id(spc_dtype dtype, const void* seg_features, int
                                   const int32_t* pc_voxel_id, int64_t n_points, void* out,
                                   hipStream_t stream);
 
+/*
+ * Measurement support (not part of the convolution): the dense MFMA rate of
+ * this part, against which the convolutions' roofline fractions are read.
+ * Launches `blocks` workgroups of 4 waves; each wave runs independent
+ * accumulator chains of v_mfma_f32_16x16x32_bf16 (shape 0, 8 chains) or
+ * v_mfma_f32_32x32x16_bf16 (shape 1, 4 chains) for `iters` rounds on
+ * register operands, with no memory traffic in the loop.  sink: device
+ * float [blocks * 256], written once per thread.  *flop (host, NULL ok)
+ * receives the FLOP the launch executes; the caller times it on `stream`.
+ */
+spc_status spc_calibrate_mfma(int32_t shape, int32_t blocks, int32_t iters, float* sink, double* flop,
+                              hipStream_t stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* spc_last_error(void);
 

@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     SpcError,
     build_kmap,
+    calibrate_mfma,
     conv_bwd_filter,
     conv_bwd_filter_noalloc,
     conv_bwd_input,

@@ -30,8 +30,8 @@ EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_co
            "spc_conv_fwd_wt", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
            "spc_conv_bwd_filter", "spc_conv_bwd_filter_noalloc", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
-           "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_last_error",
-           "spc_version")
+           "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_calibrate_mfma",
+           "spc_last_error", "spc_version")
 
 
 class SpcError(RuntimeError):
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "spc_point_to_voxel": [_P, _I64, _I32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P,
                                ctypes.POINTER(ctypes.c_int64), _P, _SZ, _P],
         "spc_gather_by_voxel_id": [_I32, _P, _I64, _I32, _P, _I64, _P, _P],
+        "spc_calibrate_mfma": [_I32, _I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -597,3 +598,15 @@ def gather_by_voxel_id(seg_features: torch.Tensor, pc_voxel_id: torch.Tensor,
                                       _ptr(pc_voxel_id), pc_voxel_id.shape[0], _ptr(out), _stream(dev))
     _check(st, "spc_gather_by_voxel_id")
     return out
+
+
+def calibrate_mfma(shape: int, blocks: int, iters: int, sink: torch.Tensor) -> float:
+    """Launches the MFMA rate probe (spc_calibrate_mfma) on the current stream
+    and returns the FLOP it executes; the caller times it."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink needs blocks * 256 floats")
+    f = ctypes.c_double(0.0)
+    _check(lib().spc_calibrate_mfma(int(shape), int(blocks), int(iters), _ptr(sink), ctypes.byref(f),
+                                    _stream(sink.device)), "spc_calibrate_mfma")
+    return f.value

@@ -185,3 +185,10 @@ def test_noalloc_dfilter_host_checks():
     b = ctypes.c_size_t()
     assert L.spc_conv_bwd_filter_workspace(10 ** 6, 10 ** 6, 128, 128, 27, 1, ctypes.byref(b)) == B.SPC_OK
     assert b.value <= 36 << 20                                     # the named workloads' largest layer fits
+
+
+def test_calibrate_mfma_host_checks():
+    L = B.lib()
+    assert L.spc_calibrate_mfma(2, 256, 10, FAKE, None, None) == B.SPC_ERR_ARG      # shape
+    assert L.spc_calibrate_mfma(0, 0, 10, FAKE, None, None) == B.SPC_ERR_ARG        # blocks
+    assert L.spc_calibrate_mfma(1, 256, 10, None, None, None) == B.SPC_ERR_ARG      # sink
