@@ -319,3 +319,36 @@ def test_workload_fused_lidar_fp16():
     print(f"{w.name} fused n={w.n}", flush=True)
     out = spc.conv_fwd_fused(x, wt, None, km["nbr"], w.n, km["order"], residual=x, relu=True)
     assert_close(out, OC.conv_fwd_fused(w.feats, w.weight, None, nbr_ref, w.feats, True), TOL[w.dtype], "fused")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("case", ["ragged", "full_block", "sparse", "unordered"])
+def test_subm_128_channel_layers(dtype, case):
+    """128 -> 128 submanifold layers (the shell workload's shape, with weights
+    pre-transposed by the binding): forward, fused residual + ReLU and dinput
+    against the oracle, over several tiles with a ragged tail, a full block
+    (every tile hits all 27 offsets), a sparse grid (tiles of one or two
+    offsets) and rows in natural order; the forward also bit for bit against
+    the per-tile-transpose staging."""
+    r = W.rng(700 + len(case))
+    if case == "full_block":
+        c, side, batch = W.random_block(r, 12), 12, 1
+    elif case == "sparse":
+        c, side, batch = W.uniform_grid(r, 700, 40, 2), 40, 2
+    else:
+        c, side, batch = W.tiny_grid(r, 14, 0.4, 2), 14, 2
+    print(f"subm 128 channels {case} n={c.shape[0]} {dtype}", flush=True)
+    t = W.small_layer(700 + len(case), c, 128, 128, 27, dtype)
+    km = spc.build_kmap(cuda(c), batch, (side,) * 3, 3, orders=case != "unordered")
+    nbr = O.subm_kmap(c, (side,) * 3, 3)
+    order = km.get("order")
+    x, w, b, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"]), cuda(t["grad"])
+    out = spc.subm_conv_fwd(x, w, b, km["nbr"], order)
+    assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], nbr), TOL[dtype], "fwd")
+    assert torch.equal(out, spc.subm_conv_fwd(x, w, b, km["nbr"], order, pretranspose=False))
+    res = cuda(t["grad"])
+    fused = spc.conv_fwd_fused(x, w, b, km["nbr"], c.shape[0], order, residual=res, relu=True)
+    assert_close(fused, OC.conv_fwd_fused(t["feats"], t["weight"], t["bias"], nbr, t["grad"], True), TOL[dtype],
+                 "fused")
+    din = spc.conv_bwd_input(g, w, km["nbr"], True, c.shape[0], order)
+    assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], nbr, c.shape[0]), TOL[dtype], "din")
