@@ -35,7 +35,7 @@ namespace {
 constexpr uint64_t EMPTY_SLOT = ~0ull;
 constexpr int KB = 256;          // threads per block of the per-row / per-entry kernels
 constexpr int WORDS_PER_THREAD = 8;
-constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_THREADS = 256;            // small blocks (16 KB of LDS) that fit beside convolution tiles
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
