@@ -33,9 +33,17 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The MFMA rate probe keeps its accumulators in VGPRs:
+# in AGPRs the compiler moves its independent accumulator chains between
+# registers every round, and the probe would time those moves.
+SOURCE_FLAGS = {
+    "calibrate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,7 +1,9 @@
 // Measurement support: the dense MFMA issue rate of this part, for the
 // roofline the convolutions are reported against.  Each wave runs
 // independent accumulator chains of one MFMA shape on register operands (no
-// memory traffic inside the loop); the caller times the launch.
+// memory traffic inside the loop); the caller times the launch.  This file is
+// built with the accumulators in VGPRs (build.py): in AGPRs the compiler
+// shuffles the chains between registers every round.
 #include "common.h"
 
 namespace spc {
