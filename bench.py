@@ -74,7 +74,7 @@ SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "din
 KERNEL_REPS = 20         # back-to-back launches per single-kernel stage for its duration
 BUSY_FILLS = 3           # 1 GiB fills queued ahead of them (~0.5 ms of GPU time)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-SECTIONS = ("lidar_step", "train96", "uniform32_f32", "kmap_tables", "extras")
+SECTIONS = ("lidar_step", "train96", "uniform32_f32", "kmap_tables", "extras", "step_graph")
 
 
 def parse():
@@ -174,6 +174,11 @@ class Step:
         # LiDAR step gets its count earlier)
         self.strided_after_fwd = inp["name"].startswith("shells")
         self.km, self.ks = None, km  # maps held for kernel_ms (the SubM one is built on first use)
+        # the strided layer of the captured step runs over capacity-sized buffers
+        # (the map's geometric bound): its upstream gradient padded with zeros
+        self.cap = spc.strided_out_bound(self.n, inp["batch"], inp["shape"], 3, 2, 1, 1)
+        self.gs_cap = torch.zeros((self.cap, self.gs.shape[1]), dtype=self.gs.dtype, device=dev)
+        self.gs_cap[:self.m] = self.gs
 
     def fwd(self, x, w, wt, map_, n_rows, subm, order):
         spc = self.spc
@@ -279,6 +284,72 @@ class Step:
         mark("dfilter_strided", 0)
         spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"])
         mark("dfilter_strided", 1)
+
+    def run_captured(self):
+        """The step as one HIP graph captures it: the strided map leaves its
+        count M on the device (spc_build_kmap_async) and the strided layer is
+        sized by the map's capacity (spc_conv_fwd_dev_rows; dinput and dfilter
+        read only the first M rows of the capacity-sized gradient).  The maps
+        run on streams forked from the current one and joined back, as in
+        run(), so a captured graph keeps them beside the convolutions."""
+        spc, inp, torch = self.spc, self.inp, self.torch
+        if getattr(self, "cap_side", None) is None:
+            self.cap_side = (torch.cuda.Stream(), torch.cuda.Stream())
+        side_s, side_k = self.cap_side
+        main = torch.cuda.current_stream()
+        keep = []  # every intermediate stays referenced until the step is issued
+        capturing = torch.cuda.is_current_stream_capturing()
+
+        def used_on_main(maps):
+            # made on a side stream, read on main: outside a capture the memory
+            # must not be reused before main is done (a graph holds its own)
+            if not capturing:
+                for v in maps.values():
+                    if isinstance(v, torch.Tensor):
+                        v.record_stream(main)
+
+        def strided_map(after):
+            side_k.wait_event(after)
+            with torch.cuda.stream(side_k):
+                ks = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, 2, 1, 1, subm=False, orders=True,
+                                    out_cap=self.cap, device_count=True)
+            done = torch.cuda.Event()
+            done.record(side_k)
+            used_on_main(ks)
+            keep.append(ks)
+            return ks, done
+
+        start = torch.cuda.Event()
+        start.record(main)
+        side_s.wait_event(start)
+        with torch.cuda.stream(side_s):
+            km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
+        done_s = torch.cuda.Event()
+        done_s.record(side_s)
+        used_on_main(km)
+        keep.append(km)
+        if not self.strided_after_fwd:
+            ks, done_k = strided_map(done_s)
+        main.wait_event(done_s)
+        y = self.fwd(self.x, self.w3, self.w3t, km["nbr"], self.n, True, km["order"])
+        if self.strided_after_fwd:
+            issued = torch.cuda.Event()
+            issued.record(main)
+            ks, done_k = strided_map(issued)
+        keep.append(y)
+        keep.append(self.fwd(y, self.w1, self.w1t, None, self.n, False, None))
+        keep.append(spc.conv_bwd_input(self.g, self.w3, km["nbr"], True, self.n, km["order"]))
+        keep.append(spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"], km["pair_out"]))
+        main.wait_event(done_k)
+        if self.pre:
+            keep.append(spc.conv_fwd_dev_rows(self.x, self.wst, None, ks["nbr"], ks["n_out_dev"], self.cap,
+                                              ks["order"], weight_t=True))
+        else:
+            keep.append(spc.conv_fwd_dev_rows(self.x, self.ws, None, ks["nbr"], ks["n_out_dev"], self.cap,
+                                              ks["order"]))
+        keep.append(spc.conv_bwd_input(self.gs_cap, self.ws, ks["nbr_in"], False, self.n, ks["order_in"]))
+        keep.append(spc.conv_bwd_filter(self.x, self.gs_cap, 27, ks["pair_ptr"], ks["pair_in"], ks["pair_out"]))
+        return keep
 
     # effective FLOP and algorithmic HBM bytes per stage (one launch / call)
     def work(self):
@@ -476,6 +547,39 @@ def run_step(inp, dev, steps, warmup, kernel_stages=True):
     return step, dict(wall=wall, dur=dur, stages=stages, kernel_ms=kernel_ms, flops=flops, bytes=bytes_)
 
 
+def graph_step(step, steps, warmup) -> dict:
+    """The whole step captured as one HIP graph (Step.run_captured, kernel
+    maps on forked streams) and replayed K times between two HIP events,
+    against the same launches made eagerly."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the allocator on the capture stream
+        for _ in range(max(warmup, 1)):
+            step.run_captured()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        held = step.run_captured()  # noqa: F841 (the graph's buffers)
+    out = {}
+    for name, call in (("graph", graph.replay), ("eager", step.run_captured)):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        a, b = event_pair()
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        out[f"{name}_ms_per_step"] = round(a.elapsed_time(b) / steps, 4)
+        out[f"{name}_host_ms_per_step"] = round(wall * 1e3 / steps, 4)
+    return out
+
+
 def step_summary(inp, step, r, steps, dtype):
     fwd_ms = mean(r["dur"]["fwd_subm"])
     kmap_ms = mean(r["dur"]["kmap_subm"])
@@ -501,6 +605,7 @@ def section_lidar(dev, steps, warmup):
     dom = max(SINGLE_KERNEL_STAGES, key=lambda k: r["kernel_ms"][k])
     out["roofline"] = roofline("k_conv", dom, r["flops"][dom], r["bytes"][dom], r["kernel_ms"][dom],
                                dtype_name(inp["dtype"]), "lidar")
+    out["step_graph"] = graph_step(step, steps, warmup)
     return step, out
 
 
@@ -847,6 +952,8 @@ def main():
         out["uniform32_f32"] = section_uniform32(dev, args.steps, args.warmup)
     if "kmap_tables" in sections:
         out["kmap_tables"] = section_kmap_tables(dev)
+    if "step_graph" in sections:
+        out["step_graph"] = graph_step(step, args.steps, args.warmup)
     if "extras" in sections:
         out["extras"] = section_extras(lidar_step, dtype_name(lidar_step.x.dtype))
     if not args.no_cpu_baseline:

@@ -28,7 +28,8 @@
  *   leaving outputs untouched; spc_last_error() then describes the failure.
  *   Only the strided spc_build_kmap (for the output count) and
  *   spc_point_to_voxel (for the voxel count) wait for the GPU, once each;
- *   every other call is asynchronous.
+ *   every other call is asynchronous (spc_build_kmap_async is the kernel map
+ *   that leaves its count in device memory instead of waiting).
  * - Sizes: row counts below 2^31; channel counts multiples of 16.
  */
 #ifndef SPC_H
@@ -143,6 +144,28 @@ spc_status spc_build_kmap(const spc_geom* g, const int32_t* coords, int64_t n_in
                           int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * spc_build_kmap without any wait, for callers that capture a layer into a HIP
+ * graph or keep the host free (the strided map of spconv USAGE.md, "Sparse
+ * Convolution", whose output count only the GPU knows).  Arguments as
+ * spc_build_kmap, except:
+ *   n_out_dev  device int32 (16-byte aligned, required) that receives the
+ *              output row count in stream order: M for a strided map, n_in
+ *              for a submanifold one.  Nothing is copied to the host.
+ *   out_coords must be set for a strided map (no count-only form).
+ * Every launch reads M on the device; a map with M > out_cap holds no rows
+ * (its kernels treat the count as 0), and *n_out_dev = M tells the caller
+ * so.  Coordinate errors are reported only through coord_err (pass it).
+ * The call itself allocates nothing and issues no memset or copy: kernels
+ * only.
+ */
+spc_status spc_build_kmap_async(const spc_geom* g, const int32_t* coords, int64_t n_in,
+                                int32_t* out_coords, int64_t out_cap, int32_t* n_out_dev,
+                                int32_t* nbr, int32_t* nbr_in,
+                                int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
+                                int32_t* order, int32_t* order_in,
+                                int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Submanifold forward (the MLX page's module docstring formula):
  *   out[c] = bias + sum_k feats[nbr[c*K + k]] @ W[k]   over offsets with nbr >= 0.
  * feats [n, cin], weight [K, cin, cout], bias [cout] fp32 (NULL ok),
@@ -246,6 +269,25 @@ spc_status spc_conv_fwd_wt(spc_dtype dtype, const void* feats, int64_t n_src, in
                            const void* weight_t, int32_t K, int32_t cout, const float* bias,
                            const int32_t* map, int32_t map_is_subm, const int32_t* order, int64_t n_rows,
                            const void* residual, int32_t relu, void* out, hipStream_t stream);
+
+/*
+ * The forward over a strided map's output rows when their count is in device
+ * memory (spc_build_kmap_async's n_out_dev): the sparse convolution of spconv
+ * USAGE.md, "Sparse Convolution", out[o] = act(bias + residual[o] +
+ * sum_k feats[map[o*K + k]] @ W[k]).  The grid covers row_cap rows (the map's
+ * out_cap); rows at or past *n_rows_dev are not written, and a count above
+ * row_cap (an overflowed map) writes nothing.  weight_t = 0: weight
+ * [K, cin, cout] as spc_sparse_conv_fwd takes it; weight_t != 0: weight
+ * [K, cout, cin] from spc_transpose_weight, as spc_conv_fwd_wt.  feats
+ * [n_src, cin], map [row_cap, K], order (NULL ok) [row_cap], residual (NULL
+ * ok; may be out) and out [row_cap, cout]; results equal spc_conv_fwd_fused /
+ * spc_conv_fwd_wt with n_rows = M bit for bit.  Errors as spc_conv_fwd_fused.
+ */
+spc_status spc_conv_fwd_dev_rows(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                                 const void* weight, int32_t weight_t, int32_t K, int32_t cout,
+                                 const float* bias, const int32_t* map, const int32_t* order,
+                                 int64_t row_cap, const int32_t* n_rows_dev, const void* residual,
+                                 int32_t relu, void* out, hipStream_t stream);
 
 /*
  * dinput (Hygon spconv-das README, "Public Interface Support": forward, dinput

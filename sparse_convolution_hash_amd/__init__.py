@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     conv_bwd_filter,
     conv_bwd_filter_noalloc,
     conv_bwd_input,
+    conv_fwd_dev_rows,
     conv_fwd_fused,
     conv_fwd_wt,
     gather_by_voxel_id,

@@ -25,9 +25,9 @@ _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _STATUS = {1: "SPC_ERR_ARG", 2: "SPC_ERR_UNSUPPORTED", 3: "SPC_ERR_CAPACITY", 4: "SPC_ERR_COORD",
            5: "SPC_ERR_WORKSPACE", 6: "SPC_ERR_HIP"}
 
-EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_subm_conv_fwd",
+EXPORTS = ("spc_out_shape", "spc_kmap_workspace", "spc_build_kmap", "spc_build_kmap_async", "spc_subm_conv_fwd",
            "spc_sparse_conv_fwd", "spc_sparse_inverse_conv_fwd", "spc_conv_fwd_fused", "spc_transpose_weight",
-           "spc_conv_fwd_wt", "spc_conv_bwd_input",
+           "spc_conv_fwd_wt", "spc_conv_fwd_dev_rows", "spc_conv_bwd_input",
            "spc_conv_bwd_filter_workspace",
            "spc_conv_bwd_filter", "spc_conv_bwd_filter_noalloc", "spc_sparse_maxpool_fwd", "spc_sparse_maxpool_bwd",
            "spc_point_to_voxel_workspace", "spc_point_to_voxel", "spc_gather_by_voxel_id", "spc_calibrate_mfma",
@@ -83,12 +83,15 @@ def lib() -> ctypes.CDLL:
         "spc_kmap_workspace": [GP, _I64, ctypes.POINTER(_SZ)],
         "spc_build_kmap": [GP, _P, _I64, _P, _I64, ctypes.POINTER(_I64), _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
                            _SZ, _P],
+        "spc_build_kmap_async": [GP, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P],
         "spc_subm_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P],
         "spc_sparse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_sparse_inverse_conv_fwd": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P],
         "spc_conv_fwd_fused": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P],
         "spc_transpose_weight": [_I32, _P, _I32, _I32, _I32, _P, _P],
         "spc_conv_fwd_wt": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I64, _P, _I32, _P, _P],
+        "spc_conv_fwd_dev_rows": [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P, _I32, _P,
+                                  _P],
         "spc_conv_bwd_input": [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _I64, _P, _P],
         "spc_conv_bwd_filter_workspace": [_I64, _I64, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
         "spc_conv_bwd_filter": [_I32, _P, _I64, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -190,7 +193,7 @@ def strided_out_bound(n_in: int, batch: int, shape, ksize, stride=1, pad=0, dil=
 def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, stride=1, pad=0, dil=1,
                subm: bool = True, pairs: bool = True, with_nbr_in: bool = True, orders: bool = False,
                out_cap: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-               table: str = "hash", count_first: bool = False) -> dict:
+               table: str = "hash", count_first: bool = False, device_count: bool = False) -> dict:
     """Kernel map of int32 [N, 4] (b, z, y, x) coordinates (spc_build_kmap).
 
     Returns a dict with ``nbr`` [n_out, K] (submanifold neighbour map or the
@@ -205,6 +208,13 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     calls).  ``table`` picks the input table: ``"hash"`` (default) or
     ``"grid"`` (occupancy bitmap + index grid over the whole input grid, 4.125
     bytes of workspace per cell); the results are the same.
+
+    ``device_count`` calls spc_build_kmap_async instead, which never waits:
+    the result then holds ``n_out_dev`` (device int32 [1], the row count M in
+    stream order), ``n_cap`` (the row capacity, out_cap or the bound) and
+    ``n_out`` = None; ``nbr``, ``out_coords`` and ``order`` span n_cap rows,
+    of which the first M are valid.  Bad coordinates then show only in
+    ``coord_err``, and M > n_cap means the map holds no rows.
     """
     _need(coords, "coords", torch.int32)
     if coords.dim() != 2 or coords.shape[1] != 4:
@@ -218,6 +228,8 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     n_out = ctypes.c_int64(0)
     if not subm and out_cap is None and not count_first:
         out_cap = strided_out_bound(n, batch, shape, ksize, stride, pad, dil)
+    if device_count and out_cap is None and not subm:
+        raise ValueError("device_count needs out_cap (count_first waits for the count)")
     if not subm and out_cap is None:
         ws = workspace if workspace is not None and workspace.numel() >= ws_bytes else \
             torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -231,6 +243,8 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
     # and the workspace in a second one, which the results do not keep alive;
     # the library gets raw addresses, and the result views are made afterwards
     parts = [("err", 4), ("nbr", max(K * cap, 4))]
+    if device_count:
+        parts.append(("nout", 4))
     if not subm:
         parts.append(("out_coords", max(cap, 1) * 4))
     want_nbr_in = not subm and (with_nbr_in or orders)
@@ -253,13 +267,23 @@ def build_kmap(coords: torch.Tensor, batch: int, shape: Sequence[int], ksize, st
         addr[name] = base + 4 * o
         o += sizes[2 * i] + sizes[2 * i + 1]
     a = addr.get
-    st = lib().spc_build_kmap(ctypes.byref(g), coords.data_ptr(), n, a("out_coords"), cap, ctypes.byref(n_out),
-                              a("nbr"), a("nbr_in"), a("pp"), a("pi"), a("po"), max(K * n, 0) if pairs else 0,
-                              a("order"), a("order_in"), a("err"), workspace.data_ptr(), workspace.numel(), stream)
-    _check(st, "spc_build_kmap")
-    m = int(n_out.value)
+    if device_count:
+        st = lib().spc_build_kmap_async(ctypes.byref(g), coords.data_ptr(), n, a("out_coords"), cap, a("nout"),
+                                        a("nbr"), a("nbr_in"), a("pp"), a("pi"), a("po"),
+                                        max(K * n, 0) if pairs else 0, a("order"), a("order_in"), a("err"),
+                                        workspace.data_ptr(), workspace.numel(), stream)
+        _check(st, "spc_build_kmap_async")
+        m = cap
+    else:
+        st = lib().spc_build_kmap(ctypes.byref(g), coords.data_ptr(), n, a("out_coords"), cap, ctypes.byref(n_out),
+                                  a("nbr"), a("nbr_in"), a("pp"), a("pi"), a("po"), max(K * n, 0) if pairs else 0,
+                                  a("order"), a("order_in"), a("err"), workspace.data_ptr(), workspace.numel(), stream)
+        _check(st, "spc_build_kmap")
+        m = int(n_out.value)
     views = dict(zip((name for name, _ in parts), buf.split_with_sizes(sizes)[0::2]))
-    res = {"coord_err": views["err"][:1], "n_out": m, "nbr": views["nbr"][:K * m].view(m, K)}
+    res = {"coord_err": views["err"][:1], "n_out": None if device_count else m, "nbr": views["nbr"][:K * m].view(m, K)}
+    if device_count:
+        res["n_out_dev"], res["n_cap"] = views["nout"][:1], cap
     if not subm:
         res["out_coords"] = views["out_coords"][:4 * m].view(m, 4)
     if want_nbr_in:
@@ -336,6 +360,37 @@ def conv_fwd_wt(feats: torch.Tensor, weight_t: torch.Tensor, bias: Optional[torc
                                _ptr(bias), _ptr(map_), 1 if map_is_subm else 0, _ptr(order), int(n_rows),
                                _ptr(residual), 1 if relu else 0, _ptr(out), _stream(dev))
     _check(st, "spc_conv_fwd_wt")
+    return out
+
+
+def conv_fwd_dev_rows(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                      map_: torch.Tensor, n_rows_dev: torch.Tensor, row_cap: int,
+                      order: Optional[torch.Tensor] = None, weight_t: bool = False,
+                      residual: Optional[torch.Tensor] = None, relu: bool = False,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward over the rows of a strided map built with device_count
+    (spc_conv_fwd_dev_rows): out [row_cap, Cout], of which the first
+    n_rows_dev rows are written.  ``weight`` is [K, Cin, Cout], or [K, Cout,
+    Cin] from transpose_weight when ``weight_t``."""
+    dev = feats.device
+    _conv_checks(feats, weight, bias, dev)
+    _need(map_, "map", torch.int32, dev)
+    _need(n_rows_dev, "n_rows_dev", torch.int32, dev)
+    if order is not None:
+        _need(order, "order", torch.int32, dev)
+    K = weight.shape[0]
+    cin, cout = (weight.shape[2], weight.shape[1]) if weight_t else (weight.shape[1], weight.shape[2])
+    if residual is not None:
+        _need(residual, "residual", feats.dtype, dev)
+        if tuple(residual.shape) != (row_cap, cout):
+            raise ValueError(f"residual must be [{row_cap}, {cout}], got {tuple(residual.shape)}")
+    if out is None:
+        out = torch.empty((row_cap, cout), dtype=feats.dtype, device=dev)
+    st = lib().spc_conv_fwd_dev_rows(_DTYPES[feats.dtype], _ptr(feats), feats.shape[0], cin, _ptr(weight),
+                                     1 if weight_t else 0, K, cout, _ptr(bias), _ptr(map_), _ptr(order),
+                                     int(row_cap), _ptr(n_rows_dev), _ptr(residual), 1 if relu else 0, _ptr(out),
+                                     _stream(dev))
+    _check(st, "spc_conv_fwd_dev_rows")
     return out
 
 

@@ -178,3 +178,25 @@ extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int6
     a.dense = map_is_subm && !identity;
     return run_conv(dtype, a, false, stream);
 }
+
+extern "C" spc_status spc_conv_fwd_dev_rows(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
+                                            const void* weight, int32_t weight_t, int32_t K, int32_t cout,
+                                            const float* bias, const int32_t* map, const int32_t* order,
+                                            int64_t row_cap, const int32_t* n_rows_dev, const void* residual,
+                                            int32_t relu, void* out, hipStream_t stream) {
+    clear_error();
+    if (!n_rows_dev) return fail(SPC_ERR_ARG, "n_rows_dev is NULL");
+    spc_status st = check_common(dtype, row_cap, n_src, cin, cout, K, feats, weight, bias, out, map, order, true);
+    if (st != SPC_OK) return st;
+    if (!aligned16(n_rows_dev) || (residual && !aligned16(residual)))
+        return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
+    // the forward over a strided map's output rows, whose count the map wrote
+    // to n_rows_dev: W as it is (the spc_sparse_conv_fwd staging) or
+    // pre-transposed by spc_transpose_weight (the spc_conv_fwd_wt staging)
+    ConvArgs a = weight_t ? ConvArgs{feats, weight, bias, map, order, out, int32_t(row_cap), int32_t(n_src), K, cin,
+                                     cout, cout, cin, 0, 0, residual, relu ? 1 : 0}
+                          : ConvArgs{feats, weight, bias, map, order, out, int32_t(row_cap), int32_t(n_src), K, cin,
+                                     cout, cin, cout, 0, 0, residual, relu ? 1 : 0};
+    a.n_rows_dev = n_rows_dev;
+    return run_conv(dtype, a, !weight_t, stream);
+}

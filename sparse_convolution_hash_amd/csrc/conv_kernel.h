@@ -48,6 +48,7 @@ struct ConvArgs {
     int32_t relu;        // ReLU on the final fp32 value
     int32_t xbuf;        // x and the weights lie within 2 GiB (buffer loads can address them)
     int32_t dense;       // a submanifold map: tiles hit many offsets each
+    const int32_t* n_rows_dev;  // live row count in device memory (n_rows is then the capacity), or NULL
 };
 
 // Launch of the convolution for one storage type: trans selects the forward's
@@ -344,7 +345,20 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // tiles run last-first: in a processing order sorted by neighbour mask
     // the tiles with the most offsets come last, and starting them first
     // keeps them off the end of the launch
-    const int row0 = (gridDim.x - 1 - blockIdx.x) * BM, col0 = blockIdx.y * BN;
+    const int col0 = blockIdx.y * BN;
+    // rows whose count is in device memory (a strided map built without a
+    // host wait): the grid covers the capacity a.n_rows; the first blocks
+    // take the live tiles (last-first, as below) and the rest leave at once,
+    // after them; a count above the capacity (a map that overflowed and holds
+    // no rows) reads as 0
+    int n_rows = a.n_rows, tiles = int(gridDim.x);
+    if (a.n_rows_dev) {
+        const int m = *a.n_rows_dev;
+        n_rows = m >= 0 && m <= a.n_rows ? m : 0;
+        tiles = (n_rows + BM - 1) / BM;
+        if (int(blockIdx.x) >= tiles) return;  // uniform per workgroup, before any barrier
+    }
+    const int row0 = (tiles - 1 - int(blockIdx.x)) * BM;
     // MFMA steps along CK: the exact variants (KCMAX <= 4) are launched for
     // KC == KCMAX only, so their step loops carry no run-time bound (a branch
     // there would split the loop into one scheduling region per step)
@@ -357,9 +371,9 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // source row of tile row r, or -1
     if (threadIdx.x < BM) {
         const int row = row0 + threadIdx.x;
-        const int rc = row < a.n_rows ? row : a.n_rows - 1;
+        const int rc = row < n_rows ? row : n_rows - 1;
         const int32_t s0 = a.order ? a.order[rc] : rc;
-        rsrc[threadIdx.x] = row < a.n_rows && (unsigned)s0 < (unsigned)a.n_rows ? s0 : -1;
+        rsrc[threadIdx.x] = row < n_rows && (unsigned)s0 < (unsigned)n_rows ? s0 : -1;
     }
 
     f32x4_t acc[RB][NB];

@@ -348,6 +348,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_scan(int32_t* __restrict__ dat
     if (total_out && threadIdx.x == 0) total_out[blockIdx.x] = uint32_t(carry);
 }
 
+// The output row count into the caller's device word, for the form of the
+// call that does not wait: the strided count as the map kernels read it
+// (hdr), or a known count (SubM: the input rows).
+__global__ void k_publish_count(const uint32_t* hdr, int32_t known, int32_t* n_out_dev) {
+    if (threadIdx.x == 0) n_out_dev[0] = hdr ? int32_t(hdr[H_NOUT]) : known;
+}
+
 // Writes each word's exclusive rank prefix and the output coordinates of
 // its set bits, in (b, z, y, x) order (coordinates only if M <= cap).  The
 // block's first rank is block_offs[block] when `scanned`, else the sum of
@@ -1024,6 +1031,19 @@ struct HostCount {
     uint32_t* words = nullptr;
 };
 
+// The row count of a call whose count the host knows (SubM: the input rows):
+// to the host word, or, for the call that does not wait, to the device word.
+spc_status publish_known(int64_t n, int64_t* n_out, int32_t* n_out_dev, hipStream_t stream) {
+    if (!n_out_dev) {
+        *n_out = n;
+        return SPC_OK;
+    }
+    hipLaunchKernelGGL(k_publish_count, dim3(1), dim3(WAVE), 0, stream, static_cast<const uint32_t*>(nullptr),
+                       int32_t(n), n_out_dev);
+    SPC_LAUNCHED("k_publish_count");
+    return SPC_OK;
+}
+
 spc_status host_count_for_device(HostCount** out) {
     static thread_local HostCount hcs[64];
     int dev = 0;
@@ -1093,19 +1113,24 @@ extern "C" spc_status spc_kmap_workspace(const spc_geom* g, int64_t n_in, size_t
     return SPC_OK;
 }
 
-extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in,
-                                     int32_t* out_coords, int64_t out_cap, int64_t* n_out,
-                                     int32_t* nbr, int32_t* nbr_in,
-                                     int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
-                                     int32_t* order, int32_t* order_in,
-                                     int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream) {
-    clear_error();
+namespace spc {
+namespace {
+
+// spc_build_kmap (n_out on the host: the strided form waits for its count)
+// and spc_build_kmap_async (n_out_dev in device memory: nothing waits).
+spc_status build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in, int32_t* out_coords, int64_t out_cap,
+                      int64_t* n_out, int32_t* n_out_dev, int32_t* nbr, int32_t* nbr_in, int32_t* pair_ptr,
+                      int32_t* pair_in, int32_t* pair_out, int64_t pair_cap, int32_t* order, int32_t* order_in,
+                      int32_t* coord_err, void* ws, size_t ws_bytes, hipStream_t stream) {
     Plan p;
     spc_status st = make_plan(gp, n_in, p);
     if (st != SPC_OK) return st;
     const bool subm = gp->subm != 0;
+    const bool wait = n_out_dev == nullptr;
     const bool strided_count_only = !subm && out_coords == nullptr;
-    if (!n_out) return fail(SPC_ERR_ARG, "n_out is NULL");
+    if (wait && !n_out) return fail(SPC_ERR_ARG, "n_out is NULL");
+    if (!wait && strided_count_only) return fail(SPC_ERR_ARG, "the call that does not wait needs out_coords");
+    if (!wait && !aligned16(n_out_dev)) return fail(SPC_ERR_ARG, "device pointers must be 16-byte aligned");
     if (n_in > 0 && !coords) return fail(SPC_ERR_ARG, "coords is NULL");
     if (!ws) return fail(SPC_ERR_ARG, "workspace is NULL");
     if (ws_bytes < p.total) return fail(SPC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
@@ -1180,8 +1205,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             st = sort_rows(p, nbr, n, n, n, s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }
-        *n_out = n_in;
-        return SPC_OK;
+        return publish_known(n_in, n_out, n_out_dev, stream);
     }
     if (subm) {
         hipLaunchKernelGGL(k_subm_probe, dim3(unsigned(std::max<int64_t>(ceil_div(entries, KB), 1))), dim3(KB), 0,
@@ -1200,8 +1224,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             st = sort_rows(p, nbr, n, n, n, s, true, 0, order, stream);
             if (st != SPC_OK) return st;
         }
-        *n_out = n_in;
-        return SPC_OK;
+        return publish_known(n_in, n_out, n_out_dev, stream);
     }
 
     // strided: output sites into the bitmap, then count them (total -> hdr,
@@ -1219,9 +1242,14 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     // M and the flags are final here: their copy goes first, and the host waits
     // for it alone once everything else is enqueued
     HostCount* hc = nullptr;
-    if ((st = host_count_for_device(&hc)) != SPC_OK) return st;
-    SPC_HIP(hipMemcpyAsync(hc->words, s.hdr, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
-    SPC_HIP(hipEventRecord(hc->ev, stream));
+    if (wait) {
+        if ((st = host_count_for_device(&hc)) != SPC_OK) return st;
+        SPC_HIP(hipMemcpyAsync(hc->words, s.hdr, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
+        SPC_HIP(hipEventRecord(hc->ev, stream));
+    } else {
+        hipLaunchKernelGGL(k_publish_count, dim3(1), dim3(WAVE), 0, stream, s.hdr, 0, n_out_dev);
+        SPC_LAUNCHED("k_publish_count");
+    }
     if (!strided_count_only) {
         // Everything after the count is sized by the caller's capacity and reads
         // M on the device (a count above the capacity reads as 0), so nothing
@@ -1284,6 +1312,7 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
             if (st != SPC_OK) return st;
         }
     }
+    if (!wait) return SPC_OK;  // flags reach coord_err through the row kernels; the count is on the device
     SPC_HIP(hipEventSynchronize(hc->ev));
     const uint32_t host_hdr[2] = {hc->words[H_FLAGS], hc->words[H_NOUT]};
     const int64_t M = host_hdr[H_NOUT];
@@ -1295,4 +1324,28 @@ extern "C" spc_status spc_build_kmap(const spc_geom* gp, const int32_t* coords, 
     if (!strided_count_only && M > out_cap)
         return fail(SPC_ERR_CAPACITY, "%lld output sites exceed out_cap=%lld", (long long)M, (long long)out_cap);
     return SPC_OK;
+}
+
+}  // namespace
+}  // namespace spc
+
+extern "C" spc_status spc_build_kmap(const spc_geom* g, const int32_t* coords, int64_t n_in, int32_t* out_coords,
+                                     int64_t out_cap, int64_t* n_out, int32_t* nbr, int32_t* nbr_in,
+                                     int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out, int64_t pair_cap,
+                                     int32_t* order, int32_t* order_in, int32_t* coord_err, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    return build_kmap(g, coords, n_in, out_coords, out_cap, n_out, nullptr, nbr, nbr_in, pair_ptr, pair_in, pair_out,
+                      pair_cap, order, order_in, coord_err, ws, ws_bytes, stream);
+}
+
+extern "C" spc_status spc_build_kmap_async(const spc_geom* g, const int32_t* coords, int64_t n_in,
+                                           int32_t* out_coords, int64_t out_cap, int32_t* n_out_dev, int32_t* nbr,
+                                           int32_t* nbr_in, int32_t* pair_ptr, int32_t* pair_in, int32_t* pair_out,
+                                           int64_t pair_cap, int32_t* order, int32_t* order_in, int32_t* coord_err,
+                                           void* ws, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    if (!n_out_dev) return fail(SPC_ERR_ARG, "n_out_dev is NULL");
+    return build_kmap(g, coords, n_in, out_coords, out_cap, nullptr, n_out_dev, nbr, nbr_in, pair_ptr, pair_in,
+                      pair_out, pair_cap, order, order_in, coord_err, ws, ws_bytes, stream);
 }

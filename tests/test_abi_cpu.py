@@ -192,3 +192,24 @@ def test_calibrate_mfma_host_checks():
     assert L.spc_calibrate_mfma(2, 256, 10, FAKE, None, None) == B.SPC_ERR_ARG      # shape
     assert L.spc_calibrate_mfma(0, 0, 10, FAKE, None, None) == B.SPC_ERR_ARG        # blocks
     assert L.spc_calibrate_mfma(1, 256, 10, None, None, None) == B.SPC_ERR_ARG      # sink
+
+
+def test_async_kmap_and_dev_rows_host_checks():
+    # the forms that leave the row count in device memory check their extra
+    # arguments before any HIP call
+    L = B.lib()
+    g = B.make_geom(2, (41, 1600, 1408), 3, 2, 1, 1, subm=False)
+    call = lambda out_coords=FAKE, n_out_dev=FAKE, ws=FAKE: L.spc_build_kmap_async(
+        ctypes.byref(g), FAKE, 1000, out_coords, 8000, n_out_dev, FAKE, None, None, None, None, 0, None, None,
+        FAKE, ws, 1 << 20, None)
+    assert call(n_out_dev=None) == B.SPC_ERR_ARG
+    assert "n_out_dev" in L.spc_last_error().decode()
+    assert call(out_coords=None) == B.SPC_ERR_ARG                   # no count-only form
+    assert call(n_out_dev=MISALIGNED) == B.SPC_ERR_ARG
+    assert call(ws=FAKE) == B.SPC_ERR_WORKSPACE                     # 1 MiB is short of this map's workspace
+    fwd = lambda n_rows_dev=FAKE, cin=64, cap=100: L.spc_conv_fwd_dev_rows(
+        1, FAKE, 100, cin, FAKE, 0, 27, 64, None, FAKE, None, cap, n_rows_dev, None, 0, FAKE, None)
+    assert fwd(n_rows_dev=None) == B.SPC_ERR_ARG
+    assert fwd(n_rows_dev=MISALIGNED) == B.SPC_ERR_ARG
+    assert fwd(cin=24) == B.SPC_ERR_UNSUPPORTED
+    assert fwd(cap=-1) == B.SPC_ERR_ARG

@@ -352,3 +352,43 @@ def test_subm_128_channel_layers(dtype, case):
                  "fused")
     din = spc.conv_bwd_input(g, w, km["nbr"], True, c.shape[0], order)
     assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], nbr, c.shape[0]), TOL[dtype], "din")
+
+
+@pytest.mark.parametrize("dtype,cin,cout", [(torch.float16, 64, 128), (torch.bfloat16, 128, 64),
+                                            (torch.float32, 32, 48)])
+def test_dev_rows_forward_equals_the_host_rows_forward(dtype, cin, cout):
+    # the strided forward over a map that left its count on the device
+    # (grid sized by the capacity, rows past M untouched) gives the host-row
+    # forward's rows bit for bit, in both weight layouts and with the fused
+    # residual + ReLU epilogue; the host-row forward is checked against the
+    # oracle by the strided workload tests
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    c = cuda(w.coords)
+    cap = spc.strided_out_bound(w.n, w.batch, w.shape, 3, 2, 1, 1)
+    km = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
+    ka = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True, out_cap=cap, device_count=True)
+    M = km["n_out"]
+    assert int(ka["n_out_dev"].item()) == M
+    t = W.small_layer(310 + cin, w.coords, cin, cout, 27, dtype)
+    x, wt = cuda(t["feats"]), cuda(t["weight"])
+    bias = cuda(t["bias"]) if t["bias"] is not None else None
+    res = cuda(W.grad_for(W.rng(311), cap, cout, dtype))
+    wT = spc.transpose_weight(wt)
+    sentinel = torch.full((cap, cout), 3.0, dtype=dtype, device=x.device)
+    print(f"dev-rows forward {dtype} {cin}->{cout} M={M} cap={cap}", flush=True)
+    ref = spc.sparse_conv_fwd(x, wt, bias, km["nbr"], M, km["order"], pretranspose=False)
+    ref_t = spc.conv_fwd_wt(x, wT, bias, km["nbr"], M, False, km["order"])
+    ref_f = spc.conv_fwd_fused(x, wt, bias, km["nbr"], M, km["order"], residual=res[:M].contiguous(), relu=True,
+                               pretranspose=False)
+    for weight_t, wgt, want, kw in ((False, wt, ref, {}), (True, wT, ref_t, {}),
+                                    (False, wt, ref_f, {"residual": res, "relu": True})):
+        out = sentinel.clone()
+        spc.conv_fwd_dev_rows(x, wgt, bias, ka["nbr"], ka["n_out_dev"], cap, ka["order"], weight_t=weight_t,
+                              out=out, **kw)
+        assert torch.equal(out[:M], want), (weight_t, kw)
+        assert torch.equal(out[M:], sentinel[M:]), "rows past the count were written"
+    # a count above the capacity (an overflowed map) writes nothing
+    over = torch.full((4,), cap + 1, dtype=torch.int32, device=x.device)
+    out = sentinel.clone()
+    spc.conv_fwd_dev_rows(x, wt, bias, ka["nbr"], over[:1], cap, ka["order"], out=out)
+    assert torch.equal(out, sentinel)

@@ -245,3 +245,55 @@ def test_hash_at_four_lidar_samples():
     shape = (41, 1600, 1408)
     check_subm(c, 4, shape, 3, tables=("hash",))
     check_strided(c, 4, shape, 3, 2, 1, 1, tables=("hash",))
+
+
+def _async_equals_waiting(c, batch, shape, k, s, p, d, cap, subm=False):
+    """The map that leaves its count on the device equals the waiting map."""
+    ref = spc.build_kmap(c, batch, shape, k, s, p, d, subm=subm, out_cap=None if subm else cap, orders=True)
+    got = spc.build_kmap(c, batch, shape, k, s, p, d, subm=subm, out_cap=None if subm else cap, orders=True,
+                         device_count=True)
+    M = ref["n_out"]
+    assert got["n_out"] is None and got["n_cap"] == (c.shape[0] if subm else cap)
+    assert int(got["n_out_dev"].item()) == M
+    assert int(got["coord_err"].item()) == 0
+    keys = ["nbr", "order", "pair_ptr"] + ([] if subm else ["out_coords", "nbr_in", "order_in"])
+    for key in keys:
+        a = got[key][:M] if key in ("nbr", "order", "out_coords") else got[key]
+        assert torch.equal(a, ref[key]), key
+    P = int(ref["pair_ptr"][-1])
+    assert torch.equal(got["pair_in"][:P], ref["pair_in"][:P]) and torch.equal(got["pair_out"][:P], ref["pair_out"][:P])
+    return got, M
+
+
+def test_async_map_equals_the_waiting_map():
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    c = cuda(w.coords)
+    bound = spc.strided_out_bound(c.shape[0], w.batch, w.shape, 3, 2, 1, 1)
+    print(f"async strided map, LiDAR scene, capacity {bound}", flush=True)
+    _async_equals_waiting(c, w.batch, w.shape, 3, 2, 1, 1, bound)
+    print("async SubM map, LiDAR scene", flush=True)
+    _async_equals_waiting(c, w.batch, w.shape, 3, 1, 1, 1, 0, subm=True)
+    # a ragged geometry: k=(3,2,3), stride (2,1,3), pad (1,0,1), dilation (1,2,1)
+    small = W.tiny_grid(W.rng(78), 11, 0.3, 2)
+    bound = spc.strided_out_bound(small.shape[0], 2, (11, 11, 11), (3, 2, 3), (2, 1, 3), (1, 0, 1), (1, 2, 1))
+    print(f"async strided map, ragged geometry, n={small.shape[0]}", flush=True)
+    _async_equals_waiting(cuda(small), 2, (11, 11, 11), (3, 2, 3), (2, 1, 3), (1, 0, 1), (1, 2, 1), bound)
+
+
+def test_async_map_capacity_overflow_and_bad_coordinates():
+    # a capacity below M: the count still reaches the device word and no row
+    # is written; bad coordinates show in coord_err only
+    w = W.workload("strided_k3s2_f16_lidar120k")
+    c = cuda(w.coords)
+    M = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, pairs=False)["n_out"]
+    print(f"async strided map with capacity {M - 1} < M = {M}", flush=True)
+    got = spc.build_kmap(c, w.batch, w.shape, 3, 2, 1, 1, subm=False, out_cap=M - 1, orders=True, device_count=True)
+    assert int(got["n_out_dev"].item()) == M
+    assert int(got["pair_ptr"][-1].item()) == 0
+    bad = np.array([[0, 1, 1, 1], [0, 1, 1, 1], [0, 9, 0, 0]], np.int32)
+    for subm in (True, False):
+        print(f"async map with bad coordinates subm={subm}", flush=True)
+        r = spc.build_kmap(cuda(bad), 1, (4, 4, 4), 3, 2, 1, 1, subm=subm, out_cap=None if subm else 64,
+                           device_count=True)
+        e = int(r["coord_err"].item())
+        assert e & spc.binding.COORD_DUPLICATE and e & spc.binding.COORD_OUT_OF_RANGE, e
