@@ -545,9 +545,16 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     __syncthreads();
     if (rows < 0) rows = rows_within(hdr, cap);
     // workgroups go to the XCDs round-robin; XCD x takes a contiguous run of
-    // row blocks, so the cells that its rows look up stay in its own L2
-    const uint32_t nb = gridDim.x, xc = blockIdx.x % 8u, per = nb / 8u;
-    const uint32_t lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
+    // row blocks, so the cells that its rows look up stay in its own L2.  The
+    // run is cut from the blocks that hold rows: in a grid sized by a
+    // capacity above M, the blocks past M's blocks keep their own index (no
+    // rows, zero counts), so that every XCD shares the rows
+    const uint32_t live_blocks = (uint32_t(rows) + KB - 1) / KB;
+    uint32_t lb = blockIdx.x;
+    if (blockIdx.x < live_blocks) {
+        const uint32_t nb = live_blocks, xc = blockIdx.x % 8u, per = nb / 8u;
+        lb = xc * per + min(xc, nb % 8u) + blockIdx.x / 8u;
+    }
     const int32_t row0 = int32_t(lb) * KB, i = row0 + t;
     if (coord_err && i == 0 && hdr[H_FLAGS]) atomicOr(coord_err, int32_t(hdr[H_FLAGS]));
     if (row0 >= rows) {  // uniform per block: a block past M (capacity above M) has no hits
