@@ -27,6 +27,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -241,9 +242,13 @@ struct WStage {
     // The same through the weights' buffer resource, without branches:
     // padding and absent items, and every item when !live, take an
     // out-of-range offset and load zeros without a memory access.
+    // NP: items loaded (at most PRE; a variant whose slab has fewer items per
+    // thread than PRE passes that count, so no load is issued for nothing)
+    template <int NP = PRE>
     __device__ void load_buf(const ConvArgs& a, __amdgpu_buffer_rsrc_t wr, int ws, bool live) {
         const uint32_t base = uint32_t(ws) * uint32_t(a.cin) * uint32_t(a.cout);
         each(a, [&](int p, int32_t g, int32_t) {
+            if (p >= NP) return;
 #pragma unroll
             for (int e = 0; e < ITEM_REGS; ++e) {
                 const uint32_t off =
@@ -251,6 +256,33 @@ struct WStage {
                 r[p * ITEM_REGS + e] = buf_ld16(wr, off);
             }
         });
+    }
+
+    // load_buf for a variant whose contraction is exactly KCH chunks (a.kch
+    // == KCH) and whose items are single chunks: item p of this thread is idx
+    // = threadIdx.x + p * CT, as in each(), but its place comes from
+    // compile-time divisors, so the loads carry no branches and can share a
+    // scheduling region with the MFMAs
+    template <int KCH, int NP>
+    __device__ void load_exact(const ConvArgs& a, __amdgpu_buffer_rsrc_t wr, int ws, bool live) {
+        static_assert(ITEM_REGS == 1, "chunk items only");
+        constexpr int N = KCH * BN;
+        const uint32_t base = uint32_t(ws) * uint32_t(a.cin) * uint32_t(a.cout);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int idx = int(threadIdx.x) + p * CT;
+            int32_t g;
+            if constexpr (ROWS) {
+                constexpr int CPR = BN / 8;
+                const int kk = idx / CPR, c = idx - kk * CPR;
+                g = kk < a.CK ? kk * a.cout + col0 + c * 8 : -1;
+            } else {
+                const int kb = idx % KCH, q = idx / KCH;
+                g = kb < a.CK / E ? (col0 + q) * a.cout + kb * E : -1;
+            }
+            const bool ok = live && idx < N && g >= 0;
+            r[p] = buf_ld16(wr, ok ? (base + uint32_t(g)) * uint32_t(sizeof(S)) : BUF_OOB);
+        }
     }
 
     __device__ void store(char* lds, const ConvArgs& a, int ws) const {
@@ -304,7 +336,8 @@ __device__ __forceinline__ bool gather_buf(u32x4 (&af)[RB][KCMAX], const ConvArg
     bool any = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int32_t src = live ? tile_k[(wave * RB + rb) * 16 + lr] : -1;
+        const int32_t v = tile_k[(wave * RB + rb) * 16 + lr];  // a valid LDS address either way
+        const int32_t src = live ? v : -1;
         any |= src >= 0;
 #pragma unroll
         for (int kc = 0; kc < KCMAX; ++kc) {
@@ -384,6 +417,12 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
     WStage<TT, BN, TRANS, ROWS> wst;
     wst.init(a, col0);
+    // slab items a thread loads per offset: fewer than the register budget
+    // PRE when an exact variant's slab is small (chunk items only)
+    using WS = WStage<TT, BN, TRANS, ROWS>;
+    constexpr int NPRE = WS::ITEM_REGS == 1 && KCMAX <= 4
+                             ? (KCMAX * 4 * BN + CT - 1) / CT < WS::PRE ? (KCMAX * 4 * BN + CT - 1) / CT : WS::PRE
+                             : WS::PRE;
     u32x4 acur[RB][KCMAX], anext[RB][KCMAX];
     // the identity map (K = 1) has one offset, whose entries are the rows
     // themselves: its column is rsrc, and nothing is staged
@@ -450,7 +489,11 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
         auto slab_of = [&](int j) { const int kg = kt0 + list[j]; return a.w_rev ? a.K - 1 - kg : kg; };
         // one offset's MFMAs: gathered rows `cur` against slab buffer j & 1
-        auto mma = [&](const u32x4 (&cur)[RB][KCMAX], int j) {
+        // nv: the number of global loads issued just before this call in the
+        // same scheduling region, which the 16-bit pattern below spreads among
+        // the MFMAs (0: none)
+        auto mma = [&](const u32x4 (&cur)[RB][KCMAX], int j, auto nv) {
+            constexpr int NV = decltype(nv)::value;
             const char* sl = lds + (j & 1) * slab_bytes;
             if constexpr (!ROWS && TT::E == 8 && KCMAX <= 4) {
                 // B fragments in (kc, nb) order, each read BLOOK fragments
@@ -479,12 +522,19 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                 {
                     // keep that order through the scheduler, which otherwise
                     // pairs each two reads with their MFMAs to save registers:
-                    // LA reads, then (RB MFMAs, one read) per fragment
-                    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+                    // LA reads, then (RB MFMAs, one read) per fragment.  With
+                    // NV loads in the region (the next offsets' slab and
+                    // gathers), one load follows every SP-th fragment's MFMAs:
+                    // a wave then issues its loads between its MFMAs instead
+                    // of stalling on the load path before the first of them
+                    // (the gathers' RB source-row reads go first)
+                    constexpr int SP = NV > 0 && NI / NV > 1 ? NI / NV : 1;
+                    __builtin_amdgcn_sched_group_barrier(0x100, NV > 0 ? LA + RB : LA, 0);
 #pragma unroll
                     for (int i = 0; i < NI; ++i) {
                         __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
                         if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        if (NV > 0 && i % SP == 0 && i / SP < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                     }
                 }
                 return;
@@ -530,12 +580,34 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.x, uint32_t(a.n_src) * uint32_t(a.CK) * uint32_t(sizeof(S)));
             const __amdgpu_buffer_rsrc_t wr =
                 buf_rsrc(a.w, uint32_t(a.K) * uint32_t(a.cin) * uint32_t(a.cout) * uint32_t(sizeof(S)));
-            auto step = [&](int j, const u32x4 (&cur)[RB][KCMAX], bool any, u32x4 (&pre)[RB][KCMAX], bool& any_pre) {
+            // The step's loads (the next slab, the gathers two offsets ahead)
+            // share one scheduling region with its MFMAs, which spread them
+            // among the MFMAs (mma); a wave without hits at this offset
+            // issues the loads alone.
+            // With chunk items (every variant except the per-tile transposing
+            // forward) the loads are branch-free.  Where the MFMA loop has the
+            // interleaving pattern (16-bit, plain slab layout) the MFMAs run
+            // for every wave, hits or not (a wave without hits multiplies
+            // zero fragments, which leaves its sums as they are), so that
+            // loads and MFMAs form one region; elsewhere a wave without hits
+            // skips its MFMAs.
+            constexpr bool MERGED = WS::ITEM_REGS == 1 && !ROWS && TT::E == 8;
+            auto loads = [&](int j, u32x4 (&pre)[RB][KCMAX], bool& any_pre) {
                 const int jn = min(j + 1, nk - 1);
-                wst.load_buf(a, wr, slab_of(jn), j + 1 < nk);
+                if constexpr (WS::ITEM_REGS == 1)
+                    wst.template load_exact<KCMAX * 4, NPRE>(a, wr, slab_of(jn), j + 1 < nk);
+                else
+                    wst.template load_buf<NPRE>(a, wr, slab_of(jn), j + 1 < nk);
                 any_pre = gather_buf<TT, RB, KCMAX>(pre, a, xr, cols + list[min(j + 2, nk - 1)] * BMP, j + 2 < nk,
                                                     wave, lr, lg);
-                if (any) mma(cur, j);
+            };
+            auto step = [&](int j, const u32x4 (&cur)[RB][KCMAX], bool any, u32x4 (&pre)[RB][KCMAX], bool& any_pre) {
+                const int jn = min(j + 1, nk - 1);
+                loads(j, pre, any_pre);
+                if constexpr (MERGED)
+                    mma(cur, j, std::integral_constant<int, NPRE + RB * KCMAX>{});
+                else if (any)
+                    mma(cur, j, std::integral_constant<int, 0>{});
                 wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(jn));
                 lds_barrier();
             };
@@ -566,7 +638,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                 wst.load(a, slab_of(j + 1));
                 any_next = gather_rows<TT, RB, KCMAX>(anext, a, cols + list[j + 1] * BMP, wave, lr, lg);
             }
-            if (any_cur) mma(acur, j);
+            if (any_cur) mma(acur, j, std::integral_constant<int, 0>{});
             if (has_next) wst.store(lds + ((j + 1) & 1) * slab_bytes, a, slab_of(j + 1));
             __syncthreads();
 #pragma unroll
