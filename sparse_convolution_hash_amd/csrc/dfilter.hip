@@ -196,7 +196,8 @@ __device__ __forceinline__ void load_idx_tr(int32_t (&r)[TT::E], const DfArgs& a
 #pragma unroll
     for (int q = 0; q < G::NQ; ++q) {
         const int64_t p = st.b + G::pair(q);
-        const int64_t pc = p < st.e ? p : st.e - 1;
+        int64_t pc = p < st.e ? p : st.e - 1;
+        pc = pc < 0 ? 0 : pc;  // a step past the end (b = e = 0) reads entry 0 and drops it
         if constexpr (IDENT)
             r[q] = int32_t(pc);
         else
@@ -287,6 +288,11 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const ItemGeo geo(has_item ? my : items - 1, xi_items, E);
     // 16-bit full tiles stage rows pair-major and read fragments transposed
     constexpr bool TR = FULL && E == 8;
+    // with accumulators of up to 2 x 2 blocks per wave the step's loads are
+    // branch-free and spread among its MFMAs (larger tiles have no registers
+    // to spare for it: the 4 x 4 one did not get faster, the 3 x 3 one lost
+    // a wave per SIMD)
+    constexpr bool SPREAD = TR && MIM <= 2 && NOM <= 2;
     auto idx_of = [&](int32_t (&r)[E], const Step& st) {
         if constexpr (TR)
             load_idx_tr<TT, IDENT, MIM, NOM>(r, a, st);
@@ -342,7 +348,14 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
             store_item<TT>(xt, gt, tmp, it, xi_items);
         }
         lds_barrier();
-        if (ahead.k >= 0) {
+        if constexpr (SPREAD) {
+            // branch-free, so that these loads share one scheduling region
+            // with the MFMAs below, which spread them among themselves (a
+            // step past the end reads clamped, valid addresses and keeps
+            // nothing: its rows' ok bits are clear)
+            rows_of(mine, use, ahead);
+            idx_of(fill, after);
+        } else if (ahead.k >= 0) {
             rows_of(mine, use, ahead);
             if (after.k >= 0) idx_of(fill, after);
         }
@@ -372,6 +385,19 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(2))) void k_
                 for (int no = 0; no < NOM; ++no)
                     if (FULL || (mi < MI && no < NO && (wi * MI + mi) * 16 < TI && (wo * NO + no) * 16 < TO))
                         acc[mi][no] = mfma16<TT>(gf[no], xf[mi], acc[mi][no]);
+        }
+        if constexpr (SPREAD) {
+            // one of the step's NV loads after every SP-th MFMA, so that a
+            // wave issues its loads between MFMAs instead of stalling on the
+            // load path before the first of them
+            constexpr int KS = PS / (4 * E), NMB = MIM * NOM, NM = NMB * KS;
+            constexpr int NV = TrGeo<MIM, NOM>::NQ * (IDENT ? 1 : 2);
+            constexpr int SP = NM / NV > 1 ? NM / NV : 1;
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i % SP == 0 && i / SP < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
         if (nxt.k != cur.k) {
             // last step of offset cur.k in this segment: D[co][ci] per 16x16
