@@ -261,9 +261,10 @@ spc_status spc_transpose_weight(spc_dtype dtype, const void* weight, int32_t K, 
  * instead of transposing them per tile, which pays for fp32 and for
  * contractions of more than 64 16-bit channels (shorter ones read W's own
  * layout with transposing LDS reads).  map_is_subm != 0 says map is a
- * submanifold nbr (n_src == n_rows), whose tiles hit many offsets: a
- * performance hint that selects the loop keeping two offsets of gathered
- * rows in flight.  Other arguments and errors as spc_conv_fwd_fused.
+ * submanifold nbr (n_src == n_rows); it changes nothing in the result or the
+ * launch (every map with K > 1 runs the loop that keeps two offsets of
+ * gathered rows in flight).  Other arguments and errors as
+ * spc_conv_fwd_fused.
  */
 spc_status spc_conv_fwd_wt(spc_dtype dtype, const void* feats, int64_t n_src, int32_t cin,
                            const void* weight_t, int32_t K, int32_t cout, const float* bias,

@@ -71,7 +71,6 @@ extern "C" spc_status spc_subm_conv_fwd(spc_dtype dtype, const void* feats, int6
     // a 1x1x1 map is the identity: skip reading it
     ConvArgs a{feats, weight, bias, K == 1 ? nullptr : nbr, K == 1 ? nullptr : order, out, int32_t(n), int32_t(n),
                K, cin, cout, cin, cout, 0, 0};
-    a.dense = K > 1;
     return run_conv(dtype, a, true, stream);
 }
 
@@ -158,7 +157,6 @@ extern "C" spc_status spc_conv_fwd_wt(spc_dtype dtype, const void* feats, int64_
     // channel, contraction-contiguous (weight dims: cout rows of cin)
     ConvArgs a{feats, weight_t, bias, identity ? nullptr : map, identity ? nullptr : order, out, int32_t(n_rows),
                int32_t(n_src), K, cin, cout, cout, cin, 0, 0, residual, relu ? 1 : 0};
-    a.dense = map_is_subm && !identity;
     return run_conv(dtype, a, false, stream);
 }
 
@@ -175,7 +173,6 @@ extern "C" spc_status spc_conv_bwd_input(spc_dtype dtype, const void* dout, int6
     // din rows gather dout rows: contraction over cout, output channels cin
     ConvArgs a{dout, weight, nullptr, map, identity ? nullptr : order, din, int32_t(n_in), int32_t(n_out), K, cout,
                cin, cin, cout, map_is_subm ? 1 : 0, 0};
-    a.dense = map_is_subm && !identity;
     return run_conv(dtype, a, false, stream);
 }
 

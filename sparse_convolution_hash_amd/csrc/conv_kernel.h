@@ -48,7 +48,6 @@ struct ConvArgs {
     const void* res;     // residual [n_rows, CN] added before the activation, or NULL (may alias y)
     int32_t relu;        // ReLU on the final fp32 value
     int32_t xbuf;        // x and the weights lie within 2 GiB (buffer loads can address them)
-    int32_t dense;       // a submanifold map: tiles hit many offsets each
     const int32_t* n_rows_dev;  // live row count in device memory (n_rows is then the capacity), or NULL
 };
 
@@ -570,9 +569,11 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
             // last offset, take out-of-range buffer offsets and load zeros
             // without a memory access; the slab staged after the last offset
             // goes to the buffer no longer read), so the compiler's wait
-            // counts stay exact.  It pays where tiles hit many offsets
-            // (submanifold maps); tiles of one or two offsets run the plain
-            // loop below, which stages nothing past the last offset.
+            // counts stay exact.  Since the step's loads share its MFMAs'
+            // scheduling region it pays on every map with more than one
+            // offset (strided and inverse maps too); the identity map of a
+            // k = 1 layer runs the plain loop below, which stages nothing
+            // past its one offset.
             // The next offset's weight slab is staged one step ahead as before
             // (its loads hit L2).
             u32x4 ga[RB][KCMAX], gb[RB][KCMAX], gc[RB][KCMAX];
@@ -735,12 +736,13 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
     const int KC = a.kch / 4;
     // gathered-row registers sized to the contraction: a 2-step variant frees
     // 32 registers per lane for contractions of up to 64 (16-bit) channels.
-    // On a submanifold map the 2- and 4-step variants keep a second offset of
-    // gathers in flight (addressing x and the weights through buffer
-    // resources, so both must lie within 2 GiB).
+    // Over any map with more than one offset the 1- to 4-step variants keep a
+    // second offset of gathers in flight (addressing x and the weights through
+    // buffer resources, so both must lie within 2 GiB); the identity map of a
+    // k = 1 layer (one offset) keeps the plain loop.
     // Up to 4 steps the variant matches KC exactly (its loops have no run-time
     // bound); 5 to 8 steps share one bounded variant.
-    const bool pipe = a.dense && a.xbuf;
+    const bool pipe = a.xbuf && a.K > 1;
     switch (KC) {
         case 1: return pipe ? launch_conv_k<TT, TRANS, 1, true>(a, stream) : launch_conv_k<TT, TRANS, 1>(a, stream);
         case 2: return pipe ? launch_conv_k<TT, TRANS, 2, true>(a, stream) : launch_conv_k<TT, TRANS, 2>(a, stream);
