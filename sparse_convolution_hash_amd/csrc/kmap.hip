@@ -813,7 +813,8 @@ struct Plan {
     // workspace offsets
     int64_t rgroups;             // radix block groups
     int64_t occ_words;           // input occupancy bitmap words (multiple of 4)
-    size_t off_table, off_occ, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, total;
+    size_t off_table, off_occ, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, off_gtot,
+        total;
     size_t sort_slot_bytes;      // per sort: keys x2, values x2, histogram matrix
 };
 
@@ -909,6 +910,7 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     p.off_sort = off;    off += 2 * p.sort_slot_bytes;                            // sort buffers, per sort
     p.rgroups = ceil_div(p.rblk, RS_GROUP);
     p.off_gsum = off;    off = align_up(off + size_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups * 4, 256);
+    p.off_gtot = off;    off = align_up(off + size_t(2 * RS_MAX_PASSES) * RS_BINS * 4, 256);     // spine totals
     p.total = off;
     return SPC_OK;
 }
@@ -932,6 +934,7 @@ struct Scratch {
     uint32_t* mask[2];           // neighbour masks of the rows, per sort slot
     SortBuf sort[2];
     int32_t* gsum;               // [2 sorts][RS_MAX_PASSES][RS_BINS][groups], zeroed by k_clear
+    int32_t* gtot;               // [2 sorts][RS_MAX_PASSES][RS_BINS] spine totals (written before read)
 };
 
 // Row pass: masks into keys (K <= 32, NULL ok) and per-block counts (NULL ok).
@@ -1009,11 +1012,20 @@ spc_status sort_orders(const Plan& p, const Scratch& s, const OrderJob* jobs, in
             const int slot = live[i]->slot;
             const SortBuf& sb = s.sort[slot];
             P.job[i].gsum = s.gsum + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS * p.rgroups;
+            // many groups (a sort sized by a large capacity): one spine launch
+            // scans them, instead of every scatter block reading them all
+            P.job[i].gtot = P.job[i].ng > RS_SPINE_GROUPS
+                                ? s.gtot + (int64_t(slot) * RS_MAX_PASSES + pass) * RS_BINS
+                                : nullptr;
             P.job[i].keys_out = sb.keys[pass & 1];
             P.job[i].vals_out = last ? live[i]->order : sb.vals[pass & 1];
         }
         hipLaunchKernelGGL(k_rs_hist, dim3(blocks), dim3(RS_THREADS), 0, stream, P);
         SPC_LAUNCHED("k_rs_hist");
+        if (P.job[0].gtot || P.job[1].gtot) {
+            hipLaunchKernelGGL(k_rs_spine, dim3(2 * RS_BINS / 4), dim3(256), 0, stream, P);
+            SPC_LAUNCHED("k_rs_spine");
+        }
         hipLaunchKernelGGL(k_rs_scatter, dim3(blocks), dim3(RS_THREADS), 0, stream, P);
         SPC_LAUNCHED("k_rs_scatter");
         for (int i = 0; i < nl; ++i) {
@@ -1168,6 +1180,7 @@ spc_status build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in, i
         sb.hist = sb.vals[1] + p.rows_max;
     }
     s.gsum = reinterpret_cast<int32_t*>(base + p.off_gsum);
+    s.gtot = reinterpret_cast<int32_t*>(base + p.off_gtot);
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
     uint32_t* occ = reinterpret_cast<uint32_t*>(base + p.off_occ);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);

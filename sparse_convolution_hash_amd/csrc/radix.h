@@ -18,6 +18,7 @@ constexpr int RS_THREADS = 512;              // threads per radix block (one per
 constexpr int RS_ITEMS = 4;                  // keys per thread in the radix passes
 constexpr int RS_TILE = RS_THREADS * RS_ITEMS;  // keys per radix block
 constexpr int RS_GROUP = 16;                 // radix blocks per group of the two-level offset sums
+constexpr int RS_SPINE_GROUPS = 64;          // above this many groups a pass scans them once (k_rs_spine)
 constexpr int RS_MAX_PASSES = 4;             // K <= 32 bits of mask, 9 bits per pass
 constexpr int RS_BITS = 9;                   // digit width of the radix passes
 constexpr int RS_BINS = 1 << RS_BITS;
@@ -35,6 +36,7 @@ struct RsJob {
     int32_t* vals_out;
     int32_t* hist;              // [RS_BINS][nb] block counts
     int32_t* gsum;              // [RS_BINS][ng] group sums, zeroed beforehand
+    int32_t* gtot;              // [RS_BINS] digit totals from k_rs_spine, or NULL (no spine)
     const uint32_t* n_dev;      // device row count when rows < 0
     int64_t cap;
     int32_t rows;
@@ -96,6 +98,43 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_hist(RsPass P) {
     if (c) atomicAdd(J.gsum + int64_t(t) * J.ng + me / RS_GROUP, c);
 }
 
+// Rows a job sorts, and its groups that hold rows (later groups' sums stay 0).
+__device__ __forceinline__ int32_t job_rows(const RsJob& J) {
+    return J.rows < 0 ? count_within(J.n_dev, J.cap) : J.rows;
+}
+__device__ __forceinline__ int live_groups(const RsJob& J, int32_t rows) {
+    return min(J.ng, int((int64_t(rows) + int64_t(RS_TILE) * RS_GROUP - 1) / (int64_t(RS_TILE) * RS_GROUP)));
+}
+
+// Pass spine, for sorts of many groups (J.gtot set): each digit's group sums
+// become exclusive prefixes in place and the digit's total goes to gtot, so a
+// scatter block reads one prefix and one total instead of every group's sum
+// (a cost that grew with the square of the rows).  One wave per digit, four
+// digits per block, RS_BINS / 4 blocks per job.
+__global__ __launch_bounds__(256) void k_rs_spine(RsPass P) {
+    constexpr int PER_JOB = RS_BINS / 4;
+    const RsJob& J = int(blockIdx.x) >= PER_JOB ? P.job[1] : P.job[0];
+    if (!J.gtot) return;  // uniform per block
+    const int d = (int(blockIdx.x) % PER_JOB) * 4 + int(threadIdx.x) / WAVE;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int ng_live = live_groups(J, job_rows(J));
+    int32_t* gs = J.gsum + int64_t(d) * J.ng;
+    int carry = 0;
+    for (int q0 = 0; q0 < ng_live; q0 += WAVE) {
+        const int q = q0 + lane;
+        const int v = q < ng_live ? gs[q] : 0;
+        int x = v;  // inclusive scan over the wave
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (q < ng_live) gs[q] = carry + x - v;
+        carry += __shfl(x, WAVE - 1);
+    }
+    if (lane == 0) J.gtot[d] = carry;
+}
+
 // Pass scatter, stable.  Slot base of digit d for this block: keys of
 // smaller digits, plus digit-d keys of earlier groups (group sums) and of
 // earlier blocks of this group (histogram columns); each wave adds the
@@ -134,8 +173,12 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(RsPass P) {
 #pragma unroll
         for (int r = 0; r < RS_ITEMS; ++r) vr[r] = tile0 + r * RS_THREADS + t;
     }
-    // digit t: totals over the groups and the part before this block
+    // digit t: totals over the groups and the part before this block.  Only
+    // the groups that hold rows have sums (blocks past the rows add nothing
+    // to their zeroed sums), so a sort sized by a capacity far above its
+    // rows reads just those
     const int g_me = me / RS_GROUP, b0 = g_me * RS_GROUP;
+    const int ng_live = live_groups(J, rows);
     int tot = 0, before = 0;
     {
         const int32_t* gs = gsum + int64_t(t) * ng;
@@ -143,13 +186,17 @@ __global__ __launch_bounds__(RS_THREADS) void k_rs_scatter(RsPass P) {
         int hv[RS_GROUP];
 #pragma unroll
         for (int u = 0; u < RS_GROUP; ++u) hv[u] = ld_clamped(hc, b0 + u, int64_t(me) + 1);
-        for (int q0 = 0; q0 < ng; q0 += RS_GROUP) {
+        if (J.gtot) {  // the spine's prefixes (uniform per block)
+            tot = J.gtot[t];
+            before = gs[g_me];
+        }
+        for (int q0 = 0; !J.gtot && q0 < ng_live; q0 += RS_GROUP) {
             int v[RS_GROUP];
 #pragma unroll
-            for (int u = 0; u < RS_GROUP; ++u) v[u] = ld_clamped(gs, q0 + u, ng);
+            for (int u = 0; u < RS_GROUP; ++u) v[u] = ld_clamped(gs, q0 + u, ng_live);
 #pragma unroll
             for (int u = 0; u < RS_GROUP; ++u) {
-                tot += q0 + u < ng ? v[u] : 0;
+                tot += q0 + u < ng_live ? v[u] : 0;
                 before += q0 + u < g_me ? v[u] : 0;
             }
         }
