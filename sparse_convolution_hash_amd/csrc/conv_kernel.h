@@ -241,13 +241,9 @@ struct WStage {
     // The same through the weights' buffer resource, without branches:
     // padding and absent items, and every item when !live, take an
     // out-of-range offset and load zeros without a memory access.
-    // NP: items loaded (at most PRE; a variant whose slab has fewer items per
-    // thread than PRE passes that count, so no load is issued for nothing)
-    template <int NP = PRE>
     __device__ void load_buf(const ConvArgs& a, __amdgpu_buffer_rsrc_t wr, int ws, bool live) {
         const uint32_t base = uint32_t(ws) * uint32_t(a.cin) * uint32_t(a.cout);
         each(a, [&](int p, int32_t g, int32_t) {
-            if (p >= NP) return;
 #pragma unroll
             for (int e = 0; e < ITEM_REGS; ++e) {
                 const uint32_t off =
@@ -416,8 +412,8 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
     WStage<TT, BN, TRANS, ROWS> wst;
     wst.init(a, col0);
-    // slab items a thread loads per offset: fewer than the register budget
-    // PRE when an exact variant's slab is small (chunk items only)
+    // slab items a thread loads per offset through load_exact: fewer than the
+    // register budget PRE when an exact variant's slab is small (chunk items)
     using WS = WStage<TT, BN, TRANS, ROWS>;
     constexpr int NPRE = WS::ITEM_REGS == 1 && KCMAX <= 4
                              ? (KCMAX * 4 * BN + CT - 1) / CT < WS::PRE ? (KCMAX * 4 * BN + CT - 1) / CT : WS::PRE
@@ -598,7 +594,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
                 if constexpr (WS::ITEM_REGS == 1)
                     wst.template load_exact<KCMAX * 4, NPRE>(a, wr, slab_of(jn), j + 1 < nk);
                 else
-                    wst.template load_buf<NPRE>(a, wr, slab_of(jn), j + 1 < nk);
+                    wst.load_buf(a, wr, slab_of(jn), j + 1 < nk);
                 any_pre = gather_buf<TT, RB, KCMAX>(pre, a, xr, cols + list[min(j + 2, nk - 1)] * BMP, j + 2 < nk,
                                                     wave, lr, lg);
             };
