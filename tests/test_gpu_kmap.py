@@ -189,6 +189,31 @@ def test_strided_golden_empty_output():
     assert int(host(res["pair_ptr"])[-1]) == 0
     assert (host(res["nbr_in"]) == -1).all()
     assert res["nbr"].shape == (0, 27)
+    # the same without a host wait: M = 0 reaches the device word, no pair, and
+    # the forward over the map's capacity writes no row
+    print("async map of the empty-output example", flush=True)
+    cap = 16
+    ra = spc.build_kmap(cuda(np.array(g["coords"], np.int32)), g["batch"], g["spatial_shape"], g["ksize"],
+                        g["stride"], g["padding"], g["dilation"], subm=False, out_cap=cap, orders=True,
+                        device_count=True)
+    assert int(ra["n_out_dev"].item()) == g["expected_n_out"] == 0
+    assert int(host(ra["pair_ptr"])[-1]) == 0 and (host(ra["nbr_in"]) == -1).all()
+    n = len(g["coords"])
+    x = torch.ones((n, 16), dtype=torch.float16, device="cuda")
+    w = torch.ones((27, 16, 16), dtype=torch.float16, device="cuda")
+    out = torch.full((cap, 16), 5.0, dtype=torch.float16, device="cuda")
+    spc.conv_fwd_dev_rows(x, w, None, ra["nbr"], ra["n_out_dev"], cap, ra["order"], out=out)
+    assert (host(out) == 5.0).all()
+
+
+def test_async_map_of_no_rows():
+    # no input rows: both kinds of map publish a count of 0
+    for subm in (True, False):
+        print(f"async map of no rows subm={subm}", flush=True)
+        r = spc.build_kmap(cuda(np.zeros((0, 4), np.int32)), 1, (4, 4, 4), 3, 2, 1, 1, subm=subm,
+                           out_cap=None if subm else 8, orders=True, device_count=True)
+        assert int(r["n_out_dev"].item()) == 0
+        assert int(host(r["pair_ptr"])[-1]) == 0
 
 
 @pytest.mark.parametrize("table", TABLES)
