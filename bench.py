@@ -71,6 +71,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 SINGLE_KERNEL_STAGES = ("fwd_subm", "fwd_k1", "dinput_subm", "fwd_strided", "dinput_strided")
+# every stage timed back to back: the single-kernel ones, and dfilter, one call of two kernels (the split-K
+# partial products over pair segments, k_dfilter, then their fixed-order sum, k_reduce_segs)
+CALL_STAGES = SINGLE_KERNEL_STAGES + ("dfilter_subm", "dfilter_strided")
+STAGE_KERNELS = {s: "k_conv" for s in SINGLE_KERNEL_STAGES}
+STAGE_KERNELS.update(dfilter_subm="k_dfilter + k_reduce_segs", dfilter_strided="k_dfilter + k_reduce_segs")
 KERNEL_REPS = 20         # back-to-back launches per single-kernel stage for its duration
 BUSY_FILLS = 3           # 1 GiB fills queued ahead of them (~0.5 ms of GPU time)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -191,8 +196,8 @@ class Step:
         return spc.conv_fwd_wt(x, wt, None, map_, n_rows, subm, order)
 
     def kernel_ms(self, stage: str, reps: int = KERNEL_REPS) -> float:
-        """Average duration of one single-kernel stage launched `reps` times back to
-        back between two HIP events (the queue never drains, so no host gap counts)."""
+        """Average duration of one stage's call launched `reps` times back to back
+        between two HIP events (the queue never drains, so no host gap counts)."""
         spc, inp = self.spc, self.inp
         if self.km is None:
             self.km = spc.build_kmap(self.coords, inp["batch"], inp["shape"], 3, orders=True)
@@ -205,6 +210,10 @@ class Step:
             "fwd_strided": lambda: self.fwd(self.x, self.ws, self.wst, ks["nbr"], ks["n_out"], False, ks["order"]),
             "dinput_strided": lambda: spc.conv_bwd_input(self.gs, self.ws, ks["nbr_in"], False, self.n,
                                                          ks["order_in"]),
+            "dfilter_subm": lambda: spc.conv_bwd_filter(self.x, self.g, 27, km["pair_ptr"], km["pair_in"],
+                                                        km["pair_out"]),
+            "dfilter_strided": lambda: spc.conv_bwd_filter(self.x, self.gs, 27, ks["pair_ptr"], ks["pair_in"],
+                                                           ks["pair_out"]),
         }[stage]
         return time_launch(self, make, reps)
 
@@ -493,6 +502,12 @@ def measured_traffic(workload: str, stage: str):
         return None
 
 
+def stage_rooflines(r: dict, dtype: str, workload: str) -> dict:
+    """A roofline entry for every stage timed back to back (kernel_ms)."""
+    return {k: roofline(STAGE_KERNELS[k], k, r["flops"][k], r["bytes"][k], ms, dtype, workload)
+            for k, ms in r["kernel_ms"].items()}
+
+
 def roofline(kernel: str, stage: str, flop: float, nbytes: float, ms: float, dtype: str, workload: str) -> dict:
     """Roofline entry of one kernel: bound by MFMA when its arithmetic intensity
     is above the ridge, else by HBM; achieved = algorithmic FLOP (or bytes) per
@@ -543,7 +558,7 @@ def run_step(inp, dev, steps, warmup, kernel_stages=True):
         stages[k] = {"ms": round(stage_ms[k], 4),
                      "TFLOP/s": round(flops[k] / t / 1e12, 2) if k in flops and t > 0 else None,
                      "alg_GB/s": round(bytes_[k] / t / 1e9, 1) if t > 0 else None}
-    kernel_ms = {k: step.kernel_ms(k) for k in SINGLE_KERNEL_STAGES} if kernel_stages else {}
+    kernel_ms = {k: step.kernel_ms(k) for k in CALL_STAGES} if kernel_stages else {}
     return step, dict(wall=wall, dur=dur, stages=stages, kernel_ms=kernel_ms, flops=flops, bytes=bytes_)
 
 
@@ -605,6 +620,7 @@ def section_lidar(dev, steps, warmup):
     dom = max(SINGLE_KERNEL_STAGES, key=lambda k: r["kernel_ms"][k])
     out["roofline"] = roofline("k_conv", dom, r["flops"][dom], r["bytes"][dom], r["kernel_ms"][dom],
                                dtype_name(inp["dtype"]), "lidar")
+    out["rooflines"] = stage_rooflines(r, dtype_name(inp["dtype"]), "lidar")
     out["step_graph"] = graph_step(step, steps, warmup)
     return step, out
 
@@ -940,6 +956,7 @@ def main():
         "stages": head["stages"],
         "kernel_ms": head["kernel_ms"],
         "roofline": roof,
+        "rooflines": stage_rooflines(r, dtype, args.workload),
     }
     lidar_step = None
     if "lidar_step" in sections or "extras" in sections:
