@@ -344,7 +344,31 @@ __device__ __forceinline__ bool gather_buf(u32x4 (&af)[RB][KCMAX], const ConvArg
     return __any(any);
 }
 
-template <typename TT, int RB, int NB, bool TRANS, int KCMAX, bool PIPE>
+// gather_buf with this lane's source rows in registers (src[rb] for its MFMA
+// row rb, or -1), as the persistent identity-map walk keeps them.
+template <typename TT, int RB, int KCMAX>
+__device__ __forceinline__ void gather_src(u32x4 (&af)[RB][KCMAX], const ConvArgs& a, __amdgpu_buffer_rsrc_t xr,
+                                           const int32_t (&src)[RB], int lg) {
+    using S = typename TT::storage;
+    constexpr int E = TT::E;
+    const uint32_t row_bytes = uint32_t(a.CK) * uint32_t(sizeof(S));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kc = 0; kc < KCMAX; ++kc) {
+            const int col = (kc * 4 + lg) * E;
+            const bool ok = src[rb] >= 0 && col < a.CK;
+            af[rb][kc] = buf_ld16(xr, ok ? uint32_t(src[rb]) * row_bytes + uint32_t(col) * uint32_t(sizeof(S)) : BUF_OOB);
+        }
+}
+
+// PERSIST (the identity map of a k = 1 layer only, launched by launch_conv_nb
+// with a grid of at most two workgroups per CU): the weight slab is staged
+// once per workgroup, which then walks tiles blockIdx.x, + gridDim.x, ...
+// with the next tile's source rows and gathers in flight behind the current
+// tile's MFMAs and epilogue.  Every tile of an identity map costs the same,
+// so the fixed stride stays balanced.
+template <typename TT, int RB, int NB, bool TRANS, int KCMAX, bool PIPE, bool PERSIST = false>
 __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     using S = typename TT::storage;
     constexpr int BN = NB * 16;
@@ -365,7 +389,8 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // the epilogue stages the tile's outputs over the slabs and the map tile
     constexpr int SROW = BN * int(sizeof(S)) + 16;  // staged output row (16 bytes of padding)
     const int main_bytes = 2 * slab_bytes + (KTILE * BMP + 2 * KTILE + 4) * 4;
-    int32_t* rsrc = reinterpret_cast<int32_t*>(lds + (main_bytes > BM * SROW ? main_bytes : BM * SROW));  // [BM]
+    const int rsrc_off = PERSIST ? slab_bytes + BM * SROW : (main_bytes > BM * SROW ? main_bytes : BM * SROW);
+    int32_t* rsrc = reinterpret_cast<int32_t*>(lds + rsrc_off);  // [BM]
     float* sbias = reinterpret_cast<float*>(rsrc + BM);                // [BN] bias of this column block, or 0
 
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
@@ -397,7 +422,7 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
 
     // the processing order of this tile's rows into LDS: rsrc[r] is the
     // source row of tile row r, or -1
-    if (threadIdx.x < BM) {
+    if (!PERSIST && threadIdx.x < BM) {
         const int row = row0 + threadIdx.x;
         const int rc = row < n_rows ? row : n_rows - 1;
         const int32_t s0 = a.order ? a.order[rc] : rc;
@@ -409,6 +434,57 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
+    // lg*4 .. lg*4+3 of row lr.  Bias, then the residual and the ReLU of a
+    // fused layer, go on the fp32 value before its one rounding (a residual
+    // aliasing y is read here, before any write of this tile).  The rounded
+    // values are staged in LDS at `stage` (over the slabs and the map tile,
+    // free after the last offset's barrier; after the slab in the persistent
+    // walk, which keeps it) and written out as whole 16-byte chunks of each
+    // row, consecutive threads on consecutive chunks: a quarter of the write
+    // requests of per-lane 8-byte stores.
+    S* y = static_cast<S*>(a.y);
+    const S* res = static_cast<const S*>(a.res);
+    auto epilogue = [&](char* stage) {
+        f32x4_t bv[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(sbias + nb * 16 + lg * 4);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = (wave * RB + rb) * 16 + lr;
+            const int row = rsrc[r];
+            f32x4_t v[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) v[nb] = acc[rb][nb] + bv[nb];
+            if (res && row >= 0) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) v[nb] += load4<TT>(res + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4);
+            }
+            if (a.relu) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[nb][e] = v[nb][e] < 0.f ? 0.f : v[nb][e];  // NaN stays NaN
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                store4<TT>(stage + r * SROW + (nb * 16 + lg * 4) * int(sizeof(S)), v[nb]);
+        }
+        if constexpr (PERSIST)
+            lds_barrier();  // the next tile's gathers stay in flight
+        else
+            __syncthreads();
+        constexpr int CPR = BN * int(sizeof(S)) / 16;  // 16-byte chunks per staged row
+        static_assert((BM * CPR) % CT == 0, "whole passes over the staged tile");
+#pragma unroll
+        for (int q = 0; q < BM * CPR / CT; ++q) {
+            const int idx = q * CT + int(threadIdx.x);
+            const int r = idx / CPR, c = idx - r * CPR;
+            const int row = rsrc[r];
+            if (row >= 0) st16(y + int64_t(row) * a.CN + col0 + c * (16 / int(sizeof(S))), ld16(stage + r * SROW + c * 16));
+        }
+    };
 
     WStage<TT, BN, TRANS, ROWS> wst;
     wst.init(a, col0);
@@ -422,6 +498,134 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
     // the identity map (K = 1) has one offset, whose entries are the rows
     // themselves: its column is rsrc, and nothing is staged
     int32_t* const cols = a.map ? tile : rsrc;
+    // one offset's MFMAs: gathered rows `cur` against slab buffer j & 1
+    // nv: the number of global loads issued just before this call in the
+    // same scheduling region, which the 16-bit pattern below spreads among
+    // the MFMAs (0: none)
+    auto mma = [&](const u32x4 (&cur)[RB][KCMAX], int j, auto nv) {
+        constexpr int NV = decltype(nv)::value;
+        const char* sl = lds + (j & 1) * slab_bytes;
+        if constexpr (!ROWS && TT::E == 8 && KCMAX <= 4) {
+            // B fragments in (kc, nb) order, each read BLOOK fragments
+            // ahead of its MFMAs, so that several LDS reads are in flight
+            // behind the MFMAs instead of one pair at a time.  Reads past
+            // the contraction re-read its last chunk row (valid data; the
+            // loop ends before those fragments are used).
+            constexpr int NI = KCMAX * NB;
+            constexpr int LA = (KCMAX <= 2 ? 3 : BLOOK) < NI ? (KCMAX <= 2 ? 3 : BLOOK) : NI;
+            auto rd = [&](int i) {
+                const int kc = min(i / NB, KC - 1), nb = i % NB;
+                return ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+            };
+            u32x4 bq[LA];
+#pragma unroll
+            for (int i = 0; i < LA; ++i) bq[i] = rd(i);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int kc = i / NB, nb = i % NB;
+                if (kc >= KC) break;
+                const u32x4 b = bq[i % LA];
+                if (i + LA < NI) bq[i % LA] = rd(i + LA);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(b, cur[rb][kc], acc[rb][nb]);
+            }
+            {
+                // keep that order through the scheduler, which otherwise
+                // pairs each two reads with their MFMAs to save registers:
+                // LA reads, then (RB MFMAs, one read) per fragment.  With
+                // NV loads in the region (the next offsets' slab and
+                // gathers), one load follows every SP-th fragment's MFMAs:
+                // a wave then issues its loads between its MFMAs instead
+                // of stalling on the load path before the first of them
+                // (the gathers' RB source-row reads go first)
+                constexpr int SP = NV > 0 && NI / NV > 1 ? NI / NV : 1;
+                __builtin_amdgcn_sched_group_barrier(0x100, NV > 0 ? LA + RB : LA, 0);
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+                    if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (NV > 0 && i % SP == 0 && i / SP < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            return;
+        }
+#pragma unroll
+        for (int kc = 0; kc < KCMAX; ++kc) {
+            if (kc >= KC) break;
+            u32x4 bf[NB];
+            if constexpr (ROWS) {  // transposing reads of the row layout
+                const char* p0 = sl + ((kc * 4 + lg) * 8 + (lr >> 2)) * row_stride<BN>() + 4 * (lr & 3) * 2;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const s16x4 lo = ds_read_tr16(p0 + nb * 32), hi = ds_read_tr16(p0 + nb * 32 + 4 * row_stride<BN>());
+                    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                    bf[nb] = u32x4{l2.x, l2.y, h2.x, h2.y};
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], cur[rb][kc], acc[rb][nb]);
+        }
+    };
+    if constexpr (PERSIST) {
+        // the identity map's walk: tile t holds rows t*BM .. t*BM + BM-1 of the
+        // processing order, each its own source; this workgroup takes tiles
+        // blockIdx.x + i*G
+        const int tiles_all = int((int64_t(a.n_rows) + BM - 1) / BM);
+        const int G = int(gridDim.x);
+        const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.x, uint32_t(a.n_src) * uint32_t(a.CK) * uint32_t(sizeof(S)));
+        // this lane's source row for its MFMA row rb of tile t, or -1 (rows
+        // past the end and tiles past the last read a clamped, valid row)
+        auto src_of = [&](int t, int32_t (&src)[RB]) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int64_t row = int64_t(t) * BM + (wave * RB + rb) * 16 + lr;
+                const int rc = row < a.n_rows ? int(row) : a.n_rows - 1;
+                const int32_t s0 = a.order ? a.order[rc] : rc;
+                src[rb] = row < a.n_rows && (unsigned)s0 < (unsigned)a.n_rows ? s0 : -1;
+            }
+        };
+        wst.load(a, 0);
+        wst.store(lds, a, 0);
+        u32x4 ga[RB][KCMAX], gb[RB][KCMAX];
+        int32_t sa[RB], sb[RB];
+        int t = int(blockIdx.x);
+        src_of(t, sa);
+        gather_src<TT, RB, KCMAX>(ga, a, xr, sa, lg);
+        src_of(t + G, sb);
+        lds_barrier();  // the slab and the bias are in place
+        constexpr int NVP = !ROWS && TT::E == 8 && KCMAX <= 4 ? RB * KCMAX : 0;
+        // one tile: the gathers of tile tt + G (their sources were read a tile
+        // ago) and the sources of tile tt + 2G go out first, then tile tt's
+        // MFMAs and epilogue; the buffers keep fixed roles in a loop unrolled
+        // by two (a copy would wait for its loads)
+        auto tile_step = [&](int tt, const u32x4 (&cur)[RB][KCMAX], int32_t (&scur)[RB], u32x4 (&nxt)[RB][KCMAX],
+                             const int32_t (&snxt)[RB]) {
+            gather_src<TT, RB, KCMAX>(nxt, a, xr, snxt, lg);
+            if (lg == 0) {  // the epilogue's row list; every wave writes its own rows
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) rsrc[(wave * RB + rb) * 16 + lr] = scur[rb];
+            }
+            src_of(tt + 2 * G, scur);
+            mma(cur, 0, std::integral_constant<int, NVP>{});
+            epilogue(lds + slab_bytes);
+            lds_barrier();  // every wave is done with the staged tile and the row list
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        };
+        for (; t < tiles_all; t += 2 * G) {
+            tile_step(t, ga, sa, gb, sb);
+            if (t + G >= tiles_all) break;
+            tile_step(t + G, gb, sb, ga, sa);
+        }
+        return;
+    }
     for (int kt0 = 0; kt0 < a.K; kt0 += KTILE) {
         const int kt = min(KTILE, a.K - kt0);
         if (!a.map) {
@@ -483,79 +687,6 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
         if (nk == 0) continue;
 
         auto slab_of = [&](int j) { const int kg = kt0 + list[j]; return a.w_rev ? a.K - 1 - kg : kg; };
-        // one offset's MFMAs: gathered rows `cur` against slab buffer j & 1
-        // nv: the number of global loads issued just before this call in the
-        // same scheduling region, which the 16-bit pattern below spreads among
-        // the MFMAs (0: none)
-        auto mma = [&](const u32x4 (&cur)[RB][KCMAX], int j, auto nv) {
-            constexpr int NV = decltype(nv)::value;
-            const char* sl = lds + (j & 1) * slab_bytes;
-            if constexpr (!ROWS && TT::E == 8 && KCMAX <= 4) {
-                // B fragments in (kc, nb) order, each read BLOOK fragments
-                // ahead of its MFMAs, so that several LDS reads are in flight
-                // behind the MFMAs instead of one pair at a time.  Reads past
-                // the contraction re-read its last chunk row (valid data; the
-                // loop ends before those fragments are used).
-                constexpr int NI = KCMAX * NB;
-                constexpr int LA = (KCMAX <= 2 ? 3 : BLOOK) < NI ? (KCMAX <= 2 ? 3 : BLOOK) : NI;
-                auto rd = [&](int i) {
-                    const int kc = min(i / NB, KC - 1), nb = i % NB;
-                    return ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
-                };
-                u32x4 bq[LA];
-#pragma unroll
-                for (int i = 0; i < LA; ++i) bq[i] = rd(i);
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    const int kc = i / NB, nb = i % NB;
-                    if (kc >= KC) break;
-                    const u32x4 b = bq[i % LA];
-                    if (i + LA < NI) bq[i % LA] = rd(i + LA);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(b, cur[rb][kc], acc[rb][nb]);
-                }
-                {
-                    // keep that order through the scheduler, which otherwise
-                    // pairs each two reads with their MFMAs to save registers:
-                    // LA reads, then (RB MFMAs, one read) per fragment.  With
-                    // NV loads in the region (the next offsets' slab and
-                    // gathers), one load follows every SP-th fragment's MFMAs:
-                    // a wave then issues its loads between its MFMAs instead
-                    // of stalling on the load path before the first of them
-                    // (the gathers' RB source-row reads go first)
-                    constexpr int SP = NV > 0 && NI / NV > 1 ? NI / NV : 1;
-                    __builtin_amdgcn_sched_group_barrier(0x100, NV > 0 ? LA + RB : LA, 0);
-#pragma unroll
-                    for (int i = 0; i < NI; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
-                        if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                        if (NV > 0 && i % SP == 0 && i / SP < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                    }
-                }
-                return;
-            }
-#pragma unroll
-            for (int kc = 0; kc < KCMAX; ++kc) {
-                if (kc >= KC) break;
-                u32x4 bf[NB];
-                if constexpr (ROWS) {  // transposing reads of the row layout
-                    const char* p0 = sl + ((kc * 4 + lg) * 8 + (lr >> 2)) * row_stride<BN>() + 4 * (lr & 3) * 2;
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const s16x4 lo = ds_read_tr16(p0 + nb * 32), hi = ds_read_tr16(p0 + nb * 32 + 4 * row_stride<BN>());
-                        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-                        bf[nb] = u32x4{l2.x, l2.y, h2.x, h2.y};
-                    }
-                } else {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) bf[nb] = ld16(sl + slab_off<BN>(kc * 4 + lg, nb * 16 + lr));
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) acc[rb][nb] = mfma16<TT>(bf[nb], cur[rb][kc], acc[rb][nb]);
-            }
-        };
         if constexpr (PIPE) {
             // Short contractions: two offsets of gathered rows in flight.  Three
             // register buffers take fixed roles in a loop unrolled by three (a
@@ -646,83 +777,51 @@ __global__ __launch_bounds__(CT) void k_conv(ConvArgs a) {
         }
     }
 
-    // epilogue: D[channel][row] per 16x16 tile; this lane holds channels
-    // lg*4 .. lg*4+3 of row lr.  Bias, then the residual and the ReLU of a
-    // fused layer, go on the fp32 value before its one rounding (a residual
-    // aliasing y is read here, before any write of this tile).  The rounded
-    // values are staged in LDS (over the slabs and the map tile, free after the
-    // last offset's barrier) and written out as whole 16-byte chunks of each
-    // row, consecutive threads on consecutive chunks: a quarter of the write
-    // requests of per-lane 8-byte stores.
-    S* y = static_cast<S*>(a.y);
-    const S* res = static_cast<const S*>(a.res);
-    f32x4_t bv[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const f32x4_t*>(sbias + nb * 16 + lg * 4);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r = (wave * RB + rb) * 16 + lr;
-        const int row = rsrc[r];
-        f32x4_t v[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) v[nb] = acc[rb][nb] + bv[nb];
-        if (res && row >= 0) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) v[nb] += load4<TT>(res + int64_t(row) * a.CN + col0 + nb * 16 + lg * 4);
-        }
-        if (a.relu) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[nb][e] = v[nb][e] < 0.f ? 0.f : v[nb][e];  // NaN stays NaN
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            store4<TT>(lds + r * SROW + (nb * 16 + lg * 4) * int(sizeof(S)), v[nb]);
-    }
-    __syncthreads();
-    constexpr int CPR = BN * int(sizeof(S)) / 16;  // 16-byte chunks per staged row
-    static_assert((BM * CPR) % CT == 0, "whole passes over the staged tile");
-#pragma unroll
-    for (int q = 0; q < BM * CPR / CT; ++q) {
-        const int idx = q * CT + int(threadIdx.x);
-        const int r = idx / CPR, c = idx - r * CPR;
-        const int row = rsrc[r];
-        if (row >= 0) st16(y + int64_t(row) * a.CN + col0 + c * (16 / int(sizeof(S))), ld16(lds + r * SROW + c * 16));
-    }
+    epilogue(lds);
+
 }
 
 constexpr int RB_DEFAULT = 2;
 
-template <typename TT, int NB, bool TRANS, int KCMAX, bool PIPE>
+template <typename TT, int NB, bool TRANS, int KCMAX, bool PIPE, bool PERSIST = false>
 spc_status launch_conv_nb(const ConvArgs& a, hipStream_t stream) {
     constexpr int BN = NB * 16;
     constexpr int BM = NW * RB_DEFAULT * 16;
-    auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX, PIPE>;
+    auto kern = k_conv<TT, RB_DEFAULT, NB, TRANS, KCMAX, PIPE, PERSIST>;
     static_assert((2 * KTILE + 4) % 4 == 0, "flags + list keep the following arrays 16-byte aligned");
     using S = typename TT::storage;
     const size_t main_bytes = 2 * size_t(slab_bytes_of<BN, rows_layout<TT, TRANS, KCMAX>()>(a.kch)) +
                               (size_t(KTILE) * (BM + 1) + 2 * KTILE + 4) * 4;
     const size_t stage_bytes = size_t(BM) * (BN * sizeof(S) + 16);  // the epilogue's staged outputs
-    const size_t lds = std::max(main_bytes, stage_bytes) + BM * 4 + BN * 4;
+    // the persistent walk keeps one slab and stages its outputs after it
+    const size_t slab1 = size_t(slab_bytes_of<BN, rows_layout<TT, TRANS, KCMAX>()>(a.kch));
+    const size_t lds = (PERSIST ? slab1 + stage_bytes : std::max(main_bytes, stage_bytes)) + BM * 4 + BN * 4;
     if (lds > 160 * 1024) return fail(SPC_ERR_UNSUPPORTED, "LDS tile of %zu bytes exceeds 160 KiB", lds);
     if (lds > 64 * 1024) SPC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
     dim3 grid(unsigned(ceil_div(a.n_rows, BM)), unsigned(a.CN / BN));
+    if (PERSIST) {
+        // at most two workgroups per CU and column block, each with an equal
+        // share (to one tile) of the tiles
+        const int64_t tiles = ceil_div(a.n_rows, BM);
+        const int64_t slots = std::max<int64_t>(1, 2 * int64_t(device_cus()) / int64_t(grid.y));
+        const int64_t per = ceil_div(tiles, std::min(tiles, slots));
+        grid.x = unsigned(ceil_div(tiles, per));
+    }
     hipLaunchKernelGGL(kern, grid, dim3(CT), lds, stream, a);
     SPC_LAUNCHED("k_conv");
     return SPC_OK;
 }
 
-template <typename TT, bool TRANS, int KCMAX, bool PIPE = false>
+template <typename TT, bool TRANS, int KCMAX, bool PIPE = false, bool PERSIST = false>
 spc_status launch_conv_k(const ConvArgs& a, hipStream_t stream) {
     const int blocks = a.CN / 16;
-    if (blocks % 8 == 0) return launch_conv_nb<TT, 8, TRANS, KCMAX, PIPE>(a, stream);
-    if (blocks % 6 == 0) return launch_conv_nb<TT, 6, TRANS, KCMAX, PIPE>(a, stream);
-    if (blocks % 4 == 0) return launch_conv_nb<TT, 4, TRANS, KCMAX, PIPE>(a, stream);
-    if (blocks % 3 == 0) return launch_conv_nb<TT, 3, TRANS, KCMAX, PIPE>(a, stream);
-    if (blocks % 2 == 0) return launch_conv_nb<TT, 2, TRANS, KCMAX, PIPE>(a, stream);
-    return launch_conv_nb<TT, 1, TRANS, KCMAX, PIPE>(a, stream);
+    if (blocks % 8 == 0) return launch_conv_nb<TT, 8, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
+    if (blocks % 6 == 0) return launch_conv_nb<TT, 6, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
+    if (blocks % 4 == 0) return launch_conv_nb<TT, 4, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
+    if (blocks % 3 == 0) return launch_conv_nb<TT, 3, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
+    if (blocks % 2 == 0) return launch_conv_nb<TT, 2, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
+    return launch_conv_nb<TT, 1, TRANS, KCMAX, PIPE, PERSIST>(a, stream);
 }
 
 template <typename TT, bool TRANS>
@@ -739,11 +838,20 @@ spc_status launch_conv_t(ConvArgs& a, hipStream_t stream) {
     // Up to 4 steps the variant matches KC exactly (its loops have no run-time
     // bound); 5 to 8 steps share one bounded variant.
     const bool pipe = a.xbuf && a.K > 1;
+    // the identity map of a k = 1 layer (rows counted on the host) walks its
+    // tiles persistently, with the slab staged once per workgroup
+    const bool persist = a.xbuf && !a.map && a.K == 1 && !a.n_rows_dev;
     switch (KC) {
-        case 1: return pipe ? launch_conv_k<TT, TRANS, 1, true>(a, stream) : launch_conv_k<TT, TRANS, 1>(a, stream);
-        case 2: return pipe ? launch_conv_k<TT, TRANS, 2, true>(a, stream) : launch_conv_k<TT, TRANS, 2>(a, stream);
-        case 3: return pipe ? launch_conv_k<TT, TRANS, 3, true>(a, stream) : launch_conv_k<TT, TRANS, 3>(a, stream);
-        case 4: return pipe ? launch_conv_k<TT, TRANS, 4, true>(a, stream) : launch_conv_k<TT, TRANS, 4>(a, stream);
+#define SPC_CONV_CASE(N)                                                  \
+    case N:                                                               \
+        if (pipe) return launch_conv_k<TT, TRANS, N, true>(a, stream);     \
+        if (persist) return launch_conv_k<TT, TRANS, N, false, true>(a, stream); \
+        return launch_conv_k<TT, TRANS, N>(a, stream);
+        SPC_CONV_CASE(1)
+        SPC_CONV_CASE(2)
+        SPC_CONV_CASE(3)
+        SPC_CONV_CASE(4)
+#undef SPC_CONV_CASE
         default: break;
     }
     if (KC <= 8) return launch_conv_k<TT, TRANS, 8>(a, stream);

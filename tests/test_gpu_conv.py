@@ -175,6 +175,29 @@ def test_workload_shells_bf16_k3_then_k1():
     assert_close(z, OC.conv_fwd(y.cpu(), w.extra["weight_k1"], None, np.arange(w.n)[None]), TOL[w.dtype], "k1")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n,cin,cout", [
+    (300_001, 32, 64),   # 2,344 tiles: several per workgroup, ragged last tile
+    (70_000, 128, 128),  # full 128-channel tiles
+    (1_000, 64, 16),     # fewer tiles than workgroups
+])
+def test_k1_layer_over_many_tiles(dtype, n, cin, cout):
+    """The identity map of a k = 1 layer, whose workgroups each walk several
+    tiles with the weight slab staged once: forward (both weight layouts) and
+    dinput against the oracle."""
+    t = W.small_layer(170 + cin, np.zeros((n, 4), np.int32), cin, cout, 1, dtype)
+    ident = np.arange(n)[None]
+    x, w, b, g = cuda(t["feats"]), cuda(t["weight"]), cuda(t["bias"]), cuda(t["grad"])
+    print(f"k1 walk n={n} {cin}->{cout} {dtype}", flush=True)
+    out = spc.subm_conv_fwd(x, w, b, None)
+    assert_close(out, OC.conv_fwd(t["feats"], t["weight"], t["bias"], ident), TOL[dtype], "k1 fwd")
+    for pre in (False, True):
+        assert torch.equal(spc.subm_conv_fwd(x, w, b, None, pretranspose=pre), out), f"pretranspose={pre}"
+    din = spc.conv_bwd_input(g, w, None, True, n)
+    assert_close(din, OC.conv_bwd_input(t["grad"], t["weight"], ident, n), TOL[dtype], "k1 dinput")
+    assert torch.equal(spc.conv_bwd_input(g, w, None, True, n), din)  # run twice: identical
+
+
 def test_workload_strided_lidar_fp16():
     w = W.workload("strided_k3s2_f16_lidar120k")
     km = spc.build_kmap(cuda(w.coords), w.batch, w.shape, 3, 2, 1, 1, subm=False, orders=True)
