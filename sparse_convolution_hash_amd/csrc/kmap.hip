@@ -41,6 +41,11 @@ constexpr int MASK_BITS = 32;                // orders are built for K <= 32
 constexpr int MAX_K = 343;                   // up to 7 x 7 x 7 offsets
 constexpr uint64_t OCC_FILTER_CELLS_PER_ROW = 8192;        // hash filter: at most 1 KiB of bitmap per row
 constexpr uint64_t OCC_FILTER_MAX_BYTES = uint64_t(1) << 30;
+// strided output sites: a byte per site (plain stores) for output grids of at
+// most this many sites per input row and this many sites in all; otherwise
+// the bitmap directly (atomic ORs)
+constexpr uint64_t BYTEMAP_SITES_PER_ROW = 32;
+constexpr uint64_t BYTEMAP_MAX_SITES = uint64_t(1) << 29;
 
 struct KGeom {
     int32_t batch, Z, Y, X;      // input grid
@@ -147,6 +152,8 @@ __device__ __forceinline__ int32_t rows_within(const uint32_t* hdr, int64_t cap)
 __global__ void k_clear(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ bitmap,
                         int64_t nwords, uint32_t* __restrict__ occ, int64_t occ_words, uint32_t* __restrict__ hdr,
                         int32_t* coord_err, int32_t* __restrict__ zero, int64_t nzero) {
+    // (a strided map with a byte map passes the byte map here as the bitmap,
+    // nwords counting its 4-byte words)
     const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     if (t < H_WORDS) hdr[t] = 0u;
@@ -171,7 +178,7 @@ __global__ void k_fill_map(int32_t* __restrict__ map, int K, int64_t cap, const 
 template <bool STRIDED>
 __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, int32_t n, KGeom g,
                                                uint64_t* table, uint32_t mask, uint32_t* occ,
-                                               uint32_t* bitmap, uint32_t* hdr) {
+                                               uint32_t* bitmap, uint8_t* sites, uint32_t* hdr) {
     const int32_t i = blockIdx.x * KB + threadIdx.x;
     if (i >= n) return;
     const int4 c = coords[i];
@@ -210,6 +217,14 @@ __global__ __launch_bounds__(KB) void k_insert(const int4* __restrict__ coords, 
         const int num = c.w + g.px - k * g.dx;
         const int q = num >= 0 ? int(qdiv(uint32_t(num), g.msx)) : -1;
         if (q >= 0 && q * g.sx == num && q < g.ox && nx < 8) ox[nx++] = q;
+    }
+    if (sites) {  // a byte per site: plain stores, which concurrent rows may repeat
+        for (int a = 0; a < nz; ++a)
+            for (int b = 0; b < ny; ++b) {
+                const uint32_t base = out_key(c.x, oz[a], oy[b], 0, g);
+                for (int d = 0; d < nx; ++d) sites[base + uint32_t(ox[d])] = 1;
+            }
+        return;
     }
     // sites along x share a bitmap word mostly: one atomic per word touched
     for (int a = 0; a < nz; ++a)
@@ -270,13 +285,37 @@ __global__ __launch_bounds__(KB) void k_subm_probe(const int4* __restrict__ coor
 
 // Popcount of each thread's WORDS_PER_THREAD bitmap words, summed per block
 // into block_sums and added to *total (zeroed beforehand).
-__global__ __launch_bounds__(KB) void k_bitmap_count(const uint32_t* __restrict__ bitmap, int64_t nwords,
+__global__ __launch_bounds__(KB) void k_bitmap_count(uint32_t* __restrict__ bitmap, int64_t nwords,
+                                                     const uint8_t* __restrict__ sites,
                                                      int32_t* __restrict__ block_sums, uint32_t* total) {
     __shared__ int32_t red[KB / WAVE];
     const int64_t w0 = (int64_t(blockIdx.x) * KB + threadIdx.x) * WORDS_PER_THREAD;
     int s = 0;
     if (w0 < nwords) {
-        const u32x4 a = ld16(bitmap + w0), b = ld16(bitmap + w0 + 4);
+        u32x4 a, b;
+        if (sites) {
+            // the byte map (bytes 0 or 1) into the thread's bitmap words: 16
+            // bytes give 16 bits, byte j bit j
+            uint32_t w[WORDS_PER_THREAD];
+            const uint8_t* src = sites + w0 * 32;
+#pragma unroll
+            for (int q = 0; q < WORDS_PER_THREAD; ++q) {
+                const u32x4 lo = ld16(src + q * 32), hi = ld16(src + q * 32 + 16);
+                const uint32_t v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                uint32_t bits = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bits |= ((v[e] & 1u) | ((v[e] >> 7) & 2u) | ((v[e] >> 14) & 4u) | ((v[e] >> 21) & 8u)) << (4 * e);
+                w[q] = bits;
+            }
+            a = u32x4{w[0], w[1], w[2], w[3]};
+            b = u32x4{w[4], w[5], w[6], w[7]};
+            st16(bitmap + w0, a);
+            st16(bitmap + w0 + 4, b);
+        } else {
+            a = ld16(bitmap + w0);
+            b = ld16(bitmap + w0 + 4);
+        }
         s = __popc(a.x) + __popc(a.y) + __popc(a.z) + __popc(a.w) + __popc(b.x) + __popc(b.y) +
             __popc(b.z) + __popc(b.w);
     }
@@ -805,6 +844,7 @@ struct Plan {
     int64_t cap;                 // table slots
     int64_t out_vol;             // strided output grid volume
     int64_t nwords;              // bitmap words (multiple of WORDS_PER_THREAD)
+    bool bytemap;                // strided output sites marked in a byte map (32 bytes per bitmap word)
     int64_t m_max;               // upper bound of the output row count
     int64_t rows_max;            // max(n, m_max)
     int64_t cblk;                // count-matrix blocks per offset
@@ -813,8 +853,8 @@ struct Plan {
     // workspace offsets
     int64_t rgroups;             // radix block groups
     int64_t occ_words;           // input occupancy bitmap words (multiple of 4)
-    size_t off_table, off_occ, off_counts, off_bitmap, off_prefix, off_bsums, off_masks, off_sort, off_gsum, off_gtot,
-        total;
+    size_t off_table, off_occ, off_counts, off_bitmap, off_sites, off_prefix, off_bsums, off_masks, off_sort, off_gsum,
+        off_gtot, total;
     size_t sort_slot_bytes;      // per sort: keys x2, values x2, histogram matrix
 };
 
@@ -894,6 +934,17 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     const int64_t wpb = int64_t(KB) * WORDS_PER_THREAD;
     p.nwords = g.subm ? 0 : std::max<int64_t>(wpb, ceil_div(ceil_div(p.out_vol, 32), wpb) * wpb);
     p.bm_blocks = p.nwords / wpb;
+    // Strided output sites: many input rows reach each site (up to 8 for
+    // k3 s2), so atomic ORs on a bitmap word contend.  A byte per site takes
+    // plain stores instead (idempotent, so concurrent rows need no atomics),
+    // and the count kernel packs the bytes into the bitmap.  That costs
+    // clearing and reading a byte per site, and scattered byte stores into a
+    // map larger than the caches are slow: it pays on output grids that are
+    // dense next to the rows (shell sets: 4 sites per input row, strided map
+    // 236 -> 205 us), not on sparse ones (LiDAR scene: 197 sites per row, no
+    // gain).
+    p.bytemap = !g.subm && uint64_t(p.nwords) * 32 <= BYTEMAP_MAX_SITES &&
+                uint64_t(p.nwords) * 32 <= BYTEMAP_SITES_PER_ROW * uint64_t(std::max<int64_t>(n_in, 1));
     p.m_max = g.subm ? n_in : std::min<int64_t>(int64_t(p.K) * n_in, p.out_vol);
     p.rows_max = std::max(n_in, p.m_max);
     p.cblk = ceil_div(p.rows_max, KB);
@@ -903,6 +954,7 @@ spc_status make_plan(const spc_geom* gp, int64_t n_in, Plan& p) {
     p.off_occ = off;     off = align_up(off + size_t(p.occ_words) * 4, 256);
     p.off_counts = off;  off = align_up(off + size_t(p.K) * p.cblk * 4, 256);
     p.off_bitmap = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
+    p.off_sites = off;   off = align_up(off + (p.bytemap ? size_t(p.nwords) * 32 : 0), 256);
     p.off_prefix = off;  off = align_up(off + size_t(p.nwords) * 4, 256);
     p.off_bsums = off;   off = align_up(off + size_t(p.bm_blocks) * 4 + 4, 256);
     p.off_masks = off;   off = align_up(off + size_t(p.rows_max) * 4 * 2, 256);   // neighbour masks, per sort
@@ -1184,6 +1236,7 @@ spc_status build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in, i
     uint64_t* table = reinterpret_cast<uint64_t*>(base + p.off_table);
     uint32_t* occ = reinterpret_cast<uint32_t*>(base + p.off_occ);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.off_bitmap);
+    uint8_t* sites = p.bytemap ? reinterpret_cast<uint8_t*>(base + p.off_sites) : nullptr;
     uint32_t* prefix = reinterpret_cast<uint32_t*>(base + p.off_prefix);
     int32_t* bsums = reinterpret_cast<int32_t*>(base + p.off_bsums);
     const int4* c4 = reinterpret_cast<const int4*>(coords);
@@ -1194,17 +1247,20 @@ spc_status build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in, i
 
     const int64_t nzero = (order || order_in) ? int64_t(2 * RS_MAX_PASSES) * RS_BINS * p.rgroups : 0;
     const int64_t fill = p.g.dense ? 0 : p.cap;   // hash slots to mark empty (the index grid is never cleared)
-    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({fill / 2, p.nwords / 4, p.occ_words / 4, nzero / 4}), KB, 4096)),
-                       dim3(KB), 0, stream, table, fill, bitmap, p.nwords, occ, p.occ_words, s.hdr, coord_err, s.gsum,
-                       nzero);
+    // the byte map is cleared in place of the bitmap, which the count kernel then writes whole
+    uint32_t* clear_bits = sites ? reinterpret_cast<uint32_t*>(sites) : bitmap;
+    const int64_t clear_words = sites ? p.nwords * 8 : p.nwords;
+    hipLaunchKernelGGL(k_clear, dim3(grid_for(std::max({fill / 2, clear_words / 4, p.occ_words / 4, nzero / 4}), KB, 4096)),
+                       dim3(KB), 0, stream, table, fill, clear_bits, clear_words, occ, p.occ_words, s.hdr, coord_err,
+                       s.gsum, nzero);
     SPC_LAUNCHED("k_clear");
     if (n > 0) {
         if (subm)
             hipLaunchKernelGGL(k_insert<false>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, bitmap,
-                               s.hdr);
+                               (uint8_t*)nullptr, s.hdr);
         else
             hipLaunchKernelGGL(k_insert<true>, dim3(nblk), dim3(KB), 0, stream, c4, n, p.g, table, mask, occ, bitmap,
-                               s.hdr);
+                               sites, s.hdr);
         SPC_LAUNCHED("k_insert");
     }
 
@@ -1250,8 +1306,8 @@ spc_status build_kmap(const spc_geom* gp, const int32_t* coords, int64_t n_in, i
     // strided: output sites into the bitmap, then count them (total -> hdr,
     // by atomics; the per-block counts are scanned separately only for large
     // bitmaps, else each emit block sums the counts before it)
-    hipLaunchKernelGGL(k_bitmap_count, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, bsums,
-                       s.hdr + H_NOUT);
+    hipLaunchKernelGGL(k_bitmap_count, dim3(unsigned(p.bm_blocks)), dim3(KB), 0, stream, bitmap, p.nwords, sites,
+                       bsums, s.hdr + H_NOUT);
     SPC_LAUNCHED("k_bitmap_count");
     const bool scanned = p.bm_blocks > EMIT_SUM_BLOCKS;
     if (scanned) {

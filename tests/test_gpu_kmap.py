@@ -160,6 +160,21 @@ def test_strided_lidar_workload():
     assert torch.equal(res["nbr"], res2["nbr"]) and torch.equal(res["out_coords"], res2["out_coords"])
 
 
+@pytest.mark.parametrize("k,s,p", [(3, 2, 1), (2, 2, 0), (3, 1, 1)])
+def test_strided_dense_output_grid(k, s, p):
+    # an output grid with few sites per input row (here at most 4) marks its
+    # sites in a byte map with plain stores; the maps equal the oracle's
+    c = W.tiny_grid(W.rng(261), 32, 0.3, 2)
+    check_strided(c, 2, (32, 32, 32), k, s, p, 1)
+
+
+def test_strided_shells_workload():
+    # the shell sets' k3 s2 map at full size (266k rows, byte-mapped output sites)
+    w = W.workload("subm_k3_k1_bf16_shells128")
+    print(f"{w.name} n={w.n}", flush=True)
+    check_strided(w.coords, w.batch, w.shape, 3, 2, 1, 1)
+
+
 def test_strided_capacity_above_the_count():
     # a capacity above M sizes the launches by the capacity; the rows past M
     # add nothing, and every result equals the exact-capacity call's
@@ -264,6 +279,14 @@ def test_shifted_sites_give_the_same_map():
     big = check_subm(shifted, 2, (200, 220, 240), 3)
     assert torch.equal(small["nbr"], big["nbr"]) and torch.equal(small["order"], big["order"])
     check_strided(shifted, 2, (200, 220, 240), 3, 2, 1, 1)
+
+
+def test_strided_map_above_the_byte_map_limit():
+    # an output grid of more than 2^29 sites (520 x 1024 x 1024, k3 s1 p1) marks
+    # its sites in the bitmap with atomic ORs instead of a byte per site; the
+    # sites lie against three faces of the grid
+    c = W.tiny_grid(W.rng(260), 12, 0.3, 1) + np.array([0, 508, 1000, 1012], np.int32)
+    check_strided(c, 1, (520, 1024, 1024), 3, 1, 1, 1, tables=("hash",))
 
 
 def test_hash_at_four_lidar_samples():
