@@ -19,6 +19,8 @@
 // (or v_mfma_f32_16x16x4_f32).  The fp32 accumulators stay in registers for
 // the whole offset loop; each output row is written once, with the bias added
 // and one rounding, so there are no atomics and the result is deterministic.
+// The identity map of a k = 1 layer has one offset and equal tiles: there a
+// workgroup stages its slab once and walks several tiles (PERSIST).
 //
 // This header holds the kernel and its launchers; the per-dtype translation
 // units conv_f32.hip, conv_f16.hip and conv_bf16.hip instantiate them (one
