@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests skip (not fail) where there is no GPU; on a GPU machine they must run
+    # GPU tests skip (not fail) on a machine without a GPU; with a GPU they run
     try:
         import torch
         have_gpu = torch.cuda.is_available()
