@@ -325,6 +325,12 @@ def test_async_map_equals_the_waiting_map():
     _async_equals_waiting(c, w.batch, w.shape, 3, 2, 1, 1, bound)
     print("async SubM map, LiDAR scene", flush=True)
     _async_equals_waiting(c, w.batch, w.shape, 3, 1, 1, 1, 0, subm=True)
+    # the shell sets' strided map marks its output sites in a byte map
+    sh = W.workload("subm_k3_k1_bf16_shells128")
+    cs = cuda(sh.coords)
+    bound = spc.strided_out_bound(cs.shape[0], sh.batch, sh.shape, 3, 2, 1, 1)
+    print(f"async strided map, shell sets, capacity {bound}", flush=True)
+    _async_equals_waiting(cs, sh.batch, sh.shape, 3, 2, 1, 1, bound)
     # a ragged geometry: k=(3,2,3), stride (2,1,3), pad (1,0,1), dilation (1,2,1)
     small = W.tiny_grid(W.rng(78), 11, 0.3, 2)
     bound = spc.strided_out_bound(small.shape[0], 2, (11, 11, 11), (3, 2, 3), (2, 1, 3), (1, 0, 1), (1, 2, 1))
