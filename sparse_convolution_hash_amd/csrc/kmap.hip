@@ -609,31 +609,75 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     //    when the neighbour is outside the grid; such entries are -1 regardless)
     uint32_t key[ROWPASS_KMAX];
     uint64_t got[ROWPASS_KMAX];
-    uint32_t inside = 0;
+    uint32_t inside = 0, occb = 0;  // occb (BITS): the occupancy bit of each entry's cell
+    // (a SubM map's centre is looked up only with the index grid, whose
+    // insert left the duplicate check to this kernel)
+    if (BITS && SUBM && K == 27) {
+        // The three x-neighbours of each (z, y) of a 3x3x3 submanifold row are
+        // adjacent cells: one 64-bit bitmap word holds all three unless the
+        // row's own x sits at a word edge, where the word beside it holds the
+        // third.  9 pairs of 8-byte loads instead of 27 4-byte ones, all
+        // issued before any is used (the edge word is the row's own word when
+        // it is not needed, and clamped to the bitmap).
+        const uint64_t* occ64 = reinterpret_cast<const uint64_t*>(occ);
+        const uint32_t last = uint32_t((uint64_t(g.batch) * g.Z * g.Y * g.X - 1) >> 6);
+        uint64_t lo[9], hi[9];
+        uint32_t rr[9];
 #pragma unroll
-    for (int k = 0; k < ROWPASS_KMAX; ++k) {
-        const uint32_t kk = ktab[k < K ? k : 0];
-        const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy,
-                  x = c.w * g.sx - g.px + int(kk & 7) * g.dx;
-        // (a SubM map's centre is looked up only with the index grid, whose
-        // insert left the duplicate check to this kernel)
-        const bool in = ok && k < K && !(SUBM && !DENSE && k == K / 2) && (unsigned)z < (unsigned)g.Z &&
-                        (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X;
-        key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
-        inside |= uint32_t(in) << k;
-        got[k] = BITS ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
+        for (int q = 0; q < 9; ++q) {
+            const uint32_t kk = ktab[3 * q];
+            const int z = c.y - g.pz + int(kk >> 6), y = c.z - g.py + int((kk >> 3) & 7);
+            const bool row_in = ok && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y;
+            const uint32_t km = row_in ? in_key(c.x, z, y, c.w, g) : 0u;
+            const uint32_t w = km >> 6, r = km & 63u;
+            const uint32_t w2 = r == 0u ? (w > 0u ? w - 1u : 0u) : (r == 63u ? min(w + 1u, last) : w);
+            lo[q] = occ64[w];
+            hi[q] = occ64[w2];
+            rr[q] = r;
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int k = 3 * q + e;
+                const bool in = row_in && !(!DENSE && k == K / 2) && (unsigned)(c.w + e - 1) < (unsigned)g.X;
+                key[k] = in ? km + uint32_t(e) - 1u : 0u;
+                inside |= uint32_t(in) << k;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 9; ++q)
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int p = int(rr[q]) + e - 1;  // -1 .. 64
+                const uint64_t b = p < 0 ? hi[q] >> 63 : (p > 63 ? hi[q] : lo[q] >> p);
+                occb |= uint32_t(b & 1u) << (3 * q + e);
+            }
+    } else {
+#pragma unroll
+        for (int k = 0; k < ROWPASS_KMAX; ++k) {
+            const uint32_t kk = ktab[k < K ? k : 0];
+            const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy,
+                      x = c.w * g.sx - g.px + int(kk & 7) * g.dx;
+            const bool in = ok && k < K && !(SUBM && !DENSE && k == K / 2) && (unsigned)z < (unsigned)g.Z &&
+                            (unsigned)y < (unsigned)g.Y && (unsigned)x < (unsigned)g.X;
+            key[k] = in ? in_key(c.x, z, y, x, g) : 0u;
+            inside |= uint32_t(in) << k;
+            got[k] = BITS ? uint64_t(occ[key[k] >> 5]) : table[home_slot(key[k]) & mask];
+        }
+        if (BITS) {
+#pragma unroll
+            for (int k = 0; k < ROWPASS_KMAX; ++k) occb |= ((uint32_t(got[k]) >> (key[k] & 31u)) & 1u) << k;
+        }
     }
     if (DENSE) {  // grid cells of the occupied neighbours (cell 0, ignored, elsewhere)
 #pragma unroll
         for (int k = 0; k < ROWPASS_KMAX; ++k) {
-            const bool hit = ((inside >> k) & (uint32_t(got[k]) >> (key[k] & 31u)) & 1u) != 0;
+            const bool hit = ((inside & occb) >> k) & 1u;
             const int32_t v = dense[hit ? key[k] : 0u];
             got[k] = uint64_t(uint32_t(hit ? v : -1));
         }
     } else if (BITS) {  // home slots of the occupied neighbours (slot 0, ignored, elsewhere)
 #pragma unroll
         for (int k = 0; k < ROWPASS_KMAX; ++k) {
-            const bool hit = ((inside >> k) & (uint32_t(got[k]) >> (key[k] & 31u)) & 1u) != 0;
+            const bool hit = ((inside & occb) >> k) & 1u;
             const uint64_t v = table[hit ? home_slot(key[k]) & mask : 0u];
             got[k] = hit ? v : EMPTY_SLOT;
         }
