@@ -612,23 +612,30 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
     uint32_t inside = 0, occb = 0;  // occb (BITS): the occupancy bit of each entry's cell
     // (a SubM map's centre is looked up only with the index grid, whose
     // insert left the duplicate check to this kernel)
-    if (BITS && SUBM && K == 27) {
-        // The three x-neighbours of each (z, y) of a 3x3x3 submanifold row are
-        // adjacent cells: one 64-bit bitmap word holds all three unless the
-        // row's own x sits at a word edge, where the word beside it holds the
-        // third.  9 pairs of 8-byte loads instead of 27 4-byte ones, all
-        // issued before any is used (the edge word is the row's own word when
-        // it is not needed, and clamped to the bitmap).
+    if (BITS && K == 27 && g.kx == 3 && g.dx == 1) {
+        // The three x-cells of each (z, y) of a 3x3x3 kernel without x
+        // dilation are adjacent: one 64-bit bitmap word holds all three unless
+        // the middle one sits at a word edge, where the word beside it holds
+        // the third.  9 pairs of 8-byte loads instead of 27 4-byte ones, all
+        // issued before any is used (the edge word is the middle cell's own
+        // word when it is not needed, and clamped to the bitmap; a middle cell
+        // outside the grid is clamped to its edge, and the in-grid cells are
+        // placed relative to it).
         const uint64_t* occ64 = reinterpret_cast<const uint64_t*>(occ);
         const uint32_t last = uint32_t((uint64_t(g.batch) * g.Z * g.Y * g.X - 1) >> 6);
         uint64_t lo[9], hi[9];
         uint32_t rr[9];
+        const int xm = c.w * g.sx - g.px + 1;  // the middle x-cell
+        const int xmc = xm < 0 ? 0 : (xm >= g.X ? g.X - 1 : xm);
+        int dxe[3];  // the x-cells relative to the clamped middle one
+#pragma unroll
+        for (int e = 0; e < 3; ++e) dxe[e] = xm - 1 + e - xmc;
 #pragma unroll
         for (int q = 0; q < 9; ++q) {
             const uint32_t kk = ktab[3 * q];
-            const int z = c.y - g.pz + int(kk >> 6), y = c.z - g.py + int((kk >> 3) & 7);
+            const int z = c.y * g.sz - g.pz + int(kk >> 6) * g.dz, y = c.z * g.sy - g.py + int((kk >> 3) & 7) * g.dy;
             const bool row_in = ok && (unsigned)z < (unsigned)g.Z && (unsigned)y < (unsigned)g.Y;
-            const uint32_t km = row_in ? in_key(c.x, z, y, c.w, g) : 0u;
+            const uint32_t km = row_in ? in_key(c.x, z, y, xmc, g) : 0u;
             const uint32_t w = km >> 6, r = km & 63u;
             const uint32_t w2 = r == 0u ? (w > 0u ? w - 1u : 0u) : (r == 63u ? min(w + 1u, last) : w);
             lo[q] = occ64[w];
@@ -637,8 +644,8 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
 #pragma unroll
             for (int e = 0; e < 3; ++e) {
                 const int k = 3 * q + e;
-                const bool in = row_in && !(!DENSE && k == K / 2) && (unsigned)(c.w + e - 1) < (unsigned)g.X;
-                key[k] = in ? km + uint32_t(e) - 1u : 0u;
+                const bool in = row_in && !(SUBM && !DENSE && k == K / 2) && (unsigned)(xm - 1 + e) < (unsigned)g.X;
+                key[k] = in ? uint32_t(int(km) + dxe[e]) : 0u;
                 inside |= uint32_t(in) << k;
             }
         }
@@ -646,7 +653,8 @@ __global__ __launch_bounds__(KB) void k_out_rows(const int4* __restrict__ rcoord
         for (int q = 0; q < 9; ++q)
 #pragma unroll
             for (int e = 0; e < 3; ++e) {
-                const int p = int(rr[q]) + e - 1;  // -1 .. 64
+                // -1 .. 64 for a cell inside the grid (any bit serves the others: they are not inside)
+                const int p = min(max(int(rr[q]) + dxe[e], -1), 64);
                 const uint64_t b = p < 0 ? hi[q] >> 63 : (p > 63 ? hi[q] : lo[q] >> p);
                 occb |= uint32_t(b & 1u) << (3 * q + e);
             }
