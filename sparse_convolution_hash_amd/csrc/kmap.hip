@@ -768,6 +768,58 @@ __global__ __launch_bounds__(KB) void k_in_rows(const int4* __restrict__ coords,
     const bool live = i < n;
     const int4 c = coords[live ? i : n - 1];
     const bool ok = live && in_grid(c, g);
+    int32_t* srow = stage + t * K;
+    uint32_t m = 0;
+    if (K == 27 && g.kz == 3 && g.ky == 3 && g.sz >= 2 && g.sy >= 2 && g.sx >= 2 && g.dz == 1 && g.dy == 1 &&
+        g.dx == 1) {
+        // Stride >= 2 with 3 offsets per axis and no dilation: at most 2
+        // offsets per axis reach an output site (their c + pad - k span less
+        // than 2 strides), so at most 8 of the 27 entries exist.  Their sites
+        // are found per axis, and only those 8 combinations load a bitmap
+        // word and a prefix (invalid ones from word 0); the rest of the row
+        // is -1.
+        int ka[3][2], oa[3][2], na[3];
+        const int cc[3] = {c.y, c.z, c.w}, pp[3] = {g.pz, g.py, g.px}, dd[3] = {g.dz, g.dy, g.dx},
+                  ss[3] = {g.sz, g.sy, g.sx}, ext[3] = {g.oz, g.oy, g.ox};
+        const uint64_t ms[3] = {g.msz, g.msy, g.msx};
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            na[a] = 0;
+            ka[a][0] = ka[a][1] = 0;
+            oa[a][0] = oa[a][1] = 0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int num = cc[a] + pp[a] - k * dd[a];
+                const int o = num >= 0 ? int(qdiv(uint32_t(num), ms[a])) : -1;
+                const bool hit = o >= 0 && o * ss[a] == num && o < ext[a];
+                if (hit && na[a] < 2) {
+                    ka[a][na[a]] = k;
+                    oa[a][na[a]] = o;
+                    ++na[a];
+                }
+            }
+        }
+        uint32_t bits8[8], pre8[8], pos8[8];
+        bool in8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int iz = q >> 2, iy = (q >> 1) & 1, ix = q & 1;
+            in8[q] = ok && iz < na[0] && iy < na[1] && ix < na[2];
+            const uint32_t key = in8[q] ? out_key(c.x, oa[0][iz], oa[1][iy], oa[2][ix], g) : 0u;
+            pos8[q] = key & 31u;
+            bits8[q] = bitmap[key >> 5];
+            pre8[q] = prefix[key >> 5];
+        }
+#pragma unroll
+        for (int k = 0; k < 27; ++k) srow[k] = -1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (!in8[q]) continue;
+            const int k = (ka[0][q >> 2] * 3 + ka[1][(q >> 1) & 1]) * 3 + ka[2][q & 1];
+            srow[k] = int32_t(pre8[q] + __popc(bits8[q] & ((1u << pos8[q]) - 1u)));
+            m |= 1u << k;
+        }
+    } else {
     uint32_t bitpos[ROWPASS_KMAX], bits[ROWPASS_KMAX], pre[ROWPASS_KMAX];
     uint32_t valid = 0;
 #pragma unroll
@@ -786,14 +838,13 @@ __global__ __launch_bounds__(KB) void k_in_rows(const int4* __restrict__ coords,
         bits[k] = bitmap[key >> 5];
         pre[k] = prefix[key >> 5];
     }
-    uint32_t m = 0;
-    int32_t* srow = stage + t * K;
 #pragma unroll
     for (int k = 0; k < ROWPASS_KMAX; ++k) {
         if (k >= K) continue;
         const bool in = (valid >> k) & 1u;
         srow[k] = in ? int32_t(pre[k] + __popc(bits[k] & ((1u << bitpos[k]) - 1u))) : -1;
         if (in) m |= 1u << k;
+    }
     }
     if (keys && live) keys[i] = m;
     __syncthreads();

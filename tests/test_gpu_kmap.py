@@ -139,7 +139,7 @@ def test_bad_coordinates_at_workload_size(table):
 @pytest.mark.parametrize("seed,shape,fill,batch,k,s,p,d", [
     (21, (6, 5, 7), 0.2, 1, 3, 2, 1, 1), (22, (7, 7, 7), 0.1, 2, 3, 2, 0, 1), (23, (8, 6, 5), 0.15, 1, 2, 2, 0, 1),
     (24, (6, 6, 6), 0.2, 1, 3, 1, 1, 2), (25, (9, 7, 8), 0.1, 2, 3, 3, 2, 1), (26, (17, 19, 23), 0.2, 2, 3, 2, 1, 1),
-    (27, (12, 12, 12), 0.3, 1, 5, 2, 2, 1),
+    (27, (12, 12, 12), 0.3, 1, 5, 2, 2, 1), (28, (13, 11, 12), 0.2, 2, 3, 2, 2, 2), (29, (10, 9, 11), 0.3, 2, 3, 2, 0, 1),
 ])
 def test_strided_tiny(seed, shape, fill, batch, k, s, p, d):
     r = W.rng(seed)
